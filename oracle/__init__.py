@@ -1,0 +1,173 @@
+"""CPU oracle for the MoE layout / dispatch / combine path (numpy in, numpy out).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does.
+It shares no code with the GPU library. The arithmetic lives in
+``moe_oracle.c`` (plain C, fp32 fmaf chain, built without fast-math); this
+file only marshals numpy arrays into it.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against library
+routines, invariants, closed forms, brute force and hand-worked fixtures.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, ERR_ARG, ERR_ALIGN, ERR_LIMIT, ERR_CAPACITY = 0, -1, -2, -3, -4
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into liboracle.so (gcc, -O2, no FP contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-std=c11",
+               "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Field(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("src_row_stride", ctypes.c_int64),
+                ("dst", ctypes.c_void_p), ("dst_row_stride", ctypes.c_int64),
+                ("row_bytes", ctypes.c_int64)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.oracle_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P]
+        L.oracle_layout.restype = ctypes.c_int
+        L.oracle_dispatch.argtypes = [ctypes.POINTER(_Field), i32, i32, i32, P]
+        L.oracle_dispatch.restype = ctypes.c_int
+        L.oracle_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64]
+        L.oracle_combine.restype = ctypes.c_int
+        L.oracle_combine_acc.argtypes = [P, i64, P, i64, P, i32, i32, i32, P]
+        L.oracle_combine_acc.restype = ctypes.c_int
+        L.oracle_required_cap.argtypes = [i32, i32, i32, i32]
+        L.oracle_required_cap.restype = i64
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: oracle returned {code}")
+        self.code = code
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _row_view(a: np.ndarray) -> Tuple[int, int]:
+    """(base pointer, row stride in elements) of a 2-D array whose rows may be
+    strided but whose elements inside a row are contiguous."""
+    assert a.ndim == 2 and (a.shape[1] <= 1 or a.strides[1] == a.itemsize)
+    return _ptr(a), a.strides[0] // a.itemsize
+
+
+def required_cap(N: int, K: int, E: int, align: int = 1) -> int:
+    return int(lib().oracle_required_cap(N, K, E, align))
+
+
+def layout(ids: np.ndarray, E: int, align: int = 1, cap: Optional[int] = None):
+    """Routing layout of ``ids`` [N, K] int32 (rows may be strided).
+
+    Returns (counts [E], offsets [E+1], pos [N, K], row_pair [cap], status).
+    """
+    assert ids.dtype == np.int32
+    N, K = ids.shape
+    if cap is None:
+        cap = max(required_cap(N, K, E, align), 0)
+    base, stride = _row_view(ids) if N > 0 else (0, K)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    pos = np.empty((N, K), np.int32)
+    row_pair = np.empty(max(cap, 0), np.int32)
+    status = np.zeros(1, np.int32)
+    rc = lib().oracle_layout(base, stride, N, K, E, align, _ptr(counts), _ptr(offsets),
+                             _ptr(pos), _ptr(row_pair), cap, _ptr(status))
+    if rc != OK:
+        raise OracleError(rc, "layout")
+    return counts, offsets, pos, row_pair, int(status[0])
+
+
+def dispatch(srcs: Sequence[np.ndarray], pos: Optional[np.ndarray], K: int,
+             dsts: Optional[List[np.ndarray]] = None, rows: Optional[int] = None,
+             fill: int = 0) -> List[np.ndarray]:
+    """Copy each token's row of every ``srcs[f]`` [N, bytes] (uint8) into
+    ``dsts[f]`` [rows, bytes] at row pos[t, k]. ``pos=None`` is the identity
+    (K must be 1). Missing ``dsts`` are allocated and filled with ``fill``."""
+    N = srcs[0].shape[0]
+    if dsts is None:
+        rows = N * K if rows is None else rows
+        dsts = [np.full((rows, s.shape[1]), fill, np.uint8) for s in srcs]
+    fs = (_Field * len(srcs))()
+    for i, (s, d) in enumerate(zip(srcs, dsts)):
+        assert s.dtype == np.uint8 and d.dtype == np.uint8 and s.shape[1] == d.shape[1]
+        sb, ss = _row_view(s) if s.shape[0] else (0, s.shape[1])
+        db, ds = _row_view(d) if d.shape[0] else (0, d.shape[1])
+        fs[i] = _Field(sb, ss, db, ds, s.shape[1])
+    pos_c = None if pos is None else np.ascontiguousarray(pos, dtype=np.int32)
+    rc = lib().oracle_dispatch(fs, len(srcs), N, K, 0 if pos_c is None else _ptr(pos_c))
+    if rc != OK:
+        raise OracleError(rc, "dispatch")
+    return dsts
+
+
+def combine(y: np.ndarray, w: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """out [N, Hc] (bf16 bits, uint16) = bf16(sum_k w[t,k] * y[pos[t,k]])."""
+    assert y.dtype == np.uint16 and w.dtype == np.float32
+    N, K = pos.shape
+    Hc = y.shape[1]
+    out = np.empty((N, Hc), np.uint16)
+    pos_c = np.ascontiguousarray(pos, dtype=np.int32)
+    yb, ys = _row_view(y) if y.shape[0] else (0, Hc)
+    wb, ws = _row_view(w) if N else (0, K)
+    rc = lib().oracle_combine(yb, ys, wb, ws, _ptr(pos_c), N, K, Hc, _ptr(out), Hc)
+    if rc != OK:
+        raise OracleError(rc, "combine")
+    return out
+
+
+def combine_acc(y: np.ndarray, w: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """The fp32 accumulators [N, Hc] of ``combine`` before the bf16 rounding."""
+    assert y.dtype == np.uint16 and w.dtype == np.float32
+    N, K = pos.shape
+    Hc = y.shape[1]
+    acc = np.empty((N, Hc), np.float32)
+    pos_c = np.ascontiguousarray(pos, dtype=np.int32)
+    yb, ys = _row_view(y) if y.shape[0] else (0, Hc)
+    wb, ws = _row_view(w) if N else (0, K)
+    rc = lib().oracle_combine_acc(yb, ys, wb, ws, _ptr(pos_c), N, K, Hc, _ptr(acc))
+    if rc != OK:
+        raise OracleError(rc, "combine_acc")
+    return acc
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(lib().oracle_f32_to_bf16(x))
+
+
+def bf16_to_f32(b: int) -> float:
+    return float(lib().oracle_bf16_to_f32(b))

@@ -1,0 +1,203 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously correct CPU oracle for the MoE
+ * layout / dispatch / combine path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library calls, links or
+ * includes this file. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it. It shares no code, header, table
+ * or helper with the GPU library.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math), so
+ * that every fp32 operation is the one written here, rounded once.
+ *
+ * What it computes, and where each step comes from:
+ *
+ *   layout   -- DeepEP (deepseek-ai/DeepEP repository dump), deep_ep.cpp,
+ *               Buffer::get_dispatch_layout: per-expert token counts of the
+ *               top-k ids; Buffer::intranode_dispatch: the receive buffer is
+ *               expert-contiguous and sized for the worst case when
+ *               num_worst_tokens is given (no host wait), with recv_src_idx
+ *               naming each received row's source. The order of rows inside
+ *               one expert's segment is not fixed by the pages; the oracle
+ *               takes ascending (token, k) -- a stable counting sort.
+ *               Masked ids: the vLLM branch compare ds-exp-2...ds-exp-ag,
+ *               mask_topk_ids writes -1 for padded tokens; any id < 0 is
+ *               skipped. ids >= E are counted in *status and skipped.
+ *   dispatch -- deep_ep.cpp intranode dispatch outputs recv_x, recv_x_scales,
+ *               recv_topk_idx, recv_topk_weights: every received row carries
+ *               the token's whole payload. Byte copies, no conversion.
+ *   combine  -- the same compare page, moe_reduce_scatter.cu, POLL + REDUCE
+ *               phase: bf16 inputs summed into fp32 accumulators in a fixed
+ *               order, one conversion to bf16 at the end; DeepEP
+ *               low_latency_combine takes topk_weights fp32 to weight the
+ *               expert outputs. Here: acc = +0; for k ascending with a valid
+ *               row, acc = fmaf(w[t,k], y[row,h], acc); out = bf16_rne(acc).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_ALIGN (-2)
+#define ORC_ERR_LIMIT (-3)
+#define ORC_ERR_CAPACITY (-4)
+
+#define ORC_MAX_K 32
+#define ORC_MAX_E 1024
+
+int oracle_version(void) { return 1; }
+
+/* Rows the receive buffer must hold so that no routing can overflow it:
+ * every (token, k) pair, plus the padding each expert segment can need when
+ * it is rounded up to a multiple of `align`. */
+int64_t oracle_required_cap(int32_t N, int32_t K, int32_t E, int32_t align) {
+    int64_t c = (int64_t)N * K;
+    if (align > 1) c += (int64_t)E * (align - 1);
+    return c;
+}
+
+/* Layout: counts[e], offsets[0..E], pos[t*K+k], row_pair[0..cap), *status. */
+int oracle_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K, int32_t E,
+                  int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_pair,
+                  int64_t cap, int32_t* status) {
+    if (N < 0 || K < 1 || E < 1 || align < 1) return ORC_ERR_ARG;
+    if (K > ORC_MAX_K || E > ORC_MAX_E) return ORC_ERR_LIMIT;
+    if ((int64_t)N * K >= ((int64_t)1 << 31)) return ORC_ERR_LIMIT;
+    if (N > 0 && ids_row_stride < K) return ORC_ERR_ARG;
+    if (cap < oracle_required_cap(N, K, E, align)) return ORC_ERR_CAPACITY;
+    if (cap >= ((int64_t)1 << 31)) return ORC_ERR_LIMIT;
+
+    int32_t bad = 0;
+
+    /* counts: one increment per valid (t, k), in (t, k) order. */
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = ids[(int64_t)t * ids_row_stride + k];
+            if (e < 0) continue;
+            if (e >= E) { ++bad; continue; }
+            counts[e] += 1;
+        }
+    }
+
+    /* offsets: exclusive running sum of counts rounded up to `align`. */
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        int32_t padded = (counts[e] + align - 1) / align * align;
+        offsets[e + 1] = offsets[e] + padded;
+    }
+
+    /* pos / row_pair: walk the pairs in (t, k) order; each valid pair takes
+     * the next free row of its expert's segment. */
+    for (int64_t r = 0; r < cap; ++r) row_pair[r] = -1;
+    int32_t cursor[ORC_MAX_E];
+    for (int32_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = ids[(int64_t)t * ids_row_stride + k];
+            int32_t p = -1;
+            if (e >= 0 && e < E) {
+                p = cursor[e];
+                cursor[e] += 1;
+                row_pair[p] = t * K + k;
+            }
+            pos[(int64_t)t * K + k] = p;
+        }
+    }
+    if (status) *status = bad;
+    return ORC_OK;
+}
+
+/* One payload field: byte rows of `row_bytes`, read from src with
+ * src_row_stride bytes between tokens, written to dst with dst_row_stride
+ * bytes between receive rows. */
+typedef struct {
+    const void* src;
+    int64_t src_row_stride;
+    void* dst;
+    int64_t dst_row_stride;
+    int64_t row_bytes;
+} oracle_field;
+
+/* Dispatch: dst_f[pos[t,k]] <- src_f[t] for every valid (t, k) and field f.
+ * pos == NULL means the identity map pos[t] = t with K == 1 (pack/unpack). */
+int oracle_dispatch(const oracle_field* fields, int32_t nfields, int32_t N, int32_t K,
+                    const int32_t* pos) {
+    if (nfields < 1 || nfields > 4 || N < 0 || K < 1 || K > ORC_MAX_K) return ORC_ERR_ARG;
+    if (pos == NULL && K != 1) return ORC_ERR_ARG;
+    for (int f = 0; f < nfields; ++f)
+        if (fields[f].row_bytes < 0) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t p = pos ? pos[(int64_t)t * K + k] : t;
+            if (p < 0) continue;
+            for (int f = 0; f < nfields; ++f) {
+                const oracle_field* d = &fields[f];
+                memcpy((char*)d->dst + (int64_t)p * d->dst_row_stride,
+                       (const char*)d->src + (int64_t)t * d->src_row_stride, (size_t)d->row_bytes);
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* bf16 -> fp32: the bf16 pattern is the top half of the fp32 pattern. */
+float oracle_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even (NaN -> 0x7FC0).
+ * Adding 0x7FFF plus the lowest kept bit carries into the kept half exactly
+ * when the dropped half is above one half, or equal to it with the kept
+ * half odd. */
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* The fp32 accumulator of one output element: acc = +0, then for k
+ * ascending with a valid row, acc = fmaf(w[t,k], y[row, h], acc). */
+static float combine_acc(const uint16_t* y, int64_t y_row_stride, const float* w,
+                         int64_t w_row_stride, const int32_t* pos, int32_t K, int32_t t, int32_t h) {
+    float acc = 0.0f;
+    for (int32_t k = 0; k < K; ++k) {
+        int32_t p = pos[(int64_t)t * K + k];
+        if (p < 0) continue;
+        float yv = oracle_bf16_to_f32(y[(int64_t)p * y_row_stride + h]);
+        acc = fmaf(w[(int64_t)t * w_row_stride + k], yv, acc);
+    }
+    return acc;
+}
+
+/* Combine: out[t,h] = bf16_rne(fp32 accumulator of (t, h)). */
+int oracle_combine(const uint16_t* y, int64_t y_row_stride, const float* w, int64_t w_row_stride,
+                   const int32_t* pos, int32_t N, int32_t K, int32_t Hc, uint16_t* out,
+                   int64_t out_row_stride) {
+    if (N < 0 || K < 1 || K > ORC_MAX_K || Hc < 0) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; ++t)
+        for (int32_t h = 0; h < Hc; ++h)
+            out[(int64_t)t * out_row_stride + h] =
+                oracle_f32_to_bf16(combine_acc(y, y_row_stride, w, w_row_stride, pos, K, t, h));
+    return ORC_OK;
+}
+
+/* The same reduction with the fp32 accumulators written out unrounded, so
+ * the order and fusion of the chain can be checked on their own. */
+int oracle_combine_acc(const uint16_t* y, int64_t y_row_stride, const float* w,
+                       int64_t w_row_stride, const int32_t* pos, int32_t N, int32_t K, int32_t Hc,
+                       float* acc_out) {
+    if (N < 0 || K < 1 || K > ORC_MAX_K || Hc < 0) return ORC_ERR_ARG;
+    for (int32_t t = 0; t < N; ++t)
+        for (int32_t h = 0; h < Hc; ++h)
+            acc_out[(int64_t)t * Hc + h] = combine_acc(y, y_row_stride, w, w_row_stride, pos, K, t, h);
+    return ORC_OK;
+}
