@@ -1,0 +1,301 @@
+"""Python binding of libmoe_get.so: MoE routing layout, dispatch and combine
+on one MI355X (gfx950).
+
+The functions named like the C ABI (``moe_get_layout``, ``moe_dispatch``,
+``moe_combine``, ...) only check tensor shapes, dtypes and alignment and pass
+device pointers plus ``torch.cuda.current_stream()`` to the library; every
+step of the path runs in the library's HIP kernels. PyTorch provides device
+memory and streams only. There is no CPU path: importing this package fails
+if the library has not been built (``python -m combine_moe_get_amd.build``).
+
+Convenience wrappers (``layout``, ``dispatch``, ``combine``,
+``pack_records``, ``unpack_records``) allocate outputs with torch and call the
+same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import torch  # loaded first so the library binds to the same HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_get.so")
+
+MOE_OK = 0
+MOE_ERR_ARG = -1
+MOE_ERR_ALIGN = -2
+MOE_ERR_LIMIT = -3
+MOE_ERR_CAPACITY = -4
+MOE_ERR_WORKSPACE = -5
+MOE_ERR_HIP = -6
+MAX_TOPK = 32
+MAX_EXPERTS = 1024
+MAX_FIELDS = 4
+
+_ERR_NAMES = {MOE_ERR_ARG: "MOE_ERR_ARG", MOE_ERR_ALIGN: "MOE_ERR_ALIGN",
+              MOE_ERR_LIMIT: "MOE_ERR_LIMIT", MOE_ERR_CAPACITY: "MOE_ERR_CAPACITY",
+              MOE_ERR_WORKSPACE: "MOE_ERR_WORKSPACE", MOE_ERR_HIP: "MOE_ERR_HIP"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m combine_moe_get_amd.build` "
+                      "(there is no fallback path)")
+
+
+class moe_field(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("src_row_stride", ctypes.c_int64),
+                ("dst", ctypes.c_void_p), ("dst_row_stride", ctypes.c_int64),
+                ("row_bytes", ctypes.c_int64)]
+
+
+def _load():
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.moe_version.restype = ctypes.c_int
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_required_capacity.argtypes = [i32, i32, i32, i32]
+    L.moe_required_capacity.restype = i64
+    L.moe_layout_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_layout_workspace_bytes.restype = sz
+    L.moe_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, sz, P, P]
+    L.moe_get_layout.restype = ctypes.c_int
+    L.moe_dispatch.argtypes = [ctypes.POINTER(moe_field), i32, i32, i32, P, P]
+    L.moe_dispatch.restype = ctypes.c_int
+    L.moe_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P]
+    L.moe_combine.restype = ctypes.c_int
+    return L
+
+
+_lib = _load()
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, _lib.moe_last_error().decode(errors="replace"))
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: Optional[torch.Tensor], name: str) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    """(pointer, row stride in elements) of a 2-D tensor with contiguous rows."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    return _dev(t, name), t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def version() -> int:
+    return int(_lib.moe_version())
+
+
+# ---------------------------------------------------------------------------
+# Entry points named like the C ABI (marshalling only).
+# ---------------------------------------------------------------------------
+
+def moe_required_capacity(N: int, K: int, E: int, align: int = 1) -> int:
+    return int(_lib.moe_required_capacity(N, K, E, align))
+
+
+def moe_layout_workspace_bytes(N: int, K: int, E: int) -> int:
+    return int(_lib.moe_layout_workspace_bytes(N, K, E))
+
+
+def moe_get_layout(ids: torch.Tensor, num_experts: int, align: int, counts: torch.Tensor,
+                   offsets: torch.Tensor, pos: torch.Tensor, row_pair: torch.Tensor,
+                   workspace: torch.Tensor, status: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """ids: int32 [N, K] (rows may be strided, e.g. a view into records)."""
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    for n, t in (("counts", counts), ("offsets", offsets), ("pos", pos), ("row_pair", row_pair)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
+        raise TypeError("status must be an int32 tensor with at least one element")
+    N, K = ids.shape
+    if counts.numel() < num_experts or offsets.numel() < num_experts + 1 or pos.numel() < N * K:
+        raise ValueError("counts, offsets or pos too small")
+    ip, istride = _rows(ids, "ids") if N > 0 else (0, K)
+    _check(_lib.moe_get_layout(ip, istride, N, K, num_experts, align, _dev(counts, "counts"),
+                               _dev(offsets, "offsets"), _dev(pos, "pos"),
+                               _dev(row_pair, "row_pair"), row_pair.numel(),
+                               _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(),
+                               _dev(status, "status"), _stream(stream)))
+
+
+def _as_bytes2d(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
+    """(pointer, row stride in bytes, row bytes) of a 2-D tensor with
+    contiguous rows, any dtype."""
+    ptr, stride = _rows(t, name)
+    es = t.element_size()
+    return ptr, stride * es, t.shape[1] * es
+
+
+def moe_dispatch(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor],
+                 pos: Optional[torch.Tensor], K: int, stream=None) -> None:
+    """Copy row t of every srcs[f] into rows pos[t, k] of dsts[f].
+
+    ``pos=None`` is the identity (K must be 1). Tensors are 2-D with
+    contiguous rows; each field's row size in bytes must match."""
+    if len(srcs) != len(dsts) or not 1 <= len(srcs) <= MAX_FIELDS:
+        raise ValueError("need 1..4 matching source / destination fields")
+    N = srcs[0].shape[0]
+    arr = (moe_field * len(srcs))()
+    for i, (s, d) in enumerate(zip(srcs, dsts)):
+        if s.shape[0] != N:
+            raise ValueError("all sources need the same number of tokens")
+        sp, ss, sb = _as_bytes2d(s, f"srcs[{i}]")
+        dp, ds, db = _as_bytes2d(d, f"dsts[{i}]")
+        if sb != db:
+            raise ValueError(f"field {i}: source rows {sb} B, destination rows {db} B")
+        arr[i] = moe_field(sp, ss, dp, ds, sb)
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()
+                            or pos.numel() != N * K):
+        raise ValueError("pos must be a contiguous int32 [N, K] tensor")
+    _check(_lib.moe_dispatch(arr, len(srcs), N, K, _dev(pos, "pos"), _stream(stream)))
+
+
+def moe_combine(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor, out: torch.Tensor,
+                stream=None) -> None:
+    """out [N, Hc] bf16 = sum_k weights[t, k] * y[pos[t, k]] (fp32 accumulate)."""
+    if y.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("y and out must be bfloat16")
+    if weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 2:
+        raise TypeError("pos must be a contiguous int32 [N, K] tensor")
+    N, K = pos.shape
+    Hc = out.shape[1]
+    if y.shape[1] != Hc or out.shape[0] != N or tuple(weights.shape) != (N, K):
+        raise ValueError("shape mismatch between y, weights, pos and out")
+    yp, ys = _rows(y, "y") if y.shape[0] else (_dev(y, "y"), Hc)
+    wp, ws = _rows(weights, "weights") if N else (0, K)
+    op, os_ = _rows(out, "out") if N else (0, Hc)
+    _check(_lib.moe_combine(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc, op, os_,
+                            _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrappers that allocate their outputs.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Layout:
+    counts: torch.Tensor      # int32 [E]
+    offsets: torch.Tensor     # int32 [E+1]
+    pos: torch.Tensor         # int32 [N, K]
+    row_pair: torch.Tensor    # int32 [cap]
+    status: torch.Tensor      # int32 [1]: ids >= E seen
+    num_experts: int
+    align: int
+
+    @property
+    def cap(self) -> int:
+        return self.row_pair.numel()
+
+    @property
+    def K(self) -> int:
+        return self.pos.shape[1]
+
+
+def layout(ids: torch.Tensor, num_experts: int, align: int = 1, cap: Optional[int] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> Layout:
+    N, K = ids.shape
+    if cap is None:
+        cap = moe_required_capacity(N, K, num_experts, align)
+        if cap < 0:
+            raise MoeError(MOE_ERR_ARG, "invalid layout sizes")
+    dev = ids.device
+    if workspace is None:
+        nbytes = moe_layout_workspace_bytes(N, K, num_experts)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    lay = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
+                 torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+                 torch.empty((N, K), dtype=torch.int32, device=dev),
+                 torch.empty(max(cap, 0), dtype=torch.int32, device=dev),
+                 torch.empty(1, dtype=torch.int32, device=dev), num_experts, align)
+    moe_get_layout(ids, num_experts, align, lay.counts, lay.offsets, lay.pos, lay.row_pair,
+                   workspace, lay.status, stream)
+    return lay
+
+
+def dispatch(srcs: Sequence[torch.Tensor], lay: Layout, stream=None) -> List[torch.Tensor]:
+    """Receive buffers [cap, ...] of every field, filled at the rows ``lay``
+    assigned (other rows are left uninitialized)."""
+    dsts = [torch.empty((lay.cap,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device)
+            for s in srcs]
+    moe_dispatch(srcs, dsts, lay.pos, lay.K, stream)
+    return dsts
+
+
+def combine(y: torch.Tensor, weights: torch.Tensor, lay: Layout,
+            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N = lay.pos.shape[0]
+    if out is None:
+        out = torch.empty((N, y.shape[1]), dtype=torch.bfloat16, device=y.device)
+    moe_combine(y, weights, lay.pos, out, stream)
+    return out
+
+
+def record_offsets(row_bytes: Sequence[int]) -> Tuple[List[int], int]:
+    """16-byte aligned offset of each field inside a per-token record and the
+    record size rounded up to 16 bytes (fields in the given order)."""
+    offs, cur = [], 0
+    for b in row_bytes:
+        cur = (cur + 15) & ~15
+        offs.append(cur)
+        cur += b
+    return offs, (cur + 15) & ~15
+
+
+def _field_views(records: torch.Tensor, tensors: Sequence[torch.Tensor]) -> List[torch.Tensor]:
+    offs, _ = record_offsets([t.shape[1] * t.element_size() for t in tensors])
+    return [records[:, o:o + t.shape[1] * t.element_size()] for o, t in zip(offs, tensors)]
+
+
+def _bytes2d(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dim() == 2 else t.reshape(t.shape[0], -1).view(torch.uint8)
+
+
+def pack_records(tensors: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
+    """Pack per-token tensors (e.g. ids, weights, hidden, scales) into one
+    uint8 record per token, each field at a 16-byte aligned offset."""
+    N = tensors[0].shape[0]
+    b = [_bytes2d(t) for t in tensors]
+    _, rec_bytes = record_offsets([x.shape[1] for x in b])
+    rec = torch.zeros((N, rec_bytes), dtype=torch.uint8, device=tensors[0].device)
+    moe_dispatch(b, _field_views(rec, b), None, 1, stream)
+    return rec
+
+
+def unpack_records(records: torch.Tensor, like: Sequence[torch.Tensor],
+                   stream=None) -> List[torch.Tensor]:
+    """Inverse of ``pack_records``: tensors shaped like ``like`` (row count
+    taken from ``records``)."""
+    N = records.shape[0]
+    outs = [torch.empty((N,) + tuple(t.shape[1:]), dtype=t.dtype, device=records.device)
+            for t in like]
+    b = [_bytes2d(o) for o in outs]
+    moe_dispatch(_field_views(records, b), b, None, 1, stream)
+    return outs

@@ -1,0 +1,186 @@
+/*
+ * moe_get.h -- C ABI of the MI355X (gfx950) MoE routing layout, dispatch and
+ * combine library (libmoe_get.so).
+ *
+ * The three calls are one GPU's share of an expert-parallel MoE layer:
+ *
+ *   moe_get_layout  per-expert histogram of the top-k ids, its exclusive
+ *                   prefix scan, and a stable row for every (token, k) pair
+ *                   in an expert-contiguous receive buffer.
+ *   moe_dispatch    copies each token's payload (hidden bytes, scales, top-k
+ *                   ids and weights, or one packed record) into the rows the
+ *                   layout gave it.
+ *   moe_combine     gathers the expert outputs back to token order as a
+ *                   top-k weighted bf16 sum, accumulated in fp32.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as device pointers must be device memory (or memory the
+ *     device can access); the `fields` array itself is host memory.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and
+ *     returns; it never synchronizes and never waits on the host.
+ *   - The library never allocates, frees or keeps state between calls; all
+ *     buffers belong to the caller. Inputs are read-only and must not
+ *     overlap outputs.
+ *   - Return value: MOE_OK (0) or a negative MOE_ERR_* code; argument
+ *     problems are found before anything is enqueued. moe_last_error()
+ *     describes the last failure of the calling thread.
+ *   - Data-dependent problems (an id >= E) never fail a call: they are
+ *     counted into the optional device status word and the entry is skipped.
+ *   - N = 0 is allowed and enqueues only the writes of empty results.
+ */
+#ifndef MOE_GET_H
+#define MOE_GET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_ARG (-1)        /* null pointer, negative size, bad count */
+#define MOE_ERR_ALIGN (-2)      /* pointer, stride or row size not aligned */
+#define MOE_ERR_LIMIT (-3)      /* K, E or a size beyond the supported range */
+#define MOE_ERR_CAPACITY (-4)   /* receive capacity below the worst case */
+#define MOE_ERR_WORKSPACE (-5)  /* workspace missing or too small */
+#define MOE_ERR_HIP (-6)        /* the HIP runtime refused a launch */
+
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_FIELDS 4
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int moe_version(void);
+
+/* Text for the last non-zero return on this thread ("" if none). The string
+ * stays valid until the next call on the same thread. */
+const char* moe_last_error(void);
+
+/*
+ * Rows a receive buffer needs so that no routing of N tokens over E experts
+ * with top-K can overflow it: N*K, plus E*(align-1) when each expert segment
+ * is padded to a multiple of `align`. Returns -1 for invalid arguments.
+ * (DeepEP repository dump, deep_ep.cpp, intranode dispatch: num_worst_tokens
+ * sizes the receive buffer for the worst case so no host wait is needed.)
+ */
+int64_t moe_required_capacity(int32_t N, int32_t K, int32_t E, int32_t align);
+
+/* Bytes of device workspace moe_get_layout needs for these sizes (a multiple
+ * of 256; 0 only if the arguments are invalid). The contents need no
+ * initialization and are scratch between calls. */
+size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E);
+
+/*
+ * Routing layout. Defined by DeepEP (repository dump, deep_ep.cpp,
+ * Buffer::get_dispatch_layout: num_tokens_per_expert counts the top-k ids per
+ * expert) and the expert-contiguous receive buffer of its dispatch, whose
+ * recv_src_idx names the source of each received row. Masked ids follow the
+ * vLLM branch compare ds-exp-2...ds-exp-ag (mask_topk_ids writes -1).
+ *
+ *   ids[t*ids_row_stride + k]  (device, int32)  expert of pair (t, k), for
+ *        t < N, k < K. Any id < 0 is masked (skipped); an id >= E is
+ *        skipped and counted in *status. ids_row_stride >= K, in int32
+ *        elements, so the ids may sit inside larger per-token records.
+ *   counts[E]       (device, out) valid pairs per expert.
+ *   offsets[E+1]    (device, out) offsets[0] = 0, offsets[e+1] = offsets[e]
+ *        + counts[e] rounded up to a multiple of `align` (align >= 1);
+ *        offsets[E] = rows used.
+ *   pos[N*K]        (device, out, row-major [N, K]) the receive row of pair
+ *        (t, k), or -1 if masked. Within an expert's segment the rows follow
+ *        ascending (t, k): the order is deterministic and independent of
+ *        the launch shape.
+ *   row_pair[cap]   (device, out) t*K + k of the pair in each row; -1 for
+ *        padding rows and rows >= offsets[E].
+ *   cap             rows of the receive buffer; must be at least
+ *        moe_required_capacity(N, K, E, align) and below 2^31.
+ *   workspace       (device) at least moe_layout_workspace_bytes(N, K, E)
+ *        bytes, 256-byte aligned; not shared with a concurrent call.
+ *   status          (device, out, may be NULL) number of ids >= E.
+ *
+ * Limits: 1 <= K <= 32, 1 <= E <= 1024, N >= 0, N*K < 2^31. Pointers must be
+ * 4-byte aligned. Errors: MOE_ERR_ARG, MOE_ERR_LIMIT, MOE_ERR_CAPACITY,
+ * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K, int32_t E,
+                   int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
+                   int32_t* row_pair, int64_t cap, void* workspace, size_t workspace_bytes,
+                   int32_t* status, hipStream_t stream);
+
+/*
+ * One payload field of a dispatch: `row_bytes` bytes per token, read from
+ * src + t*src_row_stride and written to dst + row*dst_row_stride (device
+ * pointers, strides in bytes). The field is copied byte for byte, whatever
+ * it holds (fp8/bf16 hidden states, fp32 or byte scales, ids, weights).
+ */
+typedef struct moe_field {
+    const void* src;
+    int64_t src_row_stride;
+    void* dst;
+    int64_t dst_row_stride;
+    int64_t row_bytes;
+} moe_field;
+
+/*
+ * Dispatch. For every token t < N, every k < K with pos[t*K+k] >= 0 and
+ * every field f: dst_f row pos[t*K+k] <- src_f row t. Each received row thus
+ * carries the token's whole payload, as DeepEP's dispatch returns recv_x,
+ * recv_x_scales, recv_topk_idx and recv_topk_weights per received token
+ * (repository dump, deep_ep.cpp, Buffer::intranode_dispatch).
+ *
+ *   fields[nfields]  (host array) 1..4 fields. Separate-tensor mode passes
+ *        hidden, scales, ids and weights; packed-record mode passes one
+ *        field whose rows are whole per-token records (ids, weights, hidden,
+ *        scales at 16-byte aligned offsets, as the per-token tensors are
+ *        packed in the vLLM branch compare ds-exp-2...ds-exp-ag,
+ *        moe_allgather.cu make_desc).
+ *   pos  (device, [N, K] row-major) rows from moe_get_layout. pos == NULL
+ *        means the identity pos[t] = t and requires K == 1: that call packs
+ *        separate tensors into records or unpacks records into tensors.
+ *
+ * Rows no pair maps to are left untouched. Two pairs must not share a row
+ * (moe_get_layout guarantees it). Alignment: row_bytes, both strides and
+ * both pointers must be multiples of 4; when all of them are multiples of
+ * 16 (every field), the copy runs in 16-byte vectors. Errors: MOE_ERR_ARG,
+ * MOE_ERR_LIMIT, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N, int32_t K,
+                 const int32_t* pos, hipStream_t stream);
+
+/*
+ * Combine. For every token t < N and h < Hc:
+ *     acc = +0.0f
+ *     for k = 0 .. K-1 with p = pos[t*K+k] >= 0:
+ *         acc = fmaf(w[t*w_row_stride + k], float(y[p*y_row_stride + h]), acc)
+ *     out[t*out_row_stride + h] = bf16(acc), rounded to nearest even.
+ * fp32 accumulation in a fixed order with one rounding to bf16 at the end,
+ * as the reduction of the vLLM branch compare ds-exp-2...ds-exp-ag
+ * (moe_reduce_scatter.cu, POLL + REDUCE phase); fp32 top-k weights scale the
+ * expert outputs as in DeepEP's low_latency_combine (deep_ep.cpp). The
+ * result goes straight into the caller's buffer with no staging copy (vLLM
+ * PR 49194, "Eliminate staging from NCCL symmetric reduce-scatter"). A token
+ * whose pairs are all masked gets +0.
+ *
+ *   y    (device, bf16 bits) expert outputs, rows as given by pos,
+ *        y_row_stride in elements.
+ *   w    (device, fp32) top-k weights [N, K], w_row_stride in elements
+ *        (>= K; the weights may sit inside per-token records).
+ *   pos  (device, int32 [N, K] row-major) rows from moe_get_layout.
+ *   out  (device, bf16 bits) [N, Hc], out_row_stride in elements.
+ *
+ * Alignment: y, out and their strides (in bytes) multiples of 4 and Hc even;
+ * when they are multiples of 16 and Hc of 8, the kernel moves 16-byte
+ * vectors. w and pos 4-byte aligned. Limits: 1 <= K <= 32, Hc >= 0.
+ * Errors: MOE_ERR_ARG, MOE_ERR_LIMIT, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_combine(const void* y, int64_t y_row_stride, const float* w, int64_t w_row_stride,
+                const int32_t* pos, int32_t N, int32_t K, int32_t Hc, void* out,
+                int64_t out_row_stride, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GET_H */

@@ -1,0 +1,158 @@
+"""The C-ABI library loads and exports every symbol include/*.h declares, and
+argument validation rejects bad calls before anything touches a GPU (CPU
+only: none of these calls reaches a launch)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("moe_get_layout", "moe_dispatch", "moe_combine", "moe_layout_workspace_bytes",
+              "moe_required_capacity", "moe_last_error", "moe_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import combine_moe_get_amd as m
+
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(_declared_functions()) <= exported
+
+
+def test_build_targets_gfx950_only():
+    from combine_moe_get_amd import build
+
+    arch = [f for f in build.CFLAGS if f.startswith("--offload-arch")]
+    assert arch == ["--offload-arch=gfx950"]
+    assert "-ffp-contract=off" in build.CFLAGS and "-packed-fp32-ops" in build.CFLAGS
+    assert not any("fast-math" in f and not f.startswith("-fno-") for f in build.CFLAGS)
+
+
+def test_header_compiles_as_c():
+    src = '#include "moe_get.h"\nint main(void){ return moe_version() > 0 ? 0 : 1; }\n'
+    r = subprocess.run(["gcc", "-fsyntax-only", "-x", "c", "-std=c11", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import combine_moe_get_amd as m
+
+    return m
+
+
+def test_version_and_sizes(lib):
+    assert lib.version() >= 100
+    assert lib.moe_required_capacity(4096, 8, 256, 1) == 32768
+    assert lib.moe_required_capacity(4, 2, 3, 2) == 11
+    assert lib.moe_required_capacity(-1, 8, 256, 1) == -1
+    ws = lib.moe_layout_workspace_bytes(4096, 8, 256)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.moe_layout_workspace_bytes(1, 33, 8) == 0
+    assert lib.moe_layout_workspace_bytes(1, 8, 1025) == 0
+    # the workspace stays small for every supported size
+    for E in (1, 64, 256, 1024):
+        for N in (0, 1, 4096, 262144):
+            assert lib.moe_layout_workspace_bytes(N, 8, E) <= 1 << 20
+
+
+def _err(lib):
+    return lib._lib.moe_last_error().decode()
+
+
+def test_layout_validation(lib):
+    L = lib._lib
+    P = 0x1000  # a fake, aligned pointer: validation must fail before any use
+    ws = lib.moe_layout_workspace_bytes(8, 8, 64)
+    cases = [
+        ((P, 8, -1, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 0, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 33, 64, 1, P, P, P, P, 264, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 1025, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 64, 0, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 4, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),      # stride < K
+        ((0, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),      # NULL ids
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 63, P, ws, 0, 0), lib.MOE_ERR_CAPACITY),
+        ((P, 8, 8, 8, 64, 2, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_CAPACITY), # padding room
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, ws, 0, 0), lib.MOE_ERR_WORKSPACE),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws - 4, 0, 0), lib.MOE_ERR_WORKSPACE),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P + 16, ws, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 1 << 31, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+    ]
+    for args, code in cases:
+        assert L.moe_get_layout(*args) == code, (args, _err(lib))
+        assert _err(lib)
+
+
+def _fields(lib, specs):
+    arr = (lib.moe_field * len(specs))()
+    for i, s in enumerate(specs):
+        arr[i] = lib.moe_field(*s)
+    return arr
+
+
+def test_dispatch_validation(lib):
+    L = lib._lib
+    P = 0x10000
+    good = (P, 64, P * 2, 64, 64)
+    f = _fields(lib, [good])
+    assert L.moe_dispatch(f, 0, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(f, 5, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(None, 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(f, 1, -1, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(f, 1, 4, 33, P, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_dispatch(f, 1, 4, 2, 0, 0) == lib.MOE_ERR_ARG         # identity needs K == 1
+    assert L.moe_dispatch(f, 1, 4, 2, P + 1, 0) == lib.MOE_ERR_ALIGN
+    for bad in [(P + 2, 64, P * 2, 64, 64), (P, 66, P * 2, 64, 64), (P, 64, P * 2, 64, 62),
+                (P, 64, P * 2 + 6, 64, 64)]:
+        assert L.moe_dispatch(_fields(lib, [bad]), 1, 4, 2, P, 0) == lib.MOE_ERR_ALIGN, bad
+    assert L.moe_dispatch(_fields(lib, [(P, 32, P * 2, 64, 64)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(_fields(lib, [(P, 64, P * 2, 32, 64)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(_fields(lib, [(0, 64, P * 2, 64, 64)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(_fields(lib, [(P, -1, P, 64, -16)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
+    # nothing to copy: returns before any launch
+    assert L.moe_dispatch(f, 1, 0, 2, P, 0) == lib.MOE_OK
+    assert L.moe_dispatch(_fields(lib, [(P, 64, P, 64, 0)]), 1, 4, 2, P, 0) == lib.MOE_OK
+
+
+def test_combine_validation(lib):
+    L = lib._lib
+    P = 0x10000
+    assert L.moe_combine(P, 64, P, 8, P, -1, 8, 64, P, 64, 0) == lib.MOE_ERR_ARG
+    assert L.moe_combine(P, 64, P, 8, P, 4, 0, 64, P, 64, 0) == lib.MOE_ERR_ARG
+    assert L.moe_combine(P, 64, P, 8, P, 4, 33, 64, P, 64, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_combine(0, 64, P, 8, P, 4, 8, 64, P, 64, 0) == lib.MOE_ERR_ARG
+    assert L.moe_combine(P, 64, P, 7, P, 4, 8, 64, P, 64, 0) == lib.MOE_ERR_ARG     # w stride < K
+    assert L.moe_combine(P, 32, P, 8, P, 4, 8, 64, P, 64, 0) == lib.MOE_ERR_ARG     # y stride < Hc
+    assert L.moe_combine(P, 64, P, 8, P, 4, 8, 63, P, 64, 0) == lib.MOE_ERR_ALIGN   # odd Hc
+    assert L.moe_combine(P + 2, 64, P, 8, P, 4, 8, 64, P, 64, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_combine(P, 64, P + 2, 8, P, 4, 8, 64, P, 64, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_combine(P, 64, P, 8, P, 0, 8, 64, P, 64, 0) == lib.MOE_OK          # N = 0
+    assert L.moe_combine(P, 64, P, 8, P, 4, 8, 0, P, 64, 0) == lib.MOE_OK           # Hc = 0
+    assert _err(lib) == ""

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded
+inputs, through the C ABI (via the ctypes binding).
+
+Bar: layout and dispatch bit-exact; combine within 1 bf16 ulp (ulp distance
+on the ordered bf16 encoding, +0 == -0), 0 expected because both sides run
+the same fp32 fma chain in k order and round once to nearest even.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+import oracle
+from _util import bf16_ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+ULP_TOL = 1
+
+
+@pytest.fixture(scope="module")
+def mg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_moe_get_amd as m
+
+    return m
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def host_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def check_layout(mg, lay, ids_np, E, align=1, cap=None):
+    torch.cuda.synchronize()
+    c, o, p, rp, s = oracle.layout(ids_np, E, align, cap)
+    assert np.array_equal(host(lay.counts), c)
+    assert np.array_equal(host(lay.offsets), o)
+    assert np.array_equal(host(lay.pos), p)
+    assert np.array_equal(host(lay.row_pair), rp)
+    assert int(host(lay.status)[0]) == s
+    return p
+
+
+def check_combine(out_d, y_bits, w_np, pos_np):
+    ref = oracle.combine(y_bits, np.ascontiguousarray(w_np), pos_np)
+    got = host_bf16(out_d)
+    d = bf16_ulp_diff(got, ref)
+    nz = int((d != 0).sum())
+    say(f"combine max ulp {int(d.max(initial=0))}, nonzero {nz} of {d.size}")
+    assert d.max(initial=0) <= ULP_TOL
+    return nz
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed"])
+def test_named_workload(mg, name):
+    wl = mw.make(name)
+    say(f"workload={name} seed={wl.seed} N={wl.N} K={wl.K} E={wl.E} Hc={wl.Hc}")
+    ids_d = dev(wl.ids)
+    lay = mg.layout(ids_d, wl.E)
+    pos = check_layout(mg, lay, wl.ids, wl.E)
+
+    srcs = [a for _, a in wl.fields]
+    srcs_d = [dev(a) for a in srcs]
+    dsts_d = [torch.full((lay.cap, a.shape[1]), 0xA5, dtype=torch.uint8, device="cuda") for a in srcs]
+    mg.moe_dispatch(srcs_d, dsts_d, lay.pos, wl.K)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(srcs, pos, wl.K, fill=0xA5)
+    for f, (r, d) in enumerate(zip(ref, dsts_d)):
+        assert np.array_equal(host(d), r), f"field {f}"
+
+    y = wl.y()
+    out = mg.combine(dev_bf16(y), dev(wl.weights), lay)
+    nz = check_combine(out, y, wl.weights, pos)
+    assert nz == 0
+
+    if name == "skewed":
+        # identity experts: feed the dispatched bf16 hidden rows back as y
+        yid = dsts_d[0].view(torch.bfloat16)
+        out2 = mg.combine(yid, dev(wl.weights), lay)
+        check_combine(out2, host_bf16(yid), wl.weights, pos)
+
+
+@pytest.mark.timeout(600)
+def test_large_packed_records(mg):
+    wl = mw.make("large")
+    say(f"workload=large seed={wl.seed} N={wl.N} records={wl.records.shape}")
+    rec_d = dev(wl.records)
+    ids_d = rec_d.view(torch.int32)[:, : wl.K]          # strided view, stride 1024
+    w_d = rec_d.view(torch.float32)[:, 8 : 8 + wl.K]
+    lay = mg.layout(ids_d, wl.E)
+    pos = check_layout(mg, lay, wl.ids, wl.E)
+    recv = torch.empty((lay.cap, wl.records.shape[1]), dtype=torch.uint8, device="cuda")
+    mg.moe_dispatch([rec_d], [recv], lay.pos, wl.K)
+    torch.cuda.synchronize()
+    (ref,) = oracle.dispatch([wl.records], pos, wl.K)
+    assert np.array_equal(host(recv), ref)
+    del ref, recv
+    say("large: drawing expert outputs")
+    y = wl.y()
+    out = mg.combine(dev_bf16(y), w_d, lay)
+    assert check_combine(out, y, wl.weights, pos) == 0
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.choice([1, 8, 64, 256, 1024]))
+    K = int(rng.choice([1, 2, 4, 8, 8, 3, 32]))
+    N = int(rng.choice([0, 1, 7, 64, 333, 1000, 4096]))
+    if N * K > 40000:
+        N = 40000 // K
+    row_bytes = tuple(int(b) for b in rng.choice([16, 48, 112, 4, 12, 4 * K], size=int(rng.integers(1, 5))))
+    hc = int(rng.choice([8, 64, 200, 2, 6, 7168]))
+    if hc == 7168:
+        N = min(N, 256)
+    align = int(rng.choice([1, 1, 2, 4, 16]))
+    mask = float(rng.choice([0.0, 0.1, 0.5, 1.0]))
+    bad = float(rng.choice([0.0, 0.0, 0.02]))
+    wl = mw.make_random(seed, N, K, E, hc=hc, row_bytes=row_bytes, mask_frac=mask,
+                        bad_frac=bad, distinct=bool(rng.integers(0, 2)))
+    extra = int(rng.choice([0, 0, 5]))
+    return wl, align, extra
+
+
+def test_random_stress(mg):
+    """Seeds 1000..1199: random sizes, masks, out-of-range ids, alignment,
+    capacity slack, 4-byte and 16-byte payloads, odd widths."""
+    for seed in range(1000, 1200):
+        wl, align, extra = _random_case(seed)
+        N, K, E = wl.N, wl.K, wl.E
+        cap = mg.moe_required_capacity(N, K, E, align) + extra
+        say(f"seed={seed} N={N} K={K} E={E} align={align} cap={cap} "
+            f"rows={[a.shape[1] for _, a in wl.fields]} Hc={wl.Hc}")
+        lay = mg.layout(dev(wl.ids), E, align=align, cap=cap)
+        pos = check_layout(mg, lay, wl.ids, E, align, cap)
+        srcs = [a for _, a in wl.fields]
+        dsts_d = [torch.full((cap, a.shape[1]), 0x5A, dtype=torch.uint8, device="cuda") for a in srcs]
+        mg.moe_dispatch([dev(a) for a in srcs], dsts_d, lay.pos, K)
+        torch.cuda.synchronize()
+        for r, d in zip(oracle.dispatch(srcs, pos, K, rows=cap, fill=0x5A), dsts_d):
+            assert np.array_equal(host(d), r)
+        rng = np.random.default_rng(seed + 1)
+        y = mw.bf16_bits_from_f32(rng.standard_normal((max(cap, 1), wl.Hc)).astype(np.float32))
+        out = torch.empty((N, wl.Hc), dtype=torch.bfloat16, device="cuda")
+        mg.moe_combine(dev_bf16(y), dev(wl.weights), lay.pos, out)
+        check_combine(out, y, wl.weights, pos)
+
+
+def test_strided_views_and_untouched_padding(mg):
+    rng = np.random.default_rng(7)
+    N, K, E, Hc = 300, 4, 16, 64
+    ids_full = rng.integers(-1, E, size=(N, 12)).astype(np.int32)
+    ids = ids_full[:, 2:2 + K]                         # row stride 12
+    lay = mg.layout(dev(ids_full)[:, 2:2 + K], E)
+    pos = check_layout(mg, lay, ids, E)
+    y = mw.bf16_bits_from_f32(rng.standard_normal((N * K, Hc + 8)).astype(np.float32))
+    y_d = dev_bf16(y)[:, :Hc]                          # y row stride Hc + 8
+    w_full = rng.standard_normal((N, 2 * K)).astype(np.float32)
+    w_d = dev(w_full)[:, K:]                           # w row stride 2K
+    out_full = torch.full((N, Hc + 16), 1.5, dtype=torch.bfloat16, device="cuda")
+    mg.moe_combine(y_d, w_d, lay.pos, out_full[:, :Hc])
+    torch.cuda.synchronize()
+    check_combine(out_full[:, :Hc], np.ascontiguousarray(y[:, :Hc]), w_full[:, K:], pos)
+    assert (out_full[:, Hc:] == 1.5).all()
+
+
+def test_pack_unpack_and_record_mode(mg):
+    wl = mw.make("tiny")
+    srcs_d = [dev(a) for _, a in wl.fields]
+    rec = mg.pack_records(srcs_d)
+    torch.cuda.synchronize()
+    offs, rb = mg.record_offsets([a.shape[1] for _, a in wl.fields])
+    assert rb == 4096
+    ref = np.zeros((wl.N, rb), np.uint8)
+    oracle.dispatch([a for _, a in wl.fields], None, 1,
+                    dsts=[ref[:, o:o + a.shape[1]] for o, (_, a) in zip(offs, wl.fields)])
+    assert np.array_equal(host(rec), ref)
+    back = mg.unpack_records(rec, srcs_d)
+    for a, b in zip(srcs_d, back):
+        assert torch.equal(a, b)
+    lay = mg.layout(dev(wl.ids), wl.E)
+    (drec,) = mg.dispatch([rec], lay)
+    dsep = mg.dispatch(srcs_d, lay)
+    for o, d in zip(offs, dsep):
+        assert torch.equal(drec[:, o:o + d.shape[1]], d)
+
+
+def test_edge_cases(mg):
+    # N = 0 with spare capacity: empty results, every row marked unused
+    lay = mg.layout(torch.zeros((0, 8), dtype=torch.int32, device="cuda"), 16, cap=10)
+    torch.cuda.synchronize()
+    assert (lay.counts == 0).all() and (lay.offsets == 0).all()
+    assert (lay.row_pair == -1).all() and int(lay.status[0]) == 0
+    # all masked
+    ids = np.full((50, 8), -1, np.int32)
+    lay = mg.layout(dev(ids), 32)
+    check_layout(mg, lay, ids, 32)
+    out = mg.combine(torch.ones((400, 16), dtype=torch.bfloat16, device="cuda"),
+                     torch.ones((50, 8), device="cuda"), lay)
+    torch.cuda.synchronize()
+    assert (host_bf16(out) == 0).all()                 # +0, not -0
+    # E = 1, K = 1, K = 32, E = 1024 with hot experts
+    rng = np.random.default_rng(8)
+    for (N, K, E) in [(100, 1, 1), (100, 8, 1), (1000, 1, 300), (129, 32, 1024), (5000, 8, 1024)]:
+        ids = rng.integers(0, min(E, 3) if E > 3 else E, size=(N, K)).astype(np.int32)
+        say(f"edge N={N} K={K} E={E}")
+        lay = mg.layout(dev(ids), E)
+        check_layout(mg, lay, ids, E)
+
+
+def test_non_finite_values(mg):
+    """inf and NaN propagate as in the oracle (any NaN payload counts as NaN)."""
+    N, K, Hc = 4, 2, 16
+    ids = np.array([[0, 1], [1, 0], [0, -1], [1, 1]], np.int32)
+    lay = mg.layout(dev(ids), 2)
+    pos = check_layout(mg, lay, ids, 2)
+    y = np.full((N * K, Hc), 0x3F80, np.uint16)        # 1.0
+    y[0, 0] = 0x7F80                                   # +inf
+    y[1, 1] = 0xFF80                                   # -inf
+    y[2, 2] = 0x7FC1                                   # NaN
+    y[0, 3], y[1, 3] = 0x7F80, 0xFF80                  # inf - inf -> NaN
+    y[3, 4] = 0x7F7F                                   # max finite: overflow in the sum
+    w = np.array([[1, 1], [1, 1], [1, 1], [2, 2]], np.float32)
+    out = host_bf16(mg.combine(dev_bf16(y), dev(w), lay))
+    ref = oracle.combine(y, w, pos)
+    nan_o = ((out & 0x7F80) == 0x7F80) & ((out & 0x7F) != 0)
+    nan_r = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+    assert np.array_equal(nan_o, nan_r) and nan_r.any()
+    assert np.array_equal(out[~nan_o], ref[~nan_r])
+
+
+def test_non_default_stream(mg):
+    wl = mw.make("decode")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ids_d = dev(wl.ids)
+        lay = mg.layout(ids_d, wl.E)
+        srcs_d = [dev(a) for _, a in wl.fields]
+        dsts = mg.dispatch(srcs_d, lay)
+        y = wl.y()
+        out = mg.combine(dev_bf16(y), dev(wl.weights), lay)
+    s.synchronize()
+    pos = check_layout(mg, lay, wl.ids, wl.E)
+    for r, d in zip(oracle.dispatch([a for _, a in wl.fields], pos, wl.K), dsts):
+        assert np.array_equal(host(d), r)
+    check_combine(out, y, wl.weights, pos)
+
+
+def test_graph_capture_replay(mg):
+    """layout + dispatch + combine captured once and replayed on new inputs
+    (eager work and a sync between replays); every replay checked."""
+    N, K, E, Hc = 256, 8, 64, 512
+    ids_s = torch.zeros((N, K), dtype=torch.int32, device="cuda")
+    x_s = torch.zeros((N, 1024), dtype=torch.uint8, device="cuda")
+    w_s = torch.zeros((N, K), dtype=torch.float32, device="cuda")
+    y_s = torch.zeros((N * K, Hc), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device="cuda")
+    lay = mg.Layout(torch.empty(E, dtype=torch.int32, device="cuda"),
+                    torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                    torch.empty((N, K), dtype=torch.int32, device="cuda"),
+                    torch.empty(N * K, dtype=torch.int32, device="cuda"),
+                    torch.empty(1, dtype=torch.int32, device="cuda"), E, 1)
+    recv = torch.empty((N * K, 1024), dtype=torch.uint8, device="cuda")
+    out = torch.empty((N, Hc), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        mg.moe_get_layout(ids_s, E, 1, lay.counts, lay.offsets, lay.pos, lay.row_pair, ws,
+                          lay.status)
+        mg.moe_dispatch([x_s], [recv], lay.pos, K)
+        mg.moe_combine(y_s, w_s, lay.pos, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                          # warm up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        say(f"graph replay {rep}")
+        rng = np.random.default_rng(50 + rep)
+        ids = mw.uniform_distinct_ids(rng, N, K, E)
+        ids[rng.random((N, K)) < 0.1] = -1
+        x = rng.integers(0, 256, size=(N, 1024), dtype=np.uint8)
+        w = rng.standard_normal((N, K)).astype(np.float32)
+        y = mw.bf16_bits_from_f32(rng.standard_normal((N * K, Hc)).astype(np.float32))
+        ids_s.copy_(dev(ids))
+        x_s.copy_(dev(x))
+        w_s.copy_(dev(w))
+        y_s.copy_(dev_bf16(y))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        pos = check_layout(mg, lay, ids, E)
+        (ref,) = oracle.dispatch([x], pos, K, rows=N * K)
+        got = host(recv)
+        used = host(lay.row_pair) >= 0
+        assert np.array_equal(got[used], ref[used])
+        check_combine(out, y, w, pos)
+        _ = (y_s.float() * 2).sum().item()             # unrelated eager work between replays
+
+
+def test_errors_raise(mg):
+    ids = torch.zeros((4, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(mg.MoeError) as e:
+        mg.layout(ids, 2, cap=7)
+    assert e.value.code == mg.MOE_ERR_CAPACITY
+    with pytest.raises(mg.MoeError) as e:
+        mg.layout(ids, 2000)
+    assert e.value.code == mg.MOE_ERR_LIMIT
+    lay = mg.layout(ids, 2)
+    y = torch.zeros((8, 7), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mg.MoeError) as e:
+        mg.combine(y, torch.ones((4, 2), device="cuda"), lay)
+    assert e.value.code == mg.MOE_ERR_ALIGN
+    x = torch.zeros((4, 6), dtype=torch.uint8, device="cuda")
+    with pytest.raises(mg.MoeError) as e:
+        mg.dispatch([x], lay)
+    assert e.value.code == mg.MOE_ERR_ALIGN
