@@ -99,6 +99,8 @@ def _rows(t: torch.Tensor, name: str) -> Tuple[int, int]:
     """(pointer, row stride in elements) of a 2-D tensor with contiguous rows."""
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.numel() == 0:
+        return _dev(t, name), t.shape[1]
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} rows must be contiguous")
     return _dev(t, name), t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])

@@ -80,7 +80,7 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     if (K > MOE_MAX_TOPK) return fail(MOE_ERR_LIMIT, "moe_dispatch: K=%d > %d", K, MOE_MAX_TOPK);
     if ((int64_t)N * K >= ((int64_t)1 << 31))
         return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K must be below 2^31");
-    if (pos == nullptr && K != 1)
+    if (pos == nullptr && K != 1 && N > 0)
         return fail(MOE_ERR_ARG, "moe_dispatch: pos == NULL (identity) requires K == 1");
     if (!aligned(pos, 4)) return fail(MOE_ERR_ALIGN, "moe_dispatch: pos must be 4-byte aligned");
 

@@ -343,8 +343,8 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
     if (workspace == nullptr || workspace_bytes < ws)
         return fail(MOE_ERR_WORKSPACE, "moe_get_layout: workspace of %zu bytes needed, got %zu%s",
                     ws, workspace_bytes, workspace ? "" : " (NULL)");
-    if (!aligned(workspace, 256))
-        return fail(MOE_ERR_ALIGN, "moe_get_layout: workspace must be 256-byte aligned");
+    if (!aligned(workspace, 4))
+        return fail(MOE_ERR_ALIGN, "moe_get_layout: workspace must be 4-byte aligned");
 
     clear_launch_error();
     int32_t* H = static_cast<int32_t*>(workspace);

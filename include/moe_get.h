@@ -97,7 +97,7 @@ size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E);
  *   cap             rows of the receive buffer; must be at least
  *        moe_required_capacity(N, K, E, align) and below 2^31.
  *   workspace       (device) at least moe_layout_workspace_bytes(N, K, E)
- *        bytes, 256-byte aligned; not shared with a concurrent call.
+ *        bytes, 4-byte aligned; not shared with a concurrent call.
  *   status          (device, out, may be NULL) number of ids >= E.
  *
  * Limits: 1 <= K <= 32, 1 <= E <= 1024, N >= 0, N*K < 2^31. Pointers must be

@@ -100,7 +100,7 @@ def test_layout_validation(lib):
         ((P, 8, 8, 8, 64, 2, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_CAPACITY), # padding room
         ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, ws, 0, 0), lib.MOE_ERR_WORKSPACE),
         ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws - 4, 0, 0), lib.MOE_ERR_WORKSPACE),
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P + 16, ws, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P + 2, ws, 0, 0), lib.MOE_ERR_ALIGN),
         ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ALIGN),
         ((P, 8, 8, 8, 64, 1, P, P, P, P, 1 << 31, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
         ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
