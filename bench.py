@@ -60,6 +60,137 @@ def traffic_entry(kernel, workload):
     return e
 
 
+KERNEL_SOURCES = {
+    "combine_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
+    "dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
+    "layout_hist": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
+    "layout_assign": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    for f in files:
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _per_kernel(directory, counter):
+    """{short kernel name: [value per dispatch]} for one counter."""
+    out = {}
+    for r in _counter_rows(directory):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        key = next((k for k in list(KERNEL_SOURCES) + [COPY_KERNEL] if k in name), None)
+        if key is not None:
+            out.setdefault(key, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, workload, command):
+    """HBM traffic per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, both in KiB per dispatch), each scaled by what the same
+    counter reads for the 2 GiB device copy of copy_bandwidth()."""
+    fetch, write = _per_kernel(fetch_dir, "FETCH_SIZE"), _per_kernel(write_dir, "WRITE_SIZE")
+    known_kib = COPY_BYTES / 1024
+
+    def copy_median(vals):
+        # copy_bandwidth() is the only device-to-device copy of the run: its
+        # launches must read alike, whatever scale the counter has.
+        if len(vals) < 3:
+            raise SystemExit(f"need the {COPY_KERNEL} launches of copy_bandwidth(), got {vals}")
+        m = float(np.median(vals))
+        if max(abs(v - m) for v in vals) > 0.1 * m:
+            raise SystemExit(f"{COPY_KERNEL} launches disagree: {vals}")
+        return m
+
+    fscale = known_kib / copy_median(fetch.get(COPY_KERNEL, []))
+    wscale = known_kib / copy_median(write.get(COPY_KERNEL, []))
+    result = {}
+    lines = ["| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated HBM bytes / launch |",
+             "|---|---|---|---|---|"]
+    for k, src in KERNEL_SOURCES.items():
+        if k not in fetch or k not in write:
+            continue
+        f, w = float(np.mean(fetch[k])), float(np.mean(write[k]))
+        b = (f * fscale + w * wscale) * 1024
+        result[f"{k}/{workload}"] = {
+            "fetch_kib_per_launch": round(f, 1), "write_kib_per_launch": round(w, 1),
+            "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
+            "bytes_per_launch": int(round(b)), "launches": len(fetch[k]),
+            "source_sha256_16": source_hash(src), "command": command,
+        }
+        lines.append(f"| {k} | {len(fetch[k])} | {f:.1f} | {w:.1f} | {b:.0f} |")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    old = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            old = json.load(fh)
+    old.update(result)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(old, fh, indent=1, sort_keys=True)
+    print(f"copy calibration: FETCH x{fscale:.4f}, WRITE x{wscale:.4f} "
+          f"({COPY_KERNEL}, {COPY_BYTES} B read and written per launch)")
+    print("\n".join(lines))
+
+
+class HipEvents:
+    """Timing-only HIP events, created through the HIP runtime torch loaded,
+    with hipEventDisableSystemFence: recording one skips the system-scope
+    cache write-back and invalidate an ordinary event record performs, so
+    per-op timestamps inside the timed loop barely perturb it."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch):
+        import ctypes
+
+        self.ct = ctypes
+        lib = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.L = ctypes.CDLL(lib)
+        self.L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.L.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.L.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def ms(self, a, b):
+        ms = self.ct.c_float()
+        self.L.hipEventSynchronize(b)
+        rc = self.L.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def close(self):
+        for ev in self.events:
+            self.L.hipEventDestroy(ev)
+        self.events = []
+
+
 class BufferSet:
     """Device inputs and outputs of one step."""
 
@@ -161,7 +292,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ref", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "bench into profiles/traffic.json and exit (no GPU needed)")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiled command, recorded next to the figures")
     args = ap.parse_args()
+    if args.traffic_from:
+        summarize_traffic(*args.traffic_from, args.config, args.traffic_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -195,23 +334,38 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        fns = calls[i % len(calls)]
-        e = ev[i]
-        e[0].record(stream)
-        for j, (fn, a) in enumerate(fns):
-            if fn(*a) != 0:
-                raise mg.MoeError(-6, mg._lib.moe_last_error().decode())
-            e[j + 1].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    per_op = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
-    op_ms = per_op.mean(axis=0)
+    hev = HipEvents(torch)
+    sh = stream.cuda_stream
+
+    def timed_pass(op_events):
+        """K steps between two synchronizations; with op_events, a
+        timing-only event is also recorded before and after every op."""
+        ev = [[hev.create() for _ in range(4)] for _ in range(args.steps)] if op_events else None
+        t0, t1 = hev.create(), hev.create()
+        torch.cuda.synchronize()
+        hev.record(t0, sh)
+        for i in range(args.steps):
+            if op_events:
+                hev.record(ev[i][0], sh)
+            for j, (fn, a) in enumerate(calls[i % len(calls)]):
+                if fn(*a) != 0:
+                    raise mg.MoeError(-6, mg._lib.moe_last_error().decode())
+                if op_events:
+                    hev.record(ev[i][j + 1], sh)
+        hev.record(t1, sh)
+        torch.cuda.synchronize()
+        step_ms = hev.ms(t0, t1) / args.steps
+        op = None
+        if op_events:
+            op = np.array([[hev.ms(e[j], e[j + 1]) for j in range(3)] for e in ev]).mean(axis=0)
+        return step_ms, op
+
+    # The headline figure: whole steps, nothing recorded between the ops.
+    ms_per_step, _ = timed_pass(False)
+    # Per-op times (and the combine kernel's duration for the roofline) from
+    # a second timed pass with an event between the ops.
+    ms_per_step_op_events, op_ms = timed_pass(True)
+    hev.close()
 
     b_lay, b_dis, b_com = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap)
     total = b_lay + b_dis + b_com
@@ -241,6 +395,7 @@ def main():
         },
         "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step_with_op_events": round(ms_per_step_op_events, 5),
         "per_op_us": {"layout": round(op_ms[0] * 1e3, 2), "dispatch": round(op_ms[1] * 1e3, 2),
                       "combine": round(op_ms[2] * 1e3, 2)},
         "per_op_gbs": {"layout": round(b_lay / (op_ms[0] * 1e-3) / 1e9, 1),

@@ -47,11 +47,14 @@ struct Words {
 template <int W>
 __device__ __forceinline__ Words<W> load_words(const uint16_t* p) {
     Words<W> r;
+    // Each expert-output element is read exactly once: non-temporal loads
+    // keep the stream from displacing other data in L2 and the last-level
+    // cache.
     if constexpr (W == 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else {
-        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+        r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     }
     return r;
 }

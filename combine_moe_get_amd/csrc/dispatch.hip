@@ -8,11 +8,18 @@
 // granularity, as the tensors packed by make_desc in the vLLM branch
 // compare ds-exp-2...ds-exp-ag (moe_allgather.cu).
 //
-// Launch shape: one wave per (token, 64-vector segment of the concatenated
-// fields). The token is wave-uniform, so its K receive rows are scalar loads;
-// each lane reads one vector of the source row once and stores it to the K
-// rows. Every load and store instruction of a wave covers 64 consecutive
-// vectors of one row (1 KiB with 16-byte vectors), so both sides coalesce.
+// Launch shape: one wave per (token, k, 64-vector segment of the
+// concatenated fields), segments of one receive row on consecutive waves.
+// Each lane loads one vector of the token's source row and stores it to the
+// pair's receive row; the K waves of a token re-read the same source bytes.
+// Workgroups are handed to the 8 XCDs round-robin, each XCD with its own L2,
+// so the kernel renumbers them: XCD x runs the x-th contiguous eighth of the
+// work, which keeps all waves of a token on one XCD and its re-reads in that
+// L2 (without this, measured source reads were 4x the source bytes). Every load and store instruction of a wave covers
+// 64 consecutive vectors of one row (1 KiB with 16-byte vectors). Measured
+// on MI355X at the prefill shape, this many-short-waves form writes faster
+// than one wave storing each loaded vector K times, and only with
+// non-temporal stores.
 #include "internal.hpp"
 
 namespace moe {
@@ -20,6 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
 
 struct DispatchArgs {
     const char* src[MOE_MAX_FIELDS];
@@ -37,12 +45,19 @@ struct DispatchArgs {
 template <typename VecT>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    const int32_t t = __builtin_amdgcn_readfirstlane((int32_t)(gw / a.segs));
-    if (t >= a.N) return;
-    const int32_t seg = (int32_t)(gw - (int64_t)t * a.segs);
+    // Logical workgroup: XCD (blockIdx % 8) takes a contiguous eighth. The
+    // grid is a multiple of 8, so this is a bijection on [0, gridDim.x).
+    const uint32_t per_xcd = gridDim.x / kXcds;
+    const uint32_t lb = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const uint32_t gw = lb * kWavesPerBlock + threadIdx.x / kWave;
+    const uint32_t pair = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);   // t*K + k
+    if (pair >= (uint32_t)a.N * (uint32_t)a.K) return;
+    const int32_t seg = (int32_t)(gw - pair * (uint32_t)a.segs);
     const int32_t v = seg * kWave + lane;
     if (v >= a.V) return;
+    const int32_t t = __builtin_amdgcn_readfirstlane(pair / (uint32_t)a.K);
+    const int32_t p = a.pos ? a.pos[pair] : t;
+    if (p < 0) return;
 
     // Which field this lane's vector belongs to, and its offset inside it.
     const int f1 = v >= a.vend[0], f2 = v >= a.vend[1], f3 = v >= a.vend[2];
@@ -53,17 +68,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a
     const int32_t v0 = f3 ? a.vend[2] : f2 ? a.vend[1] : f1 ? a.vend[0] : 0;
     const int64_t inner = (int64_t)(v - v0) * sizeof(VecT);
 
+    // Receive rows are written once and not read back by this pass:
+    // non-temporal stores stream them out instead of parking them as dirty
+    // lines in the caches, where the combine that follows would pay for the
+    // write-back.
     const VecT val = *reinterpret_cast<const VecT*>(src + (int64_t)t * ss + inner);
-    if (a.pos == nullptr) {
-        *reinterpret_cast<VecT*>(dst + (int64_t)t * ds + inner) = val;
-        return;
-    }
-    const int32_t* prow = a.pos + (int64_t)t * a.K;
-    for (int k = 0; k < a.K; ++k) {
-        const int32_t p = prow[k];
-        if (p < 0) continue;
-        *reinterpret_cast<VecT*>(dst + (int64_t)p * ds + inner) = val;
-    }
+    __builtin_nontemporal_store(val, reinterpret_cast<VecT*>(dst + (int64_t)p * ds + inner));
 }
 
 }  // namespace
@@ -127,11 +137,11 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     a.K = K;
     a.V = vend;
     a.segs = ceil_div<int32_t>(vend, kWave);
-    const int64_t waves = (int64_t)N * a.segs;
-    const int64_t blocks = ceil_div<int64_t>(waves, kWavesPerBlock);
-    if (blocks >= ((int64_t)1 << 31))
-        return fail(MOE_ERR_LIMIT, "moe_dispatch: launch of %lld workgroups too large",
-                    (long long)blocks);
+    const int64_t waves = (int64_t)N * K * a.segs;
+    if (waves >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K*segments=%lld waves must be below 2^31",
+                    (long long)waves);
+    const int64_t blocks = ceil_div<int64_t>(ceil_div<int64_t>(waves, kWavesPerBlock), kXcds) * kXcds;
     clear_launch_error();
     if (all16)
         dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a);

@@ -7,23 +7,25 @@
 // as written by mask_topk_ids (vLLM branch compare ds-exp-2...ds-exp-ag).
 // Rows inside one expert's segment follow ascending (t, k).
 //
-// Three launches on the caller's stream, no atomics deciding any order:
+// Two launches on the caller's stream, no atomics deciding any order:
 //   1. hist   -- each workgroup takes a contiguous chunk of pairs; each of
 //                its 4 waves a contiguous quarter. A wave finds the lanes that
 //                share an expert with one ballot per id bit, and the lowest
 //                such lane adds the group size to the wave's own LDS row.
 //                The workgroup writes its per-expert totals H[b][e].
-//   2. scan   -- one workgroup: per expert, the exclusive prefix of H over
-//                the chunks (in place), the totals (counts), and the
-//                exclusive scan of the aligned totals (offsets).
-//   3. assign -- each workgroup recounts its waves, turns the counts into
-//                per-wave bases (offsets[e] + chunk prefix + earlier waves),
-//                and walks its pairs again in order: the row of a pair is its
-//                wave's base for the expert plus the number of lower lanes in
-//                the same 64-pair step with that expert. Then all workgroups
+//   2. assign -- every workgroup reduces the whole (small) H matrix itself:
+//                per expert, the sum over earlier chunks and the total; an
+//                exclusive scan of the aligned totals gives the offsets
+//                (workgroup 0 also writes counts, offsets and status). It
+//                then recounts its waves, turns the counts into per-wave
+//                bases (offset + earlier chunks + earlier waves), and walks
+//                its pairs again in order: the row of a pair is its wave's
+//                base for the expert plus the number of lower lanes in the
+//                same 64-pair step with that expert. Finally all workgroups
 //                mark unused rows with -1.
-// Kernel boundaries are the only grid-wide ordering used, so the result does
-// not depend on scheduling.
+// The kernel boundary is the only grid-wide ordering used, so the result
+// does not depend on scheduling. H has at most 16384 entries, so the
+// redundant reduction costs each workgroup at most 64 loads per thread.
 #include "internal.hpp"
 
 namespace moe {
@@ -31,16 +33,13 @@ namespace {
 
 constexpr int kThreads = 256;              // hist / assign workgroup
 constexpr int kWaves = kThreads / kWave;   // 4
-constexpr int kScanThreads = 1024;
-constexpr int kScanRows = 16;              // chunk rows one scan thread holds
+constexpr int kHEntries = 16384;           // bound on chunks * padded experts
+constexpr int kMaxChunks = 64;
 constexpr int kPrefetch = 16;              // 64-pair steps of ids held in registers
 
 struct Plan {
     int32_t chunk;    // pairs per workgroup (multiple of kThreads)
     int32_t blocks;   // number of chunks
-    int32_t ecols;    // E padded to a power of two >= 64
-    int32_t lanes;    // scan threads per expert column
-    int32_t rows;     // chunk rows per scan thread
     int32_t nbits;    // ceil(log2(E))
 };
 
@@ -53,14 +52,12 @@ int32_t next_pow2(int32_t x) {
 Plan make_plan(int32_t N, int32_t K, int32_t E) {
     Plan p;
     const int64_t nk = (int64_t)N * K;
-    p.ecols = next_pow2(E) < kWave ? kWave : next_pow2(E);
-    p.lanes = kScanThreads / p.ecols;
-    const int64_t max_blocks = (int64_t)kScanRows * p.lanes;
+    const int32_t ecols = next_pow2(E) < kThreads ? kThreads : next_pow2(E);
+    const int64_t max_blocks = kHEntries / ecols < kMaxChunks ? kHEntries / ecols : kMaxChunks;
     int64_t chunk = ceil_div<int64_t>(ceil_div<int64_t>(nk, max_blocks), kThreads) * kThreads;
     if (chunk < kThreads) chunk = kThreads;
     p.chunk = (int32_t)chunk;
     p.blocks = (int32_t)ceil_div<int64_t>(nk, chunk);
-    p.rows = (int32_t)ceil_div<int64_t>(p.blocks, p.lanes);
     p.nbits = 0;
     while ((1 << p.nbits) < E) ++p.nbits;
     return p;
@@ -95,33 +92,63 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool valid, int
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
-// Adds this wave's per-expert counts over its quarter of the chunk into
-// cnt[wave*E + e]; returns the number of ids >= E it saw.
-__device__ __forceinline__ int32_t count_wave(const int32_t* __restrict__ ids, int64_t stride,
-                                              uint32_t nk, uint32_t K, int32_t E, int nbits,
-                                              uint32_t first, int steps, int32_t* cnt_row,
-                                              int lane) {
+// Loads the expert ids of 64-pair steps s0 .. s0+kPrefetch-1 of a wave's
+// quarter (-1 past the quarter or past the last pair). All loads are issued
+// before any is used.
+__device__ __forceinline__ void load_ids(int32_t (&e_reg)[kPrefetch],
+                                         const int32_t* __restrict__ ids, int64_t stride,
+                                         uint32_t nk, uint32_t K, uint32_t first, int s0,
+                                         int steps, int lane) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+        const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
+        e_reg[j] = (s0 + j < steps && i < nk) ? load_id(ids, stride, i, K) : -1;
+    }
+}
+
+// Adds one batch of steps to the wave's counts cnt_row[e]; returns the number
+// of ids >= E in the batch.
+__device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[kPrefetch], int s0,
+                                               int steps, int32_t E, int nbits, int32_t* cnt_row,
+                                               int lane) {
     int32_t bad = 0;
-    for (int s0 = 0; s0 < steps; s0 += kPrefetch) {
-        int32_t e_reg[kPrefetch];
 #pragma unroll
-        for (int j = 0; j < kPrefetch; ++j) {
-            const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
-            e_reg[j] = (s0 + j < steps && i < nk) ? load_id(ids, stride, i, K) : -1;
-        }
-#pragma unroll
-        for (int j = 0; j < kPrefetch; ++j) {
-            if (s0 + j < steps) {   // wave-uniform
-                const int32_t e = e_reg[j];
-                const bool valid = e >= 0 && e < E;
-                bad += __popcll(__ballot(e >= E));
-                const uint64_t peers = same_expert_lanes(e, valid, nbits);
-                if (valid && lane == __ffsll((long long)peers) - 1) cnt_row[e] += __popcll(peers);
-                __builtin_amdgcn_wave_barrier();
-            }
+    for (int j = 0; j < kPrefetch; ++j) {
+        if (s0 + j < steps) {   // wave-uniform
+            const int32_t e = e_reg[j];
+            const bool valid = e >= 0 && e < E;
+            bad += __popcll(__ballot(e >= E));
+            const uint64_t peers = same_expert_lanes(e, valid, nbits);
+            if (valid && lane == __ffsll((long long)peers) - 1) cnt_row[e] += __popcll(peers);
+            __builtin_amdgcn_wave_barrier();
         }
     }
     return bad;
+}
+
+// Gives every pair of one batch its row: the wave's running base for the
+// expert plus the number of lower lanes in the same step with that expert.
+__device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[kPrefetch], int s0, int steps,
+                                           int32_t E, int nbits, int32_t* base_row,
+                                           uint32_t first, uint32_t nk, int lane,
+                                           int32_t* __restrict__ pos,
+                                           int32_t* __restrict__ row_pair, int64_t cap) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+        if (s0 + j < steps) {   // wave-uniform
+            const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
+            const int32_t e = e_reg[j];
+            const bool valid = e >= 0 && e < E;
+            const uint64_t peers = same_expert_lanes(e, valid, nbits);
+            int32_t p = -1;
+            if (valid) p = base_row[e] + __popcll(peers & lanes_below(lane));
+            __builtin_amdgcn_wave_barrier();
+            if (valid && lane == __ffsll((long long)peers) - 1) base_row[e] += __popcll(peers);
+            __builtin_amdgcn_wave_barrier();
+            if (i < nk) pos[i] = p;
+            if (valid && p < cap) row_pair[p] = (int32_t)i;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void layout_hist(const int32_t* __restrict__ ids,
@@ -133,157 +160,195 @@ __global__ __launch_bounds__(kThreads) void layout_hist(const int32_t* __restric
     __shared__ int32_t wbad[kWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int quarter = chunk / kWaves;
+    const int steps = quarter / kWave;
+    const uint32_t first = (uint32_t)blockIdx.x * chunk + wave * quarter;
+
+    int32_t e_reg[kPrefetch];
+    load_ids(e_reg, ids, stride, nk, K, first, 0, steps, lane);
     for (int x = threadIdx.x; x < kWaves * E; x += kThreads) cnt[x] = 0;
     __syncthreads();
 
-    const int quarter = chunk / kWaves;
-    const uint32_t first = (uint32_t)blockIdx.x * chunk + wave * quarter;
-    const int32_t bad = count_wave(ids, stride, nk, K, E, nbits, first, quarter / kWave,
-                                   cnt + wave * E, lane);
+    int32_t* row = cnt + wave * E;
+    int32_t bad = count_batch(e_reg, 0, steps, E, nbits, row, lane);
+    for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
+        load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
+        bad += count_batch(e_reg, s0, steps, E, nbits, row, lane);
+    }
     if (lane == 0) wbad[wave] = bad;
     __syncthreads();
 
-    int32_t* row = H + (int64_t)blockIdx.x * E;
+    int32_t* out = H + (int64_t)blockIdx.x * E;
     for (int e = threadIdx.x; e < E; e += kThreads)
-        row[e] = cnt[e] + cnt[E + e] + cnt[2 * E + e] + cnt[3 * E + e];
+        out[e] = cnt[e] + cnt[E + e] + cnt[2 * E + e] + cnt[3 * E + e];
     if (threadIdx.x == 0) bad_out[blockIdx.x] = wbad[0] + wbad[1] + wbad[2] + wbad[3];
 }
 
-__global__ __launch_bounds__(kScanThreads) void layout_scan(int32_t* __restrict__ H,
-                                                            const int32_t* __restrict__ bad,
-                                                            int32_t blocks, int32_t E,
-                                                            int32_t ecols, int32_t lanes,
-                                                            int32_t rows, int32_t align,
-                                                            int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ status) {
-    __shared__ int32_t part[kScanThreads];
-    __shared__ int32_t scan[kScanThreads];
-    __shared__ int32_t sbad;
-    const int j = threadIdx.x;
-    const int e = j & (ecols - 1);
-    const int q = j / ecols;          // which slice of chunk rows
-    const int g0 = q * rows;
-
-    int32_t r[kScanRows];
-    int32_t sum = 0;
+// Exclusive scan over the W*64 threads of a workgroup of one value per
+// thread; returns the sum of the values of lower threads and leaves the
+// workgroup total in *total. Contains one __syncthreads.
+template <int W>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave_sums,
+                                                        int32_t* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int32_t x = v;
 #pragma unroll
-    for (int x = 0; x < kScanRows; ++x) {
-        const int g = g0 + x;
-        r[x] = (x < rows && g < blocks && e < E) ? H[(int64_t)g * E + e] : 0;
-        sum += r[x];
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
     }
-    part[j] = sum;
-    if (j == 0) sbad = 0;
+    if (lane == kWave - 1) wave_sums[wave] = x;
     __syncthreads();
-
-    int32_t before = 0, total = 0;
-    for (int x = 0; x < lanes; ++x) {
-        const int32_t v = part[x * ecols + e];
-        before += (x < q) ? v : 0;
-        total += v;
-    }
-    if (e < E) {
-        int32_t run = before;
+    int32_t before = 0, all = 0;
 #pragma unroll
-        for (int x = 0; x < kScanRows; ++x) {
-            const int g = g0 + x;
-            if (x < rows && g < blocks) {
-                H[(int64_t)g * E + e] = run;
-                run += r[x];
-            }
+    for (int w = 0; w < W; ++w) {
+        before += (w < wave) ? wave_sums[w] : 0;
+        all += wave_sums[w];
+    }
+    *total = all;
+    return before + x - v;
+}
+
+// Per expert e (columns tid, tid+256, ... of H): pairs in chunks before b
+// (before_s) and in all chunks (total_s). C columns per thread and at most
+// 64/C chunks, so every load is issued before the first sum.
+template <int C>
+__device__ __forceinline__ void reduce_chunks(const int32_t* __restrict__ H, int32_t blocks,
+                                              int32_t E, int b, int32_t* total_s,
+                                              int32_t* before_s) {
+    constexpr int R = kMaxChunks / C;
+    int32_t v[C][R];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int e = threadIdx.x + c * kThreads;
+#pragma unroll
+        for (int g = 0; g < R; ++g) v[c][g] = (e < E && g < blocks) ? H[(int64_t)g * E + e] : 0;
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int e = threadIdx.x + c * kThreads;
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int g = 0; g < R; ++g) {
+            before += (g < b) ? v[c][g] : 0;
+            total += v[c][g];
         }
-        if (q == 0) counts[e] = total;
+        if (e < E) {
+            total_s[e] = total;
+            before_s[e] = before;
+        }
     }
-
-    // Inclusive scan of the aligned totals over the expert columns.
-    const int64_t padded = (q == 0 && e < E) ? ((int64_t)total + align - 1) / align * align : 0;
-    if (j < ecols) scan[j] = (int32_t)padded;
-    __syncthreads();
-    for (int off = 1; off < ecols; off <<= 1) {
-        const int32_t v = (j < ecols && j >= off) ? scan[j - off] : 0;
-        __syncthreads();
-        if (j < ecols) scan[j] += v;
-        __syncthreads();
-    }
-    if (j < E) offsets[j + 1] = scan[j];
-    if (j == 0) offsets[0] = 0;
-
-    int32_t b = 0;
-    for (int g = j; g < blocks; g += kScanThreads) b += bad[g];
-    if (b) atomicAdd(&sbad, b);
-    __syncthreads();
-    if (j == 0 && status) *status = sbad;
 }
 
 __global__ __launch_bounds__(kThreads) void layout_assign(
     const int32_t* __restrict__ ids, int64_t stride, uint32_t nk, uint32_t K, int32_t E,
     int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ row_pair, int64_t cap) {
-    __shared__ int32_t cnt[kWaves * MOE_MAX_EXPERTS];
+    const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ status, int32_t* __restrict__ pos, int32_t* __restrict__ row_pair,
+    int64_t cap) {
+    __shared__ int32_t cnt[kWaves * MOE_MAX_EXPERTS];   // per-wave counts, then bases
+    __shared__ int32_t total_s[MOE_MAX_EXPERTS];       // valid pairs per expert
+    __shared__ int32_t start_s[MOE_MAX_EXPERTS];       // segment start (offsets[e])
+    __shared__ int32_t base[MOE_MAX_EXPERTS];          // pairs in earlier chunks, then chunk base
+    __shared__ int32_t wave_sums[kWaves];
+    __shared__ int32_t used_s;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int b = blockIdx.x;
+    const bool active = b < blocks;
+    const int quarter = chunk / kWaves;
+    const int steps = active ? quarter / kWave : 0;
+    const uint32_t first = (uint32_t)b * chunk + wave * quarter;
 
-    if (b < blocks) {
-        for (int x = threadIdx.x; x < kWaves * E; x += kThreads) cnt[x] = 0;
-        __syncthreads();
-        const int quarter = chunk / kWaves;
-        const int steps = quarter / kWave;
-        const uint32_t first = (uint32_t)b * chunk + wave * quarter;
-        int32_t* mine = cnt + wave * E;
-        count_wave(ids, stride, nk, K, E, nbits, first, steps, mine, lane);
-        __syncthreads();
+    // The ids of the first batch and the chunk histograms are fetched
+    // together; the ids stay in registers for both passes below.
+    int32_t e_first[kPrefetch];
+    load_ids(e_first, ids, stride, nk, K, first, 0, steps, lane);
+    if (E <= kThreads)
+        reduce_chunks<1>(H, blocks, E, b, total_s, base);
+    else if (E <= 2 * kThreads)
+        reduce_chunks<2>(H, blocks, E, b, total_s, base);
+    else
+        reduce_chunks<4>(H, blocks, E, b, total_s, base);
+    for (int x = threadIdx.x; x < kWaves * E; x += kThreads) cnt[x] = 0;
+    __syncthreads();
 
-        // Per-wave bases: expert offset + earlier chunks + earlier waves.
-        const int32_t* hrow = H + (int64_t)b * E;
-        for (int e = threadIdx.x; e < E; e += kThreads) {
-            int32_t run = offsets[e] + hrow[e];
+    // Offsets: exclusive scan of the aligned totals; thread i owns experts
+    // 4i .. 4i+3 (E <= 1024).
+    int32_t mine4[4];
+    int32_t sum4 = 0;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const int32_t c = cnt[w * E + e];
-                cnt[w * E + e] = run;
-                run += c;
+    for (int j = 0; j < 4; ++j) {
+        const int e = threadIdx.x * 4 + j;
+        const int32_t c = e < E ? total_s[e] : 0;
+        mine4[j] = (int32_t)(((int64_t)c + align - 1) / align * align);
+        sum4 += mine4[j];
+    }
+    int32_t used = 0;
+    int32_t run = block_exclusive_scan<kWaves>(sum4, wave_sums, &used);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = threadIdx.x * 4 + j;
+        if (e < E) {
+            if (b == 0) {
+                counts[e] = total_s[e];
+                offsets[e] = run;
             }
+            start_s[e] = run;
+            base[e] += run;
         }
-        __syncthreads();
+        run += mine4[j];
+    }
+    if (threadIdx.x == 0) {
+        used_s = used;
+        if (b == 0) offsets[E] = used;
+    }
+    if (b == 0 && status != nullptr && threadIdx.x < kWave) {
+        int32_t nb = 0;
+        for (int g = lane; g < blocks; g += kWave) nb += bad[g];
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) nb += __shfl_xor(nb, off, kWave);
+        if (lane == 0) *status = nb;
+    }
 
-        for (int s0 = 0; s0 < steps; s0 += kPrefetch) {
-            int32_t e_reg[kPrefetch];
+    // Per-wave counts of this chunk.
+    int32_t* mine = cnt + wave * E;
+    count_batch(e_first, 0, steps, E, nbits, mine, lane);
+    for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
+        int32_t e_reg[kPrefetch];
+        load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
+        count_batch(e_reg, s0, steps, E, nbits, mine, lane);
+    }
+    __syncthreads();
+
+    // Per-wave bases: segment start + earlier chunks + earlier waves.
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        int32_t r = base[e];
 #pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) {
-                const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
-                e_reg[j] = (s0 + j < steps && i < nk) ? load_id(ids, stride, i, K) : -1;
-            }
-#pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) {
-                if (s0 + j < steps) {   // wave-uniform
-                    const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
-                    const int32_t e = e_reg[j];
-                    const bool valid = e >= 0 && e < E;
-                    const uint64_t peers = same_expert_lanes(e, valid, nbits);
-                    int32_t p = -1;
-                    if (valid) p = mine[e] + __popcll(peers & lanes_below(lane));
-                    __builtin_amdgcn_wave_barrier();
-                    if (valid && lane == __ffsll((long long)peers) - 1) mine[e] += __popcll(peers);
-                    __builtin_amdgcn_wave_barrier();
-                    if (i < nk) pos[i] = p;
-                    if (valid && p < cap) row_pair[p] = (int32_t)i;
-                }
-            }
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t c = cnt[w * E + e];
+            cnt[w * E + e] = r;
+            r += c;
         }
+    }
+    __syncthreads();
+
+    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap);
+    for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
+        int32_t e_reg[kPrefetch];
+        load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
+        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap);
     }
 
     // Rows no pair landed in: past the used rows, and alignment padding.
-    const int64_t used = offsets[E];
-    for (int64_t r = used + (int64_t)b * kThreads + threadIdx.x; r < cap;
+    for (int64_t r = used_s + (int64_t)b * kThreads + threadIdx.x; r < cap;
          r += (int64_t)gridDim.x * kThreads)
         row_pair[r] = -1;
     if (align > 1) {
         for (int e = b; e < E; e += gridDim.x) {
-            const int32_t hi = offsets[e + 1];
-            for (int32_t r = offsets[e] + counts[e] + threadIdx.x; r < hi; r += kThreads)
+            const int32_t hi = e + 1 < E ? start_s[e + 1] : used_s;
+            for (int32_t r = start_s[e] + total_s[e] + threadIdx.x; r < hi; r += kThreads)
                 row_pair[r] = -1;
         }
     }
@@ -352,10 +417,8 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
     if (p.blocks > 0)
         layout_hist<<<p.blocks, kThreads, 0, stream>>>(ids, ids_row_stride, (uint32_t)nk,
                                                        (uint32_t)K, E, p.chunk, p.nbits, H, bad);
-    layout_scan<<<1, kScanThreads, 0, stream>>>(H, bad, p.blocks, E, p.ecols, p.lanes, p.rows,
-                                                align, counts, offsets, status);
     layout_assign<<<p.blocks > 0 ? p.blocks : 1, kThreads, 0, stream>>>(
         ids, ids_row_stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H,
-        counts, offsets, pos, row_pair, cap);
+        bad, counts, offsets, status, pos, row_pair, cap);
     return check_launch("moe_get_layout");
 }

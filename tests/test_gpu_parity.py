@@ -220,11 +220,27 @@ def test_edge_cases(mg):
     assert (host_bf16(out) == 0).all()                 # +0, not -0
     # E = 1, K = 1, K = 32, E = 1024 with hot experts
     rng = np.random.default_rng(8)
-    for (N, K, E) in [(100, 1, 1), (100, 8, 1), (1000, 1, 300), (129, 32, 1024), (5000, 8, 1024)]:
+    for (N, K, E) in [(100, 1, 1), (100, 8, 1), (1000, 1, 300), (129, 32, 1024), (5000, 8, 1024),
+                      # around the one-workgroup layout's limits (32768 pairs, 512 experts)
+                      (4096, 8, 512), (4096, 8, 513), (4097, 8, 256), (1024, 32, 64), (1025, 32, 64)]:
         ids = rng.integers(0, min(E, 3) if E > 3 else E, size=(N, K)).astype(np.int32)
         say(f"edge N={N} K={K} E={E}")
         lay = mg.layout(dev(ids), E)
         check_layout(mg, lay, ids, E)
+
+
+@pytest.mark.parametrize("N,K,E", [(4096, 8, 256), (4097, 8, 256), (4096, 8, 600)])
+def test_layout_paths_agree_on_uniform_and_skewed_ids(mg, N, K, E):
+    """Both layout forms (one workgroup, and histogram + assign) against the
+    oracle on the same kind of routing, with masks and a hot expert."""
+    rng = np.random.default_rng(N + E)
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.05] = -1
+    ids[rng.random((N, K)) < 0.2] = 3                  # hot expert (duplicates within a token)
+    for align in (1, 8):
+        say(f"layout paths N={N} K={K} E={E} align={align}")
+        lay = mg.layout(dev(ids), E, align=align)
+        check_layout(mg, lay, ids, E, align)
 
 
 def test_non_finite_values(mg):
