@@ -29,15 +29,17 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch+combine effective HBM GB/s and tokens/s, 4096×7168 top-8, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-COMBINE_SRC = os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip")
 
 
-def algorithmic_bytes(N, K, E, P, Hc, R, cap):
+def algorithmic_bytes(N, K, E, P, Hc, R, cap, epilogue=False):
     """Bytes each op must move at minimum: every input read once, every
-    output written once."""
+    output written once. With the epilogue, combine also reads the residual
+    and gamma and writes residual_out."""
     layout = 4 * N * K + 8 * E + 4 + 4 * N * K + 4 * cap
     dispatch = N * P + 4 * N * K + R * P
     combine = R * Hc * 2 + 8 * N * K + N * Hc * 2
+    if epilogue:
+        combine += N * Hc * 2 + Hc * 2 + N * Hc * 2
     return layout, dispatch, combine
 
 
@@ -55,12 +57,13 @@ def traffic_entry(kernel, workload):
     except (OSError, ValueError):
         return None
     e = data.get(f"{kernel}/{workload}")
-    if not e or e.get("source_sha256_16") != source_hash(COMBINE_SRC):
+    if not e or e.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return e
 
 
 KERNEL_SOURCES = {
+    "combine_epilogue_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
     "combine_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
     "dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
     "layout_hist": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
@@ -103,13 +106,15 @@ def summarize_traffic(fetch_dir, write_dir, workload, command):
     known_kib = COPY_BYTES / 1024
 
     def copy_median(vals):
-        # copy_bandwidth() is the only device-to-device copy of the run: its
-        # launches must read alike, whatever scale the counter has.
-        if len(vals) < 3:
+        # The 2 GiB copies of copy_bandwidth() are the largest launches of
+        # that kernel (the runtime also uses it for small uploads); they must
+        # read alike, whatever scale the counter has.
+        big = [v for v in vals if v > 0.5 * max(vals, default=0.0)]
+        if len(big) < 3:
             raise SystemExit(f"need the {COPY_KERNEL} launches of copy_bandwidth(), got {vals}")
-        m = float(np.median(vals))
-        if max(abs(v - m) for v in vals) > 0.1 * m:
-            raise SystemExit(f"{COPY_KERNEL} launches disagree: {vals}")
+        m = float(np.median(big))
+        if max(abs(v - m) for v in big) > 0.1 * m:
+            raise SystemExit(f"{COPY_KERNEL} launches disagree: {big}")
         return m
 
     fscale = known_kib / copy_median(fetch.get(COPY_KERNEL, []))
@@ -210,8 +215,12 @@ class BufferSet:
         self.ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device=d)
         self.dsts = [torch.empty((cap, a.shape[1]), dtype=torch.uint8, device=d) for a in self.srcs]
         self.out = torch.empty((N, wl.Hc), dtype=torch.bfloat16, device=d)
+        g = torch.Generator().manual_seed(wl.seed + 31)
+        self.residual = (torch.randn((N, wl.Hc), generator=g) * 2).to(torch.bfloat16).to(d)
+        self.gamma = (torch.rand(wl.Hc, generator=g) + 0.5).to(torch.bfloat16).to(d)
+        self.residual_out = torch.empty((N, wl.Hc), dtype=torch.bfloat16, device=d)
 
-    def calls(self, mg, wl, stream):
+    def calls(self, mg, wl, stream, epilogue=False):
         """Argument tuples of the three C-ABI calls, marshalled once."""
         L = mg._lib
         N, K, E = wl.N, wl.K, wl.E
@@ -223,9 +232,20 @@ class BufferSet:
                self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap, self.ws.data_ptr(),
                self.ws.numel(), self.status.data_ptr(), stream)
         dis = (fields, len(self.srcs), N, K, self.pos.data_ptr(), stream)
+        if not epilogue:
+            com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K,
+                   wl.Hc, self.out.data_ptr(), wl.Hc, stream)
+            return (L.moe_get_layout, lay), (L.moe_dispatch, dis), (L.moe_combine, com)
+        import ctypes
+
+        ep = mg.moe_epilogue()
+        ep.residual, ep.residual_row_stride = self.residual.data_ptr(), wl.Hc
+        ep.gamma, ep.eps = self.gamma.data_ptr(), 1e-6
+        ep.residual_out, ep.residual_out_row_stride = self.residual_out.data_ptr(), wl.Hc
+        self._ep = ep
         com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K, wl.Hc,
-               self.out.data_ptr(), wl.Hc, stream)
-        return (L.moe_get_layout, lay), (L.moe_dispatch, dis), (L.moe_combine, com)
+               ctypes.byref(ep), self.out.data_ptr(), wl.Hc, stream)
+        return (L.moe_get_layout, lay), (L.moe_dispatch, dis), (L.moe_combine_epilogue, com)
 
 
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
@@ -292,6 +312,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ref", action="store_true")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="combine with the fused residual add + RMSNorm epilogue "
+                         "(moe_combine_epilogue) instead of the plain combine")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench into profiles/traffic.json and exit (no GPU needed)")
@@ -322,7 +345,7 @@ def main():
     R = N * K
     sets = [BufferSet(torch, mg, wl, y) for _ in range(max(1, args.sets))]
     stream = torch.cuda.current_stream()
-    calls = [s.calls(mg, wl, stream.cuda_stream) for s in sets]
+    calls = [s.calls(mg, wl, stream.cuda_stream, args.epilogue) for s in sets]
 
     def step(i):
         for fn, a in calls[i % len(calls)]:
@@ -367,11 +390,12 @@ def main():
     ms_per_step_op_events, op_ms = timed_pass(True)
     hev.close()
 
-    b_lay, b_dis, b_com = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap)
+    b_lay, b_dis, b_com = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
     total = b_lay + b_dis + b_com
     value = total / (ms_per_step * 1e-3) / 1e9
     combine_gbs = b_com / (op_ms[2] * 1e-3) / 1e9
-    traffic = traffic_entry("combine_kernel", args.config)
+    ckernel = "combine_epilogue_kernel" if args.epilogue else "combine_kernel"
+    traffic = traffic_entry(ckernel, args.config)
 
     result = {
         "metric": METRIC,
@@ -389,7 +413,8 @@ def main():
         "config": {
             "workload": f"{args.config}: N={N} tokens, top-{K} of {E} experts, dispatch payload "
                         f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields)}), "
-                        f"combine bf16 hidden {Hc}, fp32 accumulation",
+                        f"combine bf16 hidden {Hc}, fp32 accumulation"
+                        + (", fused residual add + RMSNorm epilogue" if args.epilogue else ""),
             "tokens": N, "topk": K, "experts": E, "hidden": Hc, "payload_bytes": P,
             "buffer_sets": len(sets), "algorithmic_bytes_per_step": total,
         },
@@ -402,7 +427,7 @@ def main():
                        "dispatch": round(b_dis / (op_ms[1] * 1e-3) / 1e9, 1),
                        "combine": round(combine_gbs, 1)},
         "roofline": {
-            "kernel": "combine_kernel",
+            "kernel": ckernel,
             "bound": "hbm",
             "achieved": round(combine_gbs, 1),
             "peak": HBM_PEAK_GBS,

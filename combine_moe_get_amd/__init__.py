@@ -50,6 +50,14 @@ class moe_field(ctypes.Structure):
                 ("row_bytes", ctypes.c_int64)]
 
 
+class moe_epilogue(ctypes.Structure):
+    _fields_ = [("bias0", ctypes.c_void_p), ("bias0_row_stride", ctypes.c_int64),
+                ("bias1", ctypes.c_void_p), ("bias1_row_stride", ctypes.c_int64),
+                ("residual", ctypes.c_void_p), ("residual_row_stride", ctypes.c_int64),
+                ("gamma", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("residual_out", ctypes.c_void_p), ("residual_out_row_stride", ctypes.c_int64)]
+
+
 def _load():
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -65,6 +73,9 @@ def _load():
     L.moe_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P]
     L.moe_combine.restype = ctypes.c_int
+    L.moe_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32,
+                                       ctypes.POINTER(moe_epilogue), P, i64, P]
+    L.moe_combine_epilogue.restype = ctypes.c_int
     return L
 
 
@@ -196,6 +207,49 @@ def moe_combine(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor, out: 
     op, os_ = _rows(out, "out") if N else (0, Hc)
     _check(_lib.moe_combine(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc, op, os_,
                             _stream(stream)))
+
+
+def moe_combine_epilogue(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor,
+                         out: torch.Tensor, bias0: Optional[torch.Tensor] = None,
+                         bias1: Optional[torch.Tensor] = None,
+                         residual: Optional[torch.Tensor] = None,
+                         gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                         residual_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Combine, then + bias0 + bias1 and, with a residual, residual add
+    (written to residual_out) and RMSNorm with gamma into out. All bf16."""
+    if y.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("y and out must be bfloat16")
+    if weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 2:
+        raise TypeError("pos must be a contiguous int32 [N, K] tensor")
+    N, K = pos.shape
+    Hc = out.shape[1]
+    if y.shape[1] != Hc or out.shape[0] != N or tuple(weights.shape) != (N, K):
+        raise ValueError("shape mismatch between y, weights, pos and out")
+
+    def rows(t, name):
+        if t is None:
+            return 0, 0
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (N, Hc):
+            raise ValueError(f"{name} must be bfloat16 [N, Hc]")
+        return _rows(t, name) if N else (_dev(t, name), Hc)
+
+    ep = moe_epilogue()
+    ep.bias0, ep.bias0_row_stride = rows(bias0, "bias0")
+    ep.bias1, ep.bias1_row_stride = rows(bias1, "bias1")
+    ep.residual, ep.residual_row_stride = rows(residual, "residual")
+    ep.residual_out, ep.residual_out_row_stride = rows(residual_out, "residual_out")
+    if gamma is not None:
+        if gamma.dtype != torch.bfloat16 or gamma.numel() != Hc or not gamma.is_contiguous():
+            raise ValueError("gamma must be a contiguous bfloat16 [Hc] tensor")
+        ep.gamma = _dev(gamma, "gamma")
+    ep.eps = eps
+    yp, ys = _rows(y, "y") if y.shape[0] else (_dev(y, "y"), Hc)
+    wp, ws = _rows(weights, "weights") if N else (0, K)
+    op, os_ = _rows(out, "out") if N else (0, Hc)
+    _check(_lib.moe_combine_epilogue(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc,
+                                     ctypes.byref(ep), op, os_, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -179,6 +179,56 @@ int moe_combine(const void* y, int64_t y_row_stride, const float* w, int64_t w_r
                 const int32_t* pos, int32_t N, int32_t K, int32_t Hc, void* out,
                 int64_t out_row_stride, hipStream_t stream);
 
+/*
+ * Optional terms applied after the top-k sum by moe_combine_epilogue. All
+ * pointers are device pointers to bf16 bits; row strides are in elements. A
+ * NULL pointer leaves its term out.
+ *   bias0, bias1  [N, Hc] per-token biases added to the fp32 sum (DeepEP
+ *                 repository dump, deep_ep.cpp, Buffer::intranode_combine
+ *                 takes bias_0 / bias_1 [num_recv_tokens, hidden]; added here
+ *                 after the top-k sum, bias0 first).
+ *   residual      [N, Hc] skip connection. When given, the sum plus residual
+ *                 is written to residual_out and RMS-normalised into out with
+ *                 gamma [Hc] and eps, as the fused reduce-scatter + residual +
+ *                 RMSNorm kernel of the vLLM branch compare
+ *                 ds-exp-2...ds-exp-ag (moe_rs_fused.cu) does.
+ */
+typedef struct moe_epilogue {
+    const void* bias0;
+    int64_t bias0_row_stride;
+    const void* bias1;
+    int64_t bias1_row_stride;
+    const void* residual;
+    int64_t residual_row_stride;
+    const void* gamma;
+    float eps;
+    void* residual_out;
+    int64_t residual_out_row_stride;
+} moe_epilogue;
+
+/*
+ * Combine with an epilogue. For every token t, with acc[h] the fp32 value
+ * moe_combine computes before its final rounding:
+ *     acc[h] += bias0[t,h]; acc[h] += bias1[t,h]           (fp32, if given)
+ *     without residual:  out[t,h] = bf16(acc[h])
+ *     with residual:     acc[h] += residual[t,h];  residual_out[t,h] = bf16(acc[h])
+ *                        s = 1 / sqrt(sum_h acc[h]^2 / Hc + eps)
+ *                        out[t,h] = bf16(acc[h] * s * gamma[h])
+ * residual_out is bit-exact with that definition; out of the RMSNorm is within
+ * one bf16 ulp of it (the sum of squares is an fp32 tree sum, s a hardware
+ * reciprocal square root). ep == NULL is moe_combine.
+ *
+ * Alignment: y, out and every given row pointer 16-byte aligned with strides
+ * multiples of 8 elements, Hc a multiple of 8. Limits: Hc <= 16384 when any
+ * term is given, 1 <= K <= 32, eps >= 0. Errors: MOE_ERR_ARG (residual
+ * without gamma or residual_out, negative eps), MOE_ERR_ALIGN, MOE_ERR_LIMIT,
+ * MOE_ERR_HIP.
+ */
+int moe_combine_epilogue(const void* y, int64_t y_row_stride, const float* w,
+                         int64_t w_row_stride, const int32_t* pos, int32_t N, int32_t K,
+                         int32_t Hc, const moe_epilogue* ep, void* out, int64_t out_row_stride,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

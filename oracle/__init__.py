@@ -59,6 +59,11 @@ def lib():
         L.oracle_combine.restype = ctypes.c_int
         L.oracle_combine_acc.argtypes = [P, i64, P, i64, P, i32, i32, i32, P]
         L.oracle_combine_acc.restype = ctypes.c_int
+        L.oracle_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, P, P, P,
+                                              ctypes.c_float, P, P]
+        L.oracle_combine_epilogue.restype = ctypes.c_int
+        L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
+        L.oracle_bf16_from_f64.restype = ctypes.c_uint16
         L.oracle_required_cap.argtypes = [i32, i32, i32, i32]
         L.oracle_required_cap.restype = i64
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -163,6 +168,44 @@ def combine_acc(y: np.ndarray, w: np.ndarray, pos: np.ndarray) -> np.ndarray:
     if rc != OK:
         raise OracleError(rc, "combine_acc")
     return acc
+
+
+def combine_epilogue(y: np.ndarray, w: np.ndarray, pos: np.ndarray,
+                     bias0: Optional[np.ndarray] = None, bias1: Optional[np.ndarray] = None,
+                     residual: Optional[np.ndarray] = None, gamma: Optional[np.ndarray] = None,
+                     eps: float = 1e-6):
+    """Combine followed by the optional biases and, with a residual, the
+    residual add and RMSNorm. Returns (out, residual_out or None), bf16 bits.
+    bias0 / bias1 / residual are [N, Hc] bf16 bits, gamma [Hc]."""
+    assert y.dtype == np.uint16 and w.dtype == np.float32
+    N, K = pos.shape
+    Hc = y.shape[1]
+    out = np.empty((N, Hc), np.uint16)
+    res_out = np.empty((N, Hc), np.uint16) if residual is not None else None
+    pos_c = np.ascontiguousarray(pos, dtype=np.int32)
+    yb, ys = _row_view(y) if y.shape[0] else (0, Hc)
+    wb, ws = _row_view(w) if N else (0, K)
+
+    def opt(a, shape):
+        if a is None:
+            return None, 0
+        a = np.ascontiguousarray(a, dtype=np.uint16)
+        assert a.shape == shape
+        return a, _ptr(a)
+
+    b0, p0 = opt(bias0, (N, Hc))
+    b1, p1 = opt(bias1, (N, Hc))
+    r, pr = opt(residual, (N, Hc))
+    g, pg = opt(gamma, (Hc,))
+    rc = lib().oracle_combine_epilogue(yb, ys, wb, ws, _ptr(pos_c), N, K, Hc, p0, p1, pr, pg,
+                                       eps, 0 if res_out is None else _ptr(res_out), _ptr(out))
+    if rc != OK:
+        raise OracleError(rc, "combine_epilogue")
+    return out, res_out
+
+
+def bf16_from_f64(x: float) -> int:
+    return int(lib().oracle_bf16_from_f64(x))
 
 
 def f32_to_bf16(x: float) -> int:

@@ -163,6 +163,26 @@ uint16_t oracle_f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+/* double -> bf16, round to nearest, ties to even, in one step: scale the
+ * magnitude so the 8 kept significand bits are the integer part, round that
+ * with rint (nearest-even in the default rounding mode), and rebuild. */
+uint16_t oracle_bf16_from_f64(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double m = fabs(v);
+    if (m == 0.0) return sign;
+    int e;
+    frexp(m, &e);                    /* m = f * 2^e, 0.5 <= f < 1 */
+    if (e < -125) e = -125;          /* bf16 subnormal range shares one quantum */
+    double q = ldexp(1.0, e - 8);    /* spacing of bf16 values near m */
+    double r = rint(m / q) * q;      /* exact: m / q < 2^9 */
+    if (r >= 0x1.0p128) return sign | 0x7F80;
+    float f = (float)r;              /* exactly representable */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
 /* The fp32 accumulator of one output element: acc = +0, then for k
  * ascending with a valid row, acc = fmaf(w[t,k], y[row, h], acc). */
 static float combine_acc(const uint16_t* y, int64_t y_row_stride, const float* w,
@@ -199,5 +219,58 @@ int oracle_combine_acc(const uint16_t* y, int64_t y_row_stride, const float* w,
     for (int32_t t = 0; t < N; ++t)
         for (int32_t h = 0; h < Hc; ++h)
             acc_out[(int64_t)t * Hc + h] = combine_acc(y, y_row_stride, w, w_row_stride, pos, K, t, h);
+    return ORC_OK;
+}
+
+/* Combine epilogue: the combine accumulator of every element of a token,
+ * then (each only if given, all in fp32):
+ *   acc += bias0[t,h]; acc += bias1[t,h]
+ *     -- DeepEP (repository dump, deep_ep.cpp, Buffer::intranode_combine):
+ *        optional bias_0 / bias_1 [num_recv_tokens, hidden], dtype of x;
+ *        where they are added is not shown, taken here after the top-k sum.
+ *   with a residual:
+ *     acc += residual[t,h];  residual_out[t,h] = bf16(acc)
+ *     scale = 1 / sqrt(sum_h acc^2 / Hc + eps)
+ *     out[t,h] = bf16(acc * scale * gamma[h])
+ *     -- vLLM branch compare ds-exp-2...ds-exp-ag, moe_rs_fused.cu, fused
+ *        POLL + REDUCE + RESIDUAL + RMSNORM phase: fp32 sum plus residual,
+ *        that value stored as the new residual, RMSNorm of the same fp32
+ *        values with gamma.
+ *   without a residual: out[t,h] = bf16(acc).
+ * The pages fix fp32 for the sums but not the order of the sum of squares
+ * (a block tree there), so the oracle forms it and the scale in double and
+ * rounds each normed element once from double. */
+int oracle_combine_epilogue(const uint16_t* y, int64_t y_row_stride, const float* w,
+                            int64_t w_row_stride, const int32_t* pos, int32_t N, int32_t K,
+                            int32_t Hc, const uint16_t* bias0, const uint16_t* bias1,
+                            const uint16_t* residual, const uint16_t* gamma, float eps,
+                            uint16_t* residual_out, uint16_t* out) {
+    if (N < 0 || K < 1 || K > ORC_MAX_K || Hc < 0) return ORC_ERR_ARG;
+    if (residual && (!gamma || !residual_out)) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+        float* acc = (float*)__builtin_alloca((size_t)Hc * sizeof(float));
+        for (int32_t h = 0; h < Hc; ++h) {
+            float a = combine_acc(y, y_row_stride, w, w_row_stride, pos, K, t, h);
+            int64_t i = (int64_t)t * Hc + h;
+            if (bias0) a = a + oracle_bf16_to_f32(bias0[i]);
+            if (bias1) a = a + oracle_bf16_to_f32(bias1[i]);
+            if (residual) a = a + oracle_bf16_to_f32(residual[i]);
+            acc[h] = a;
+        }
+        if (!residual) {
+            for (int32_t h = 0; h < Hc; ++h) out[(int64_t)t * Hc + h] = oracle_f32_to_bf16(acc[h]);
+            continue;
+        }
+        double ss = 0.0;
+        for (int32_t h = 0; h < Hc; ++h) ss += (double)acc[h] * (double)acc[h];
+        double scale = 1.0 / sqrt(ss / (double)Hc + (double)eps);
+        for (int32_t h = 0; h < Hc; ++h) {
+            int64_t i = (int64_t)t * Hc + h;
+            residual_out[i] = oracle_f32_to_bf16(acc[h]);
+            double v = (double)acc[h] * scale * (double)oracle_bf16_to_f32(gamma[h]);
+            out[i] = oracle_bf16_from_f64(v);
+        }
+    }
     return ORC_OK;
 }

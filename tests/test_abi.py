@@ -156,3 +156,35 @@ def test_combine_validation(lib):
     assert L.moe_combine(P, 64, P, 8, P, 0, 8, 64, P, 64, 0) == lib.MOE_OK          # N = 0
     assert L.moe_combine(P, 64, P, 8, P, 4, 8, 0, P, 64, 0) == lib.MOE_OK           # Hc = 0
     assert _err(lib) == ""
+
+
+def test_combine_epilogue_validation(lib):
+    import ctypes
+
+    L = lib._lib
+    P = 0x10000
+
+    def ep(**kw):
+        e = lib.moe_epilogue()
+        e.eps = 1e-6
+        for k, v in kw.items():
+            setattr(e, k, v)
+        return ctypes.byref(e)
+
+    args = (P, 64, P, 8, P, 4, 8, 64)
+    # a residual needs gamma and residual_out
+    assert L.moe_combine_epilogue(*args, ep(residual=P, residual_row_stride=64), P, 64, 0) == lib.MOE_ERR_ARG
+    assert L.moe_combine_epilogue(*args, ep(residual=P, residual_row_stride=64, gamma=P), P, 64, 0) == lib.MOE_ERR_ARG
+    full = dict(residual=P, residual_row_stride=64, gamma=P, residual_out=P, residual_out_row_stride=64)
+    assert L.moe_combine_epilogue(*args, ep(**full, eps=-1.0), P, 64, 0) == lib.MOE_ERR_ARG
+    assert L.moe_combine_epilogue(*args, ep(**full, eps=float("nan")), P, 64, 0) == lib.MOE_ERR_ARG
+    # alignment: Hc multiple of 8, 16-byte rows, gamma 16-byte aligned
+    assert L.moe_combine_epilogue(P, 60, P, 8, P, 4, 8, 60, ep(**full), P, 60, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_combine_epilogue(*args, ep(bias0=P + 4, bias0_row_stride=64), P, 64, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_combine_epilogue(*args, ep(bias0=P, bias0_row_stride=68), P, 64, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_combine_epilogue(*args, ep(**dict(full, gamma=P + 8)), P, 64, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_combine_epilogue(*args, ep(bias1=P, bias1_row_stride=32), P, 64, 0) == lib.MOE_ERR_ARG
+    # the register-resident token row bounds Hc
+    assert L.moe_combine_epilogue(P, 16392, P, 8, P, 4, 8, 16392, ep(bias0=P, bias0_row_stride=16392),
+                                  P, 16392, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_combine_epilogue(P, 64, P, 8, P, 0, 8, 64, ep(**full), P, 64, 0) == lib.MOE_OK   # N = 0
