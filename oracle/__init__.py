@@ -64,6 +64,16 @@ def lib():
         L.oracle_combine_epilogue.restype = ctypes.c_int
         L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
         L.oracle_bf16_from_f64.restype = ctypes.c_uint16
+        L.oracle_layout_padded.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P]
+        L.oracle_layout_padded.restype = ctypes.c_int
+        L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+        L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_f32.restype = ctypes.c_float
+        L.oracle_fp8_block_scale.argtypes = [P, ctypes.c_int]
+        L.oracle_fp8_block_scale.restype = ctypes.c_float
+        L.oracle_dispatch_fp8.argtypes = [P, i64, i32, i32, i32, P, P, i64, P, i32, i64, i32, i32]
+        L.oracle_dispatch_fp8.restype = ctypes.c_int
         L.oracle_required_cap.argtypes = [i32, i32, i32, i32]
         L.oracle_required_cap.restype = i64
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -202,6 +212,64 @@ def combine_epilogue(y: np.ndarray, w: np.ndarray, pos: np.ndarray,
     if rc != OK:
         raise OracleError(rc, "combine_epilogue")
     return out, res_out
+
+
+def layout_padded(ids: np.ndarray, E: int, M: int):
+    """Padded per-expert layout: expert e owns rows e*M .. e*M+M-1.
+    Returns (counts [E], pos [N, K], row_pair [E*M], status (ids >= E, dropped))."""
+    assert ids.dtype == np.int32
+    N, K = ids.shape
+    base, stride = _row_view(ids) if N > 0 else (0, K)
+    counts = np.empty(E, np.int32)
+    pos = np.empty((N, K), np.int32)
+    row_pair = np.empty(E * M, np.int32)
+    status = np.zeros(2, np.int32)
+    rc = lib().oracle_layout_padded(base, stride, N, K, E, M, _ptr(counts), _ptr(pos),
+                                    _ptr(row_pair), _ptr(status))
+    if rc != OK:
+        raise OracleError(rc, "layout_padded")
+    return counts, pos, row_pair, (int(status[0]), int(status[1]))
+
+
+SCALE_ROWS, SCALE_COLS, SCALE_UE8M0 = 0, 1, 2
+
+
+def dispatch_fp8(x: np.ndarray, pos: np.ndarray, rows: int, scale_mode: int = SCALE_ROWS,
+                 M: int = 0, round_scale: bool = False, fill: int = 0):
+    """Quantising dispatch of bf16 x [N, H] (bits). Returns (codes [rows, H]
+    uint8, scales): fp32 [rows, H/128] (SCALE_ROWS), fp32 [rows/M, H/128, M]
+    (SCALE_COLS) or int32 [rows/M, H/512, M] (SCALE_UE8M0)."""
+    assert x.dtype == np.uint16
+    N, H = x.shape
+    K = pos.shape[1]
+    codes = np.full((rows, H), fill, np.uint8)
+    if scale_mode == SCALE_ROWS:
+        scales = np.zeros((rows, H // 128), np.float32)
+    elif scale_mode == SCALE_COLS:
+        scales = np.zeros((rows // M, H // 128, M), np.float32)
+    else:
+        scales = np.zeros((rows // M, H // 512, M), np.int32)
+    pos_c = np.ascontiguousarray(pos, dtype=np.int32)
+    xb, xs = _row_view(x) if N else (0, H)
+    rc = lib().oracle_dispatch_fp8(xb, xs, N, K, H, _ptr(pos_c), _ptr(codes), H, _ptr(scales),
+                                   scale_mode, H // 128, M, int(round_scale))
+    if rc != OK:
+        raise OracleError(rc, "dispatch_fp8")
+    return codes, scales
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(lib().oracle_f32_to_e4m3(x))
+
+
+def e4m3_to_f32(c: int) -> float:
+    return float(lib().oracle_e4m3_to_f32(c))
+
+
+def fp8_block_scale(block: np.ndarray, round_scale: bool) -> float:
+    b = np.ascontiguousarray(block, dtype=np.uint16)
+    assert b.size == 128
+    return float(lib().oracle_fp8_block_scale(_ptr(b), int(round_scale)))
 
 
 def bf16_from_f64(x: float) -> int:

@@ -274,3 +274,154 @@ int oracle_combine_epilogue(const uint16_t* y, int64_t y_row_stride, const float
     }
     return ORC_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Low-latency dispatch forms (DeepEP repository dump, deep_ep.cpp,
+ * Buffer::low_latency_dispatch; config.hpp, LowLatencyLayout):
+ *  - a padded per-expert receive buffer packed_recv_x [E, M, H] with
+ *    packed_recv_count [E] and the source of every row;
+ *  - FP8 cast on dispatch: bf16 x, e4m3 payload, fp32 scales per token and
+ *    per 128 channels stored column-major [E, H/128, M], or (use_ue8m0, which
+ *    needs round_scale) power-of-two scales as 8-bit exponents packed four to
+ *    an int32 [E, H/512, M].
+ * The cast itself is not on the pages; this oracle takes, per 128-channel
+ * block of a token: amax = max |x| (fp32), s = amax / 448 but at least
+ * 2^-126, with round_scale s = the smallest power of two >= s, and
+ * q = e4m3(x / s) (fp32 division, round to nearest even, saturating to
+ * +-448; e4m3fn: 4 exponent bits, bias 7, no infinities).
+ * ------------------------------------------------------------------------- */
+
+/* Padded layout: expert e's segment starts at row e*M; the first M pairs of
+ * expert e in (t, k) order take rows e*M .. e*M+M-1, later ones are dropped.
+ * counts[e] = rows filled; status[0] = ids >= E, status[1] = pairs dropped
+ * for capacity. row_pair[E*M] as in oracle_layout. */
+int oracle_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                         int32_t E, int32_t M, int32_t* counts, int32_t* pos, int32_t* row_pair,
+                         int32_t* status) {
+    if (N < 0 || K < 1 || E < 1 || M < 0) return ORC_ERR_ARG;
+    if (K > ORC_MAX_K || E > ORC_MAX_E) return ORC_ERR_LIMIT;
+    if ((int64_t)N * K >= ((int64_t)1 << 31) || (int64_t)E * M >= ((int64_t)1 << 31))
+        return ORC_ERR_LIMIT;
+    if (N > 0 && ids_row_stride < K) return ORC_ERR_ARG;
+    int32_t bad = 0, dropped = 0;
+    for (int64_t r = 0; r < (int64_t)E * M; ++r) row_pair[r] = -1;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = ids[(int64_t)t * ids_row_stride + k];
+            int32_t p = -1;
+            if (e >= E) {
+                ++bad;
+            } else if (e >= 0) {
+                if (counts[e] < M) {
+                    p = e * M + counts[e];
+                    counts[e] += 1;
+                    row_pair[p] = t * K + k;
+                } else {
+                    ++dropped;
+                }
+            }
+            pos[(int64_t)t * K + k] = p;
+        }
+    }
+    if (status) {
+        status[0] = bad;
+        status[1] = dropped;
+    }
+    return ORC_OK;
+}
+
+/* fp32 -> e4m3fn, round to nearest even, finite overflow saturates to
+ * +-448, NaN -> 0x7F. e4m3fn: sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits; normals 2^-6 .. 448, subnormals multiples of 2^-9. Done on the value:
+ * find its spacing, round the scaled value with rint, rebuild the code. */
+uint8_t oracle_f32_to_e4m3(float f) {
+    if (isnan(f)) return 0x7F;
+    uint8_t sign = signbit(f) ? 0x80 : 0;
+    double m = fabs((double)f);
+    if (m >= 448.0) return sign | 0x7E;
+    int e;
+    frexp(m, &e);                       /* m = g * 2^e, 0.5 <= g < 1 */
+    if (e < -5) e = -5;                 /* subnormal range: spacing 2^-9 */
+    double q = ldexp(1.0, e - 4);       /* spacing of e4m3 values near m */
+    double r = rint(m / q) * q;         /* exact */
+    if (r >= 448.0) return sign | 0x7E;
+    if (r == 0.0) return sign;
+    int re;
+    double g = frexp(r, &re);           /* r = g * 2^re */
+    int biased = re - 1 + 7;            /* exponent of 1.xxx * 2^(re-1) */
+    uint8_t code;
+    if (biased <= 0) {                  /* subnormal: r = mant * 2^-9 */
+        code = (uint8_t)(r / ldexp(1.0, -9));
+    } else {
+        int mant = (int)((g * 2.0 - 1.0) * 8.0 + 0.5);
+        code = (uint8_t)((biased << 3) | mant);
+    }
+    return sign | code;
+}
+
+float oracle_e4m3_to_f32(uint8_t c) {
+    int s = c >> 7, ex = (c >> 3) & 15, mn = c & 7;
+    if (ex == 15 && mn == 7) return NAN;
+    double v = ex == 0 ? ldexp((double)mn, -9) : ldexp(1.0 + mn / 8.0, ex - 7);
+    return (float)(s ? -v : v);
+}
+
+/* The scale of one 128-channel block of bf16 values. */
+float oracle_fp8_block_scale(const uint16_t* x, int round_scale) {
+    float amax = 0.0f;
+    for (int i = 0; i < 128; ++i) {
+        float a = fabsf(oracle_bf16_to_f32(x[i]));
+        if (a > amax) amax = a;
+    }
+    float s = amax / 448.0f;
+    if (s < 0x1.0p-126f) s = 0x1.0p-126f;
+    if (round_scale) {
+        int e;
+        float g = frexpf(s, &e);       /* s = g * 2^e, 0.5 <= g < 1 */
+        s = (g == 0.5f) ? s : ldexpf(1.0f, e);
+    }
+    return s;
+}
+
+/* Quantising dispatch: for every valid (t, k), row p = pos[t*K+k] gets the
+ * e4m3 codes of x[t] (H bytes at dst + p*dst_row_stride) and, per block b,
+ * its scale. scale_mode 0: fp32 rows, scales[p*scale_row_stride + b];
+ * 1: fp32 column-major per expert, scales[((p/M)*(H/128) + b)*M + p%M];
+ * 2: ue8m0 column-major per expert, int32 words [((p/M)*(H/512) + b/4)*M + p%M],
+ *    byte b%4 = biased exponent of the (power-of-two) scale. */
+int oracle_dispatch_fp8(const uint16_t* x, int64_t x_row_stride, int32_t N, int32_t K, int32_t H,
+                        const int32_t* pos, uint8_t* dst, int64_t dst_row_stride, void* scales,
+                        int32_t scale_mode, int64_t scale_row_stride, int32_t M,
+                        int32_t round_scale) {
+    if (N < 0 || K < 1 || K > ORC_MAX_K || H < 0 || H % 128 != 0) return ORC_ERR_ARG;
+    if (scale_mode == 2 && (!round_scale || H % 512 != 0)) return ORC_ERR_ARG;
+    if (scale_mode != 0 && M < 1) return ORC_ERR_ARG;
+    const int32_t nb = H / 128;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+        const uint16_t* xr = x + (int64_t)t * x_row_stride;
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t p = pos[(int64_t)t * K + k];
+            if (p < 0) continue;
+            for (int32_t b = 0; b < nb; ++b) {
+                float s = oracle_fp8_block_scale(xr + 128 * b, round_scale);
+                for (int i = 0; i < 128; ++i)
+                    dst[(int64_t)p * dst_row_stride + 128 * b + i] =
+                        oracle_f32_to_e4m3(oracle_bf16_to_f32(xr[128 * b + i]) / s);
+                if (scale_mode == 0) {
+                    ((float*)scales)[(int64_t)p * scale_row_stride + b] = s;
+                } else if (scale_mode == 1) {
+                    ((float*)scales)[((int64_t)(p / M) * nb + b) * M + p % M] = s;
+                } else {
+                    uint32_t bits;
+                    memcpy(&bits, &s, 4);
+                    uint8_t* word = (uint8_t*)((uint32_t*)scales +
+                                               ((int64_t)(p / M) * (nb / 4) + b / 4) * M + p % M);
+                    word[b % 4] = (uint8_t)(bits >> 23);
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}

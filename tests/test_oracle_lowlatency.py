@@ -1,0 +1,169 @@
+"""Pins of the oracle's low-latency dispatch forms (CPU only): the padded
+per-expert layout and the FP8 (e4m3) cast on dispatch with per-128-channel
+scales (DeepEP repository dump, deep_ep.cpp, Buffer::low_latency_dispatch;
+config.hpp, LowLatencyLayout). The cast's arithmetic is this build's reading
+(the kernel is not on the pages): amax/448 per block, at least 2^-126,
+optionally rounded up to a power of two; e4m3 round-to-nearest-even,
+saturating.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+from _util import bf16_bits_to_float
+
+
+def _bits(a):
+    return mw.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+# ---------------------------------------------------------------- layout ---
+
+@pytest.mark.parametrize("seed", range(12))
+def test_padded_layout_is_the_stable_layout_shifted(orc, seed):
+    rng = np.random.default_rng(seed)
+    N, K, E = int(rng.integers(0, 300)), int(rng.integers(1, 9)), int(rng.integers(1, 40))
+    ids = rng.integers(-1, E + 2, size=(N, K)).astype(np.int32)
+    M = int(rng.choice([N, max(1, N // 4), 3, 0])) if N else 2
+    counts, pos, row_pair, (bad, dropped) = orc.layout_padded(ids, E, M)
+    full_counts, offsets, full_pos, _, full_bad = orc.layout(ids, E)
+    assert bad == full_bad
+    assert (counts == np.minimum(full_counts, M)).all()
+    assert dropped == int(np.maximum(full_counts - M, 0).sum())
+    flat, fpos = ids.reshape(-1), full_pos.reshape(-1)
+    for i, e in enumerate(flat):
+        if fpos[i] < 0:
+            assert pos.reshape(-1)[i] == -1
+            continue
+        rank = fpos[i] - offsets[e]                   # rank within the expert, (t, k) order
+        expect = e * M + rank if rank < M else -1
+        assert pos.reshape(-1)[i] == expect
+    for e in range(E):
+        seg = row_pair[e * M:(e + 1) * M]
+        assert (seg[counts[e]:] == -1).all() and (np.diff(seg[:counts[e]]) > 0).all()
+
+
+def test_padded_layout_hand_worked(orc):
+    # N=4 K=2 E=3 (ids as in tests/golden/layout_hand.txt, case plain), M=2:
+    # e0 pairs (0,1),(1,0),(3,1) -> rows 0,1 then dropped; e1 (2,0) -> row 2;
+    # e2 (0,0),(1,1),(3,0) -> rows 4,5 then dropped.
+    ids = np.array([[2, 0], [0, 2], [1, -1], [2, 0]], np.int32)
+    counts, pos, row_pair, (bad, dropped) = orc.layout_padded(ids, 3, 2)
+    assert counts.tolist() == [2, 1, 2]
+    assert pos.reshape(-1).tolist() == [4, 0, 1, 5, 2, -1, -1, -1]
+    assert row_pair.tolist() == [1, 2, 4, -1, 0, 3]
+    assert (bad, dropped) == (0, 2)
+
+
+# ------------------------------------------------------------------ e4m3 ---
+
+def _torch_e4m3(v):
+    return torch.tensor(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_matches_torch_in_range(orc):
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-4, 3, 20000),
+                        rng.uniform(-463.9, 463.9, 5000)]).astype(np.float32)
+    # exact ties between neighbouring e4m3 values
+    codes = np.arange(0, 0x7E, dtype=np.uint8)
+    vals = np.array([orc.e4m3_to_f32(int(c)) for c in codes], np.float64)
+    ties = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, ties, -ties, [0.0, -0.0, 2 ** -9, 2 ** -10, 448.0, -448.0]]).astype(np.float32)
+    ours = np.array([orc.f32_to_e4m3(float(x)) for x in v], np.uint8)
+    ref = _torch_e4m3(v)
+    same = (ours == ref) | ((ours & 0x7F) == 0) & ((ref & 0x7F) == 0)   # +-0
+    assert same.all(), v[~same][:10]
+
+
+def test_e4m3_saturates_and_decodes(orc):
+    for x, c in [(448.0, 0x7E), (449.0, 0x7E), (1e9, 0x7E), (-1e9, 0xFE), (float("inf"), 0x7E),
+                 (float("nan"), 0x7F), (2.0 ** -9, 0x01), (2.0 ** -6, 0x08), (1.0, 0x38)]:
+        assert orc.f32_to_e4m3(x) == c, x
+    for c in range(256):
+        v = orc.e4m3_to_f32(c)
+        if (c & 0x7F) == 0x7F:
+            assert math.isnan(v)
+        else:
+            assert orc.f32_to_e4m3(v) == c or (c & 0x7F) == 0
+
+
+# ----------------------------------------------------------------- scale ---
+
+def test_block_scale_rules(orc):
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        blk = _bits(rng.standard_normal(128) * 10.0 ** rng.integers(-8, 4))
+        amax = float(np.abs(bf16_bits_to_float(blk)).max())
+        s = orc.fp8_block_scale(blk, False)
+        assert s == max(float(np.float32(np.float32(amax) / np.float32(448.0))), 2.0 ** -126)
+        r = orc.fp8_block_scale(blk, True)
+        m, e = math.frexp(r)
+        assert m == 0.5 and r >= s and r < 2 * s            # smallest power of two >= s
+    assert orc.fp8_block_scale(np.zeros(128, np.uint16), False) == 2.0 ** -126
+
+
+def test_constant_block_maps_to_max_code(orc):
+    for c in (1.0, -3.5, 1e-3, 7.0e4):
+        x = np.tile(_bits([c] * 128), (1, 1))
+        pos = np.zeros((1, 1), np.int32)
+        codes, scales = orc.dispatch_fp8(x, pos, 1)
+        assert (codes == (0xFE if c < 0 else 0x7E)).all()
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_dequantisation_error_bound(orc, round_scale):
+    rng = np.random.default_rng(2)
+    N, H = 16, 512
+    x = _bits(rng.standard_normal((N, H)) * np.exp(rng.standard_normal((N, 1)) * 3))
+    pos = np.arange(N, dtype=np.int32).reshape(N, 1)
+    codes, scales = orc.dispatch_fp8(x, pos, N, round_scale=round_scale)
+    xf = bf16_bits_to_float(x).astype(np.float64)
+    deq = np.vectorize(orc.e4m3_to_f32)(codes).astype(np.float64) * np.repeat(scales, 128, axis=1)
+    blk_max = np.repeat(np.abs(xf).reshape(N, -1, 128).max(axis=2), 128, axis=1)
+    # e4m3 keeps 3 mantissa bits: relative error <= 2^-4 in the normal range,
+    # absolute error <= half the subnormal spacing (2^-10 times the scale) below it
+    err = np.abs(deq - xf)
+    bound = np.maximum(np.abs(xf) * 2.0 ** -4, np.repeat(scales, 128, axis=1) * 2.0 ** -10) * 1.0001
+    assert (err <= bound).all()
+    # the largest element of each block lands near the top of the e4m3 range
+    top = np.abs(deq) >= blk_max * (1 - 2.0 ** -3)
+    assert top.reshape(N, -1, 128).any(axis=2).all()
+
+
+def test_scale_layouts_agree(orc):
+    rng = np.random.default_rng(3)
+    N, K, E, H, M = 40, 4, 8, 1024, 40
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    x = _bits(rng.standard_normal((N, H)))
+    counts, pos, row_pair, _ = orc.layout_padded(ids, E, M)
+    rows = E * M
+    c_rows, s_rows = orc.dispatch_fp8(x, pos, rows, orc.SCALE_ROWS, M, True)
+    c_cols, s_cols = orc.dispatch_fp8(x, pos, rows, orc.SCALE_COLS, M, True)
+    c_ue, s_ue = orc.dispatch_fp8(x, pos, rows, orc.SCALE_UE8M0, M, True)
+    assert np.array_equal(c_rows, c_cols) and np.array_equal(c_rows, c_ue)
+    # column-major per expert is a transpose of the row-major scales
+    assert np.array_equal(s_cols, s_rows.reshape(E, M, H // 128).transpose(0, 2, 1))
+    # ue8m0 bytes are the biased exponents of the power-of-two scales
+    exps = (s_rows.view(np.uint32) >> 23).astype(np.uint8).reshape(E, M, H // 512, 4)
+    assert np.array_equal(s_ue.view(np.uint8).reshape(E, H // 512, M, 4), exps.transpose(0, 2, 1, 3))
+    # every used row holds the codes of its source token
+    used = row_pair >= 0
+    t = row_pair[used] // K
+    solo, solo_s = orc.dispatch_fp8(x, np.arange(N, dtype=np.int32).reshape(N, 1), N, round_scale=True)
+    assert np.array_equal(c_rows[used], solo[t]) and np.array_equal(s_rows[used], solo_s[t])
+
+
+def test_errors(orc):
+    x = np.zeros((2, 100), np.uint16)
+    with pytest.raises(orc.OracleError):
+        orc.dispatch_fp8(x, np.zeros((2, 1), np.int32), 2)              # H % 128
+    x = np.zeros((2, 128), np.uint16)
+    with pytest.raises(orc.OracleError):
+        orc.dispatch_fp8(x, np.zeros((2, 1), np.int32), 2, orc.SCALE_UE8M0, 2, True)   # H % 512
+    with pytest.raises(orc.OracleError):
+        orc.dispatch_fp8(np.zeros((2, 512), np.uint16), np.zeros((2, 1), np.int32), 2,
+                         orc.SCALE_UE8M0, 2, False)                      # ue8m0 needs round_scale
