@@ -31,6 +31,9 @@ MOE_ERR_LIMIT = -3
 MOE_ERR_CAPACITY = -4
 MOE_ERR_WORKSPACE = -5
 MOE_ERR_HIP = -6
+MOE_SCALE_ROWS = 0
+MOE_SCALE_COLS = 1
+MOE_SCALE_UE8M0 = 2
 MAX_TOPK = 32
 MAX_EXPERTS = 1024
 MAX_FIELDS = 4
@@ -73,6 +76,10 @@ def _load():
     L.moe_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P]
     L.moe_combine.restype = ctypes.c_int
+    L.moe_get_layout_padded.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, sz, P, P]
+    L.moe_get_layout_padded.restype = ctypes.c_int
+    L.moe_dispatch_fp8.argtypes = [P, i64, i32, i32, i32, P, P, i64, P, i32, i64, i32, i32, P]
+    L.moe_dispatch_fp8.restype = ctypes.c_int
     L.moe_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32,
                                        ctypes.POINTER(moe_epilogue), P, i64, P]
     L.moe_combine_epilogue.restype = ctypes.c_int
@@ -155,6 +162,58 @@ def moe_get_layout(ids: torch.Tensor, num_experts: int, align: int, counts: torc
                                _dev(workspace, "workspace"),
                                workspace.numel() * workspace.element_size(),
                                _dev(status, "status"), _stream(stream)))
+
+
+def moe_get_layout_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: int,
+                          counts: torch.Tensor, pos: torch.Tensor, row_pair: torch.Tensor,
+                          workspace: torch.Tensor, status: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    """Padded per-expert layout: expert e owns rows e*M .. e*M+M-1."""
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    for n, t in (("counts", counts), ("pos", pos), ("row_pair", row_pair)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 2):
+        raise TypeError("status must be an int32 tensor with at least two elements")
+    N, K = ids.shape
+    if (counts.numel() < num_experts or pos.numel() < N * K
+            or row_pair.numel() < num_experts * rows_per_expert):
+        raise ValueError("counts, pos or row_pair too small")
+    ip, istride = _rows(ids, "ids") if N > 0 else (0, K)
+    _check(_lib.moe_get_layout_padded(ip, istride, N, K, num_experts, rows_per_expert,
+                                      _dev(counts, "counts"), _dev(pos, "pos"),
+                                      _dev(row_pair, "row_pair"), _dev(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _dev(status, "status"), _stream(stream)))
+
+
+def moe_dispatch_fp8(x: torch.Tensor, pos: Optional[torch.Tensor], K: int, dst: torch.Tensor,
+                     scales: torch.Tensor, scale_format: int = MOE_SCALE_ROWS,
+                     rows_per_expert: int = 0, round_scale: bool = False, stream=None) -> None:
+    """Quantising dispatch: bf16 x [N, H] -> e4m3 codes in dst [rows, H]
+    (uint8) at rows pos[t, k], scales as scale_format (see moe_get.h)."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if dst.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("dst must be uint8 or float8_e4m3fn")
+    N, H = x.shape
+    xp, xs = _rows(x, "x") if N else (0, H)
+    dp, ds = _rows(dst, "dst") if dst.shape[0] else (0, H)
+    if scale_format == MOE_SCALE_ROWS:
+        if scales.dtype != torch.float32 or scales.dim() != 2 or scales.stride(1) != 1:
+            raise TypeError("row scales must be float32 [rows, >= H/128] with contiguous rows")
+        srs = scales.stride(0)
+    else:
+        if not scales.is_contiguous():
+            raise TypeError("column-major scales must be a contiguous tensor")
+        srs = 0
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()
+                            or pos.numel() != N * K):
+        raise ValueError("pos must be a contiguous int32 [N, K] tensor")
+    _check(_lib.moe_dispatch_fp8(xp, xs, N, K, H, _dev(pos, "pos"), dp, ds,
+                                 _dev(scales, "scales"), scale_format, srs, rows_per_expert,
+                                 int(bool(round_scale)), _stream(stream)))
 
 
 def _as_bytes2d(t: torch.Tensor, name: str) -> Tuple[int, int, int]:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_get.so")
-SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip"]
+SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "quant.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

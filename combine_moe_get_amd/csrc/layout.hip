@@ -128,11 +128,14 @@ __device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[kPrefetch]
 
 // Gives every pair of one batch its row: the wave's running base for the
 // expert plus the number of lower lanes in the same step with that expert.
+// In the padded form (M > 0) expert e's segment is rows e*M .. e*M+M-1 and
+// a pair ranked past it is dropped (pos = -1).
 __device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[kPrefetch], int s0, int steps,
                                            int32_t E, int nbits, int32_t* base_row,
                                            uint32_t first, uint32_t nk, int lane,
                                            int32_t* __restrict__ pos,
-                                           int32_t* __restrict__ row_pair, int64_t cap) {
+                                           int32_t* __restrict__ row_pair, int64_t cap,
+                                           int32_t M) {
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
         if (s0 + j < steps) {   // wave-uniform
@@ -145,8 +148,9 @@ __device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[kPrefetch], in
             __builtin_amdgcn_wave_barrier();
             if (valid && lane == __ffsll((long long)peers) - 1) base_row[e] += __popcll(peers);
             __builtin_amdgcn_wave_barrier();
+            if (M > 0 && p >= (e + 1) * M) p = -1;   // past the expert's padded segment
             if (i < nk) pos[i] = p;
-            if (valid && p < cap) row_pair[p] = (int32_t)i;
+            if (p >= 0 && p < cap) row_pair[p] = (int32_t)i;
         }
     }
 }
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
     const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ status, int32_t* __restrict__ pos, int32_t* __restrict__ row_pair,
-    int64_t cap) {
+    int64_t cap, int32_t M) {
     __shared__ int32_t cnt[kWaves * MOE_MAX_EXPERTS];   // per-wave counts, then bases
     __shared__ int32_t total_s[MOE_MAX_EXPERTS];       // valid pairs per expert
     __shared__ int32_t start_s[MOE_MAX_EXPERTS];       // segment start (offsets[e])
@@ -287,29 +291,43 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     }
     int32_t used = 0;
     int32_t run = block_exclusive_scan<kWaves>(sum4, wave_sums, &used);
+    int32_t dropped4 = 0;   // padded form: pairs beyond their expert's M rows
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = threadIdx.x * 4 + j;
         if (e < E) {
+            const int32_t start = M > 0 ? e * M : run;
             if (b == 0) {
-                counts[e] = total_s[e];
-                offsets[e] = run;
+                counts[e] = M > 0 ? min(total_s[e], M) : total_s[e];
+                if (offsets != nullptr) offsets[e] = start;
             }
-            start_s[e] = run;
-            base[e] += run;
+            if (M > 0) dropped4 += max(total_s[e] - M, 0);
+            start_s[e] = start;
+            base[e] += start;
         }
         run += mine4[j];
     }
     if (threadIdx.x == 0) {
-        used_s = used;
-        if (b == 0) offsets[E] = used;
+        used_s = M > 0 ? E * M : used;
+        if (b == 0 && offsets != nullptr) offsets[E] = M > 0 ? E * M : used;
     }
     if (b == 0 && status != nullptr && threadIdx.x < kWave) {
         int32_t nb = 0;
         for (int g = lane; g < blocks; g += kWave) nb += bad[g];
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) nb += __shfl_xor(nb, off, kWave);
-        if (lane == 0) *status = nb;
+        if (lane == 0) status[0] = nb;
+    }
+    if (M > 0) {
+        // status[1]: one wave-reduced sum per wave, then wave 0 adds them
+        int32_t d = dropped4;
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, kWave);
+        __syncthreads();   // wave_sums is free again after the scan
+        if (lane == 0) wave_sums[wave] = d;
+        __syncthreads();
+        if (b == 0 && status != nullptr && threadIdx.x == 0)
+            status[1] = wave_sums[0] + wave_sums[1] + wave_sums[2] + wave_sums[3];
     }
 
     // Per-wave counts of this chunk.
@@ -334,21 +352,22 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     }
     __syncthreads();
 
-    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap);
+    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M);
     for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
         int32_t e_reg[kPrefetch];
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
-        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap);
+        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M);
     }
 
     // Rows no pair landed in: past the used rows, and alignment padding.
     for (int64_t r = used_s + (int64_t)b * kThreads + threadIdx.x; r < cap;
          r += (int64_t)gridDim.x * kThreads)
         row_pair[r] = -1;
-    if (align > 1) {
+    if (align > 1 || M > 0) {
         for (int e = b; e < E; e += gridDim.x) {
             const int32_t hi = e + 1 < E ? start_s[e + 1] : used_s;
-            for (int32_t r = start_s[e] + total_s[e] + threadIdx.x; r < hi; r += kThreads)
+            const int32_t filled = M > 0 ? min(total_s[e], M) : total_s[e];
+            for (int32_t r = start_s[e] + filled + threadIdx.x; r < hi; r += kThreads)
                 row_pair[r] = -1;
         }
     }
@@ -419,6 +438,49 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
                                                        (uint32_t)K, E, p.chunk, p.nbits, H, bad);
     layout_assign<<<p.blocks > 0 ? p.blocks : 1, kThreads, 0, stream>>>(
         ids, ids_row_stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H,
-        bad, counts, offsets, status, pos, row_pair, cap);
+        bad, counts, offsets, status, pos, row_pair, cap, 0);
     return check_launch("moe_get_layout");
+}
+
+extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
+                                     int32_t K, int32_t E, int32_t M, int32_t* counts,
+                                     int32_t* pos, int32_t* row_pair, void* workspace,
+                                     size_t workspace_bytes, int32_t* status,
+                                     hipStream_t stream) {
+    if (N < 0 || K < 1 || E < 1 || M < 1)
+        return fail(MOE_ERR_ARG, "moe_get_layout_padded: need N >= 0, K >= 1, E >= 1, M >= 1 "
+                    "(got N=%d K=%d E=%d M=%d)", N, K, E, M);
+    if (K > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_LIMIT, "moe_get_layout_padded: K=%d E=%d beyond K <= %d, E <= %d", K,
+                    E, MOE_MAX_TOPK, MOE_MAX_EXPERTS);
+    const int64_t nk = (int64_t)N * K;
+    const int64_t cap = (int64_t)E * M;
+    if (nk >= ((int64_t)1 << 31) || cap >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_get_layout_padded: N*K and E*M must be below 2^31");
+    if (N > 0 && (ids == nullptr || pos == nullptr))
+        return fail(MOE_ERR_ARG, "moe_get_layout_padded: ids and pos must not be NULL");
+    if (N > 0 && ids_row_stride < K)
+        return fail(MOE_ERR_ARG, "moe_get_layout_padded: ids_row_stride < K");
+    if (counts == nullptr || row_pair == nullptr)
+        return fail(MOE_ERR_ARG, "moe_get_layout_padded: counts and row_pair must not be NULL");
+    if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(pos, 4) || !aligned(row_pair, 4) ||
+        !aligned(status, 4))
+        return fail(MOE_ERR_ALIGN, "moe_get_layout_padded: int32 pointers must be 4-byte aligned");
+    const Plan p = make_plan(N, K, E);
+    const size_t ws = workspace_for(p, E);
+    if (workspace == nullptr || workspace_bytes < ws)
+        return fail(MOE_ERR_WORKSPACE, "moe_get_layout_padded: workspace of %zu bytes needed, "
+                    "got %zu", ws, workspace_bytes);
+    if (!aligned(workspace, 4))
+        return fail(MOE_ERR_ALIGN, "moe_get_layout_padded: workspace must be 4-byte aligned");
+    clear_launch_error();
+    int32_t* H = static_cast<int32_t*>(workspace);
+    int32_t* bad = H + (int64_t)p.blocks * E;
+    if (p.blocks > 0)
+        layout_hist<<<p.blocks, kThreads, 0, stream>>>(ids, ids_row_stride, (uint32_t)nk,
+                                                       (uint32_t)K, E, p.chunk, p.nbits, H, bad);
+    layout_assign<<<p.blocks > 0 ? p.blocks : 1, kThreads, 0, stream>>>(
+        ids, ids_row_stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, 1, H, bad,
+        counts, nullptr, status, pos, row_pair, cap, M);
+    return check_launch("moe_get_layout_padded");
 }

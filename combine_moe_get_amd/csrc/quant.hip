@@ -1,0 +1,193 @@
+// quant.hip -- dispatch with an FP8 (e4m3fn) cast and per-128-channel scales,
+// the payload form of DeepEP's low-latency dispatch with use_fp8 (repository
+// dump, deep_ep.cpp, Buffer::low_latency_dispatch: bf16 x, e4m3 payload,
+// fp32 scales per token and 128 channels stored column-major, or 8-bit
+// exponents of power-of-two scales with use_ue8m0 and round_scale).
+//
+// The cast is not on the pages; this library takes, per token and block:
+// s = max(amax / 448, 2^-126), rounded up to a power of two with round_scale,
+// q = e4m3(x / s) with round to nearest even and saturation at +-448.
+//
+// Launch shape: one wave per (token, k, 512 channels). Lane i holds 8
+// channels (one 16-byte load); the 16 lanes of a 128-channel block find its
+// amax with four xor-shuffles, so every lane derives the same scale. Each
+// lane writes its 8 codes with one 8-byte non-temporal store (512 contiguous
+// bytes per wave). Workgroups are renumbered per XCD, as in the plain
+// dispatch, so the K waves re-reading a token's row share one L2.
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kXcds = 8;
+constexpr int kChanPerWave = kWave * 8;   // 512
+constexpr int kBlock = 128;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Fp8Args {
+    const uint16_t* x;
+    int64_t xs;          // elements
+    int32_t N, K, H, segs;
+    const int32_t* pos;  // NULL: identity (K == 1)
+    uint8_t* dst;
+    int64_t ds;          // bytes
+    void* scales;
+    int32_t mode;
+    int64_t srs;         // MOE_SCALE_ROWS: floats between rows
+    int32_t M;           // rows per expert for the column-major forms
+    int32_t round_scale;
+};
+
+// fp32 -> e4m3fn code on the bit pattern: round the 20 bits dropped below
+// the 3 kept mantissa bits to nearest even, rebias the exponent (127 -> 7),
+// saturate finite overflow at 448 (0x7E); below 2^-6 the codes are the
+// multiples of 2^-9, found by scaling by 2^9 (exact) and rounding to even.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;               // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;       // >= 448, and infinity
+    if (a < 0x3C800000u)                             // below 2^-6
+        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const uint32_t c = (r >> 20) - (120u << 3);
+    return sign | (c > 0x7Eu ? 0x7Eu : c);
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(const Fp8Args a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t per_xcd = gridDim.x / kXcds;
+    const uint32_t lb = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const uint32_t gw = lb * kWavesPerBlock + threadIdx.x / kWave;
+    const uint32_t pair = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
+    if (pair >= (uint32_t)a.N * (uint32_t)a.K) return;
+    const int32_t seg = (int32_t)(gw - pair * (uint32_t)a.segs);
+    const int32_t t = __builtin_amdgcn_readfirstlane(pair / (uint32_t)a.K);
+    const int32_t p = a.pos ? a.pos[pair] : t;
+    if (p < 0) return;
+
+    // The 16 lanes of a 128-channel block are either all inside H or all
+    // past it (H % 128 == 0); every lane takes part in the shuffles.
+    const int32_t c0 = seg * kChanPerWave + lane * 8;
+    const bool active = c0 < a.H;
+    float f[8];
+    if (active) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.xs + c0);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+
+    float s = amax / 448.0f;
+    s = fmaxf(s, __uint_as_float(0x00800000u));      // at least 2^-126
+    if (a.round_scale) {
+        const uint32_t sb = __float_as_uint(s);
+        if (sb & 0x007FFFFFu) s = __uint_as_float((sb & 0x7F800000u) + 0x00800000u);
+    }
+
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_code(f[i] / s) << (8 * i);
+        hi |= e4m3_code(f[4 + i] / s) << (8 * i);
+    }
+    if (active) {
+        const u32x2 codes = {lo, hi};
+        __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(a.dst + (int64_t)p * a.ds + c0));
+    }
+
+    const int32_t b = c0 / kBlock;                   // this lane's block
+    const int32_t nb = a.H / kBlock;
+    if (a.mode == MOE_SCALE_UE8M0) {
+        // the wave's 512 channels are exactly one word of four exponents
+        const uint32_t ex = __float_as_uint(s) >> 23;
+        const uint32_t word = __shfl(ex, 0, kWave) | (__shfl(ex, 16, kWave) << 8) |
+                              (__shfl(ex, 32, kWave) << 16) | (__shfl(ex, 48, kWave) << 24);
+        if (lane == 0 && active) {
+            const int64_t i = ((int64_t)(p / a.M) * (nb / 4) + seg) * a.M + p % a.M;
+            static_cast<uint32_t*>(a.scales)[i] = word;
+        }
+    } else if ((lane & 15) == 0 && active) {
+        const int64_t i = a.mode == MOE_SCALE_ROWS
+                              ? (int64_t)p * a.srs + b
+                              : ((int64_t)(p / a.M) * nb + b) * a.M + p % a.M;
+        static_cast<float*>(a.scales)[i] = s;
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K,
+                                int32_t H, const int32_t* pos, void* dst, int64_t dst_row_stride,
+                                void* scales, int32_t scale_format, int64_t scale_row_stride,
+                                int32_t rows_per_expert, int32_t round_scale, hipStream_t stream) {
+    if (N < 0 || K < 1 || H < 0)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: need N >= 0, K >= 1, H >= 0");
+    if (K > MOE_MAX_TOPK) return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8: K=%d > %d", K, MOE_MAX_TOPK);
+    if (scale_format < MOE_SCALE_ROWS || scale_format > MOE_SCALE_UE8M0)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: unknown scale_format %d", scale_format);
+    if (H % kBlock != 0)
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: H=%d must be a multiple of 128", H);
+    if (scale_format == MOE_SCALE_UE8M0 && (!round_scale || H % kChanPerWave != 0))
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: ue8m0 scales need round_scale and H %% 512 == 0");
+    if (scale_format != MOE_SCALE_ROWS && rows_per_expert < 1)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: column-major scales need rows_per_expert >= 1");
+    if (scale_format == MOE_SCALE_ROWS && scale_row_stride < H / kBlock)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: scale_row_stride < H/128");
+    if (pos == nullptr && K != 1 && N > 0)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: pos == NULL (identity) requires K == 1");
+    const int32_t segs = ceil_div<int32_t>(H, kChanPerWave);
+    const int64_t waves = (int64_t)N * K * segs;
+    if ((int64_t)N * K >= ((int64_t)1 << 31) || waves >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8: N*K*(H/512) must be below 2^31");
+    if (N == 0 || H == 0) return ok();
+    if (x == nullptr || dst == nullptr || scales == nullptr)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8: NULL pointer");
+    if (!aligned(x, 16) || x_row_stride % 8 != 0 || x_row_stride < H)
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: x must be 16-byte aligned with a row stride "
+                    "that is a multiple of 8 elements and >= H");
+    if (!aligned(dst, 8) || dst_row_stride % 8 != 0 || dst_row_stride < H)
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: dst must be 8-byte aligned with a row stride "
+                    "that is a multiple of 8 bytes and >= H");
+    if (!aligned(scales, 4) || !aligned(pos, 4))
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: scales and pos must be 4-byte aligned");
+
+    Fp8Args a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.xs = x_row_stride;
+    a.N = N;
+    a.K = K;
+    a.H = H;
+    a.segs = segs;
+    a.pos = pos;
+    a.dst = static_cast<uint8_t*>(dst);
+    a.ds = dst_row_stride;
+    a.scales = scales;
+    a.mode = scale_format;
+    a.srs = scale_row_stride;
+    a.M = rows_per_expert;
+    a.round_scale = round_scale ? 1 : 0;
+    const int64_t blocks =
+        ceil_div<int64_t>(ceil_div<int64_t>(waves, kWavesPerBlock), kXcds) * kXcds;
+    clear_launch_error();
+    dispatch_fp8_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(a);
+    return check_launch("moe_dispatch_fp8");
+}

@@ -180,6 +180,61 @@ int moe_combine(const void* y, int64_t y_row_stride, const float* w, int64_t w_r
                 int64_t out_row_stride, hipStream_t stream);
 
 /*
+ * Padded per-expert layout, the receive form of DeepEP's low-latency dispatch
+ * (repository dump, deep_ep.cpp, Buffer::low_latency_dispatch: packed_recv_x
+ * [num_local_experts, max_tokens, hidden] with packed_recv_count and the
+ * source of each row). Expert e owns rows e*M .. e*M+M-1; its pairs take them
+ * in ascending (t, k) order, and pairs beyond M are dropped (pos = -1).
+ *
+ *   counts[E]      (device, out) rows filled per expert, min(pairs, M).
+ *   pos[N*K]       (device, out) row of pair (t, k), -1 if masked, out of
+ *                  range or dropped.
+ *   row_pair[E*M]  (device, out) t*K + k of each row, -1 for unfilled rows.
+ *   status         (device, out, may be NULL) two int32: [0] ids >= E,
+ *                  [1] pairs dropped for capacity.
+ *   workspace      as for moe_get_layout (moe_layout_workspace_bytes).
+ * With M >= N and distinct ids per token nothing is dropped. Limits as
+ * moe_get_layout, plus M >= 1 and E*M < 2^31. Errors: MOE_ERR_ARG,
+ * MOE_ERR_LIMIT, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                          int32_t E, int32_t M, int32_t* counts, int32_t* pos, int32_t* row_pair,
+                          void* workspace, size_t workspace_bytes, int32_t* status,
+                          hipStream_t stream);
+
+/* Scale layouts of moe_dispatch_fp8. */
+#define MOE_SCALE_ROWS 0   /* fp32 [rows, H/128]: scales[row*scale_row_stride + b] */
+#define MOE_SCALE_COLS 1   /* fp32 column-major per expert, [E, H/128, M] */
+#define MOE_SCALE_UE8M0 2  /* int32 [E, H/512, M], byte j of a word = exponent of block 4i+j */
+
+/*
+ * Dispatch with an FP8 cast, as DeepEP's low-latency dispatch does with
+ * use_fp8 (repository dump, deep_ep.cpp, Buffer::low_latency_dispatch:
+ * bf16 x, e4m3 payload, fp32 scales per token and 128 channels stored
+ * column-major, or with use_ue8m0 -- which needs round_scale -- power-of-two
+ * scales as 8-bit exponents, four per int32). The cast itself is not on the
+ * pages; this library takes, per token and 128-channel block b:
+ *     amax = max |x|,  s = max(amax / 448, 2^-126)            (fp32)
+ *     round_scale: s = the smallest power of two >= s
+ *     q[h] = e4m3(x[h] / s)   (fp32 division; e4m3fn, round to nearest
+ *                              even, finite overflow saturates to +-448)
+ * For every valid pair, row p = pos[t*K+k] gets the H code bytes at
+ * dst + p*dst_row_stride and the H/128 scales in scale_format:
+ *   MOE_SCALE_ROWS   fp32 scales[p*scale_row_stride + b]
+ *   MOE_SCALE_COLS   fp32 scales[((p/M)*(H/128) + b)*M + p%M]   (M = rows_per_expert)
+ *   MOE_SCALE_UE8M0  int32 word ((p/M)*(H/512) + b/4)*M + p%M, byte b%4 = biased
+ *                    exponent of s (needs round_scale and H % 512 == 0)
+ * x: bf16 bits, 16-byte aligned, row stride a multiple of 8 elements;
+ * dst: 8-byte aligned, row stride a multiple of 8 bytes; scales 4-byte aligned.
+ * H % 128 == 0. Rows no pair maps to are left untouched. Errors:
+ * MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT, MOE_ERR_HIP.
+ */
+int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K, int32_t H,
+                     const int32_t* pos, void* dst, int64_t dst_row_stride, void* scales,
+                     int32_t scale_format, int64_t scale_row_stride, int32_t rows_per_expert,
+                     int32_t round_scale, hipStream_t stream);
+
+/*
  * Optional terms applied after the top-k sum by moe_combine_epilogue. All
  * pointers are device pointers to bf16 bits; row strides are in elements. A
  * NULL pointer leaves its term out.
@@ -219,7 +274,7 @@ typedef struct moe_epilogue {
  * reciprocal square root). ep == NULL is moe_combine.
  *
  * Alignment: y, out and every given row pointer 16-byte aligned with strides
- * multiples of 8 elements, Hc a multiple of 8. Limits: Hc <= 16384 when any
+ * multiples of 8 elements, Hc a multiple of 8. Limits: Hc <= 65536 when any
  * term is given, 1 <= K <= 32, eps >= 0. Errors: MOE_ERR_ARG (residual
  * without gamma or residual_out, negative eps), MOE_ERR_ALIGN, MOE_ERR_LIMIT,
  * MOE_ERR_HIP.

@@ -185,6 +185,29 @@ def test_combine_epilogue_validation(lib):
     assert L.moe_combine_epilogue(*args, ep(**dict(full, gamma=P + 8)), P, 64, 0) == lib.MOE_ERR_ALIGN
     assert L.moe_combine_epilogue(*args, ep(bias1=P, bias1_row_stride=32), P, 64, 0) == lib.MOE_ERR_ARG
     # the register-resident token row bounds Hc
-    assert L.moe_combine_epilogue(P, 16392, P, 8, P, 4, 8, 16392, ep(bias0=P, bias0_row_stride=16392),
-                                  P, 16392, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_combine_epilogue(P, 65544, P, 8, P, 4, 8, 65544, ep(bias0=P, bias0_row_stride=65544),
+                                  P, 65544, 0) == lib.MOE_ERR_LIMIT
     assert L.moe_combine_epilogue(P, 64, P, 8, P, 0, 8, 64, ep(**full), P, 64, 0) == lib.MOE_OK   # N = 0
+
+
+def test_layout_padded_and_fp8_validation(lib):
+    L = lib._lib
+    P = 0x10000
+    ws = lib.moe_layout_workspace_bytes(8, 8, 64)
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 0, P, P, P, P, ws, P, 0) == lib.MOE_ERR_ARG    # M = 0
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 1025, 4, P, P, P, P, ws, P, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 1024, 1 << 21, P, P, P, P, ws, P, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 4, P, P, P, 0, ws, P, 0) == lib.MOE_ERR_WORKSPACE
+    assert L.moe_get_layout_padded(P + 2, 8, 8, 8, 64, 4, P, P, P, P, ws, P, 0) == lib.MOE_ERR_ALIGN
+    F = L.moe_dispatch_fp8
+    assert F(P, 256, 4, 2, 200, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN         # H % 128
+    assert F(P, 512, 4, 2, 256, P, P, 256, P, 2, 0, 4, 0, 0) == lib.MOE_ERR_ARG           # ue8m0 w/o round
+    assert F(P, 256, 4, 2, 256, P, P, 256, P, 2, 0, 4, 1, 0) == lib.MOE_ERR_ARG           # ue8m0, H % 512
+    assert F(P, 256, 4, 2, 256, P, P, 256, P, 1, 0, 0, 0, 0) == lib.MOE_ERR_ARG           # cols need M
+    assert F(P, 256, 4, 2, 256, P, P, 256, P, 0, 1, 0, 0, 0) == lib.MOE_ERR_ARG           # row stride
+    assert F(P, 256, 4, 2, 256, P, P, 256, P, 7, 2, 0, 0, 0) == lib.MOE_ERR_ARG           # format
+    assert F(P + 8, 256, 4, 2, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN     # x alignment
+    assert F(P, 256, 4, 2, 256, P, P + 4, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN     # dst alignment
+    assert F(P, 256, 4, 2, 256, 0, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ARG           # identity, K=2
+    assert F(P, 256, 4, 33, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_LIMIT
+    assert F(P, 256, 0, 2, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_OK                # N = 0

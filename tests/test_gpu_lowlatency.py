@@ -1,0 +1,155 @@
+"""GPU parity of the low-latency forms: the padded per-expert layout and the
+FP8 (e4m3) cast on dispatch, against the oracle. Bar: bit-exact (layout,
+codes and scales; the cast decides integer codes, and both sides take that
+decision in fp32: amax, one fp32 division by the scale, round to nearest
+even)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_moe_get_amd as m
+
+    return m
+
+
+def say(msg):
+    print(f"[gpu-lowlatency] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def padded(mg, ids_np, E, M):
+    N, K = ids_np.shape
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    pos = torch.empty((N, K), dtype=torch.int32, device="cuda")
+    row_pair = torch.empty(E * M, dtype=torch.int32, device="cuda")
+    status = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(mg.moe_layout_workspace_bytes(N, K, E), 256), dtype=torch.uint8, device="cuda")
+    mg.moe_get_layout_padded(dev(ids_np), E, M, counts, pos, row_pair, ws, status)
+    torch.cuda.synchronize()
+    c, p, rp, st = oracle.layout_padded(ids_np, E, M)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(pos.cpu().numpy(), p)
+    assert np.array_equal(row_pair.cpu().numpy(), rp)
+    assert tuple(status.cpu().tolist()) == st
+    return pos, p
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_padded_layout_random(mg, seed):
+    rng = np.random.default_rng(200 + seed)
+    E = int(rng.choice([1, 8, 64, 256, 1024]))
+    K = int(rng.choice([1, 2, 4, 8]))
+    N = int(rng.choice([1, 50, 128, 1000, 4096]))
+    M = int(rng.choice([N, max(1, N // 8), 1, 3]))
+    ids = rng.integers(-1, E + 1, size=(N, K)).astype(np.int32)
+    say(f"padded seed={seed} N={N} K={K} E={E} M={M}")
+    padded(mg, ids, E, M)
+
+
+def test_padded_layout_decode_and_prefill_shapes(mg):
+    for name, M in (("decode", 128), ("prefill", 4096)):
+        wl = mw.make(name)
+        say(f"padded {name} M={M}")
+        _, p = padded(mg, wl.ids, wl.E, M)
+        assert (p >= 0).all()                        # nothing dropped with M >= N
+
+
+def _x(rng, N, H):
+    x = rng.standard_normal((N, H)) * np.exp(rng.standard_normal((N, 1)) * 2)
+    x[0, :128] = 0.0                                  # an all-zero block
+    if N > 1:
+        x[1, -128:] = 1e30                            # a block of huge values
+        x[1, H // 2 + 3] = -2.0 ** -130               # a bf16 subnormal
+    return mw.bf16_bits_from_f32(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt,round_scale", [(0, False), (0, True), (1, False), (1, True), (2, True)])
+def test_fp8_dispatch_decode_padded(mg, fmt, round_scale):
+    """The decode setting of the low-latency kernels: 128 tokens, hidden 7168,
+    top-8 of 256 experts, padded receive buffer M = 128."""
+    rng = np.random.default_rng(7 + fmt)
+    N, K, E, H, M = 128, 8, 256, 7168, 128
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    x = _x(rng, N, H)
+    pos_d, pos = padded(mg, ids, E, M)
+    rows = E * M
+    say(f"fp8 decode format={fmt} round_scale={round_scale}")
+    dst = torch.full((rows, H), 0xA5, dtype=torch.uint8, device="cuda")
+    if fmt == 0:
+        scales = torch.zeros((rows, H // 128), dtype=torch.float32, device="cuda")
+    elif fmt == 1:
+        scales = torch.zeros((E, H // 128, M), dtype=torch.float32, device="cuda")
+    else:
+        scales = torch.zeros((E, H // 512, M), dtype=torch.int32, device="cuda")
+    x_d = dev(x.view(np.int16)).view(torch.bfloat16)
+    mg.moe_dispatch_fp8(x_d, pos_d, K, dst, scales, fmt, M, round_scale)
+    torch.cuda.synchronize()
+    codes, ref_scales = oracle.dispatch_fp8(x, pos, rows, fmt, M, round_scale, fill=0xA5)
+    assert np.array_equal(dst.cpu().numpy(), codes)
+    got = scales.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref_scales.view(np.uint32))
+
+
+def test_fp8_dispatch_prefill_rows(mg):
+    wl = mw.make("prefill")
+    rng = np.random.default_rng(11)
+    N, H = wl.N, 7168
+    x = _x(rng, N, H)
+    lay = mg.layout(dev(wl.ids), wl.E)
+    torch.cuda.synchronize()
+    pos = lay.pos.cpu().numpy()
+    say("fp8 prefill rows")
+    dst = torch.empty((lay.cap, H), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((lay.cap, H // 128), dtype=torch.float32, device="cuda")
+    mg.moe_dispatch_fp8(dev(x.view(np.int16)).view(torch.bfloat16), lay.pos, wl.K, dst, scales)
+    torch.cuda.synchronize()
+    codes, ref_scales = oracle.dispatch_fp8(x, pos, lay.cap)
+    assert np.array_equal(dst.cpu().numpy(), codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+
+
+@pytest.mark.parametrize("H", [128, 384, 640])
+def test_fp8_identity_partial_segments(mg, H):
+    """pos = None quantises N tokens in place order; H not a multiple of 512
+    leaves part of the last wave idle."""
+    rng = np.random.default_rng(H)
+    N = 33
+    x = _x(rng, N, H)
+    dst = torch.full((N, H), 0x11, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((N, H // 128 + 3), dtype=torch.float32, device="cuda")   # padded stride
+    mg.moe_dispatch_fp8(dev(x.view(np.int16)).view(torch.bfloat16), None, 1, dst, scales)
+    torch.cuda.synchronize()
+    codes, ref_scales = oracle.dispatch_fp8(x, np.arange(N, dtype=np.int32).reshape(N, 1), N)
+    assert np.array_equal(dst.cpu().numpy(), codes)
+    s = scales.cpu().numpy()
+    assert np.array_equal(s[:, :H // 128].view(np.uint32), ref_scales.view(np.uint32))
+    assert (s[:, H // 128:] == 0).all()
+
+
+def test_fp8_codes_decode_to_torch_float8(mg):
+    """The codes are OCP e4m3fn: torch reads them back as float8_e4m3fn."""
+    rng = np.random.default_rng(5)
+    N, H = 8, 512
+    x = _x(rng, N, H)
+    dst = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((N, H // 128), dtype=torch.float32, device="cuda")
+    mg.moe_dispatch_fp8(dev(x.view(np.int16)).view(torch.bfloat16), None, 1, dst, scales)
+    deq = dst.view(torch.float8_e4m3fn).float() * scales.repeat_interleave(128, dim=1)
+    xf = dev(x.view(np.int16)).view(torch.bfloat16).float()
+    ok = (deq - xf).abs() <= xf.abs() * 2.0 ** -4 + scales.repeat_interleave(128, dim=1) * 2.0 ** -10
+    assert bool(ok.all())
