@@ -68,6 +68,7 @@ KERNEL_SOURCES = {
     "dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
     "layout_hist": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
     "layout_assign": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
+    "dispatch_fp8_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
@@ -248,6 +249,77 @@ class BufferSet:
         return (L.moe_get_layout, lay), (L.moe_dispatch, dis), (L.moe_combine_epilogue, com)
 
 
+SCALE_FORMATS = {"rows": 0, "cols": 1, "ue8m0": 2}
+
+
+def ll_algorithmic_bytes(N, K, E, M, H, Hc, R, scale_format):
+    """Minimum bytes of the low-latency step. Layout: ids in, counts, pos
+    and the whole padded row_pair table (E*M entries, unused rows -1) out.
+    Dispatch: each token's bf16 row read once, pos, and per landed pair H
+    e4m3 codes plus its scales (4 B per 128 channels, or 1 B per 128 as
+    packed UE8M0 exponents). Combine as in the plain step."""
+    layout = 4 * N * K + 4 * E + 4 * N * K + 4 * E * M + 8
+    sb = H // 128 if scale_format == "ue8m0" else 4 * (H // 128)
+    dispatch = 2 * N * H + 4 * N * K + R * (H + sb)
+    combine = R * Hc * 2 + 8 * N * K + N * Hc * 2
+    return layout, dispatch, combine
+
+
+class LowLatencySet:
+    """Device inputs and outputs of one low-latency step: padded layout (M
+    rows per expert), bf16 -> e4m3 cast on dispatch with per-128-channel
+    scales, combine reading the expert outputs from the padded buffer."""
+
+    def __init__(self, torch, mg, wl, x_bits, y_bits, M, scale_format, round_scale):
+        d = "cuda"
+        N, K, E, Hc = wl.N, wl.K, wl.E, wl.Hc
+        H = x_bits.shape[1]
+        self.M, self.H, self.fmt = M, H, SCALE_FORMATS[scale_format]
+        self.round_scale = int(round_scale)
+        self.ids = torch.from_numpy(np.ascontiguousarray(wl.ids)).to(d)
+        self.w = torch.from_numpy(np.ascontiguousarray(wl.weights)).to(d)
+        self.x = torch.from_numpy(x_bits.view(np.int16)).to(d).view(torch.bfloat16)
+        self.counts = torch.empty(E, dtype=torch.int32, device=d)
+        self.pos = torch.empty((N, K), dtype=torch.int32, device=d)
+        self.row_pair = torch.empty(E * M, dtype=torch.int32, device=d)
+        self.status = torch.empty(2, dtype=torch.int32, device=d)
+        self.ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device=d)
+        self.codes = torch.empty((E * M, H), dtype=torch.uint8, device=d)
+        if self.fmt == 0:
+            self.scales = torch.empty((E * M, H // 128), dtype=torch.float32, device=d)
+        elif self.fmt == 1:
+            self.scales = torch.empty((E, H // 128, M), dtype=torch.float32, device=d)
+        else:
+            self.scales = torch.empty((E, H // 512, M), dtype=torch.int32, device=d)
+        self.out = torch.empty((N, Hc), dtype=torch.bfloat16, device=d)
+        # Expert outputs in the padded layout: pair (t, k) finds the
+        # workload's y row t*K + k at its padded row; other rows are unused.
+        mg.moe_get_layout_padded(self.ids, E, M, self.counts, self.pos, self.row_pair,
+                                 self.ws, self.status)
+        torch.cuda.synchronize()
+        st = self.status.cpu().tolist()
+        if st != [0, 0]:
+            raise SystemExit(f"low-latency bench needs no bad ids and no drops (status {st}); "
+                             f"raise --rows-per-expert above {M}")
+        y = torch.from_numpy(y_bits.view(np.int16)).to(d).view(torch.bfloat16)
+        self.y = torch.empty((E * M, Hc), dtype=torch.bfloat16, device=d)
+        self.y[self.pos.flatten().long()] = y
+        del y
+
+    def calls(self, mg, wl, stream, epilogue=False):
+        L = mg._lib
+        N, K, E, Hc, H, M = wl.N, wl.K, wl.E, wl.Hc, self.H, self.M
+        srs = H // 128 if self.fmt == 0 else 0
+        lay = (self.ids.data_ptr(), K, N, K, E, M, self.counts.data_ptr(), self.pos.data_ptr(),
+               self.row_pair.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+               self.status.data_ptr(), stream)
+        dis = (self.x.data_ptr(), H, N, K, H, self.pos.data_ptr(), self.codes.data_ptr(), H,
+               self.scales.data_ptr(), self.fmt, srs, M, self.round_scale, stream)
+        com = (self.y.data_ptr(), Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K, Hc,
+               self.out.data_ptr(), Hc, stream)
+        return (L.moe_get_layout_padded, lay), (L.moe_dispatch_fp8, dis), (L.moe_combine, com)
+
+
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     """A plain device copy (read + write) of `nbytes`: the achievable-HBM
     reference next to the 8 TB/s spec."""
@@ -282,23 +354,68 @@ def cpu_baseline(wl, y, total_bytes, budget_s):
         oracle.dispatch(srcs, pos, wl.K, dsts=dsts)
         oracle.combine(y, w, pos)
 
-    one()   # warm host caches and page in outputs
-    times = []
-    t_all = time.perf_counter()
-    while not times or (time.perf_counter() - t_all < budget_s and len(times) < 50):
-        t0 = time.perf_counter()
-        one()
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return _time_oracle(one, wl, total_bytes, budget_s,
+                        f"full {wl.name} steps (layout+dispatch+combine)")
+
+
+def _time_oracle(one, wl, total_bytes, budget_s, what):
+    """Median step time of the oracle at the configured thread count, then
+    again on one thread (the layout is serial either way)."""
+    import oracle
+
+    def run(budget):
+        one()   # warm host caches and page in outputs
+        times = []
+        t_all = time.perf_counter()
+        while not times or (time.perf_counter() - t_all < budget and len(times) < 50):
+            t0 = time.perf_counter()
+            one()
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    cores = int(oracle.lib().omp_get_max_threads())
+    t, n = run(budget_s)
+    prev = oracle.set_threads(1)
+    try:
+        t1, n1 = run(budget_s / 2)
+    finally:
+        oracle.set_threads(prev)
     return {
         "value": round(total_bytes / t / 1e9, 3),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{len(times)} full {wl.name} steps (layout+dispatch+combine), median "
-                  f"{t * 1e3:.1f} ms/step, {wl.N / t:.0f} tokens/s",
+        "sample": f"{n} {what}, median {t * 1e3:.1f} ms/step, {wl.N / t:.0f} tokens/s",
+        "single_thread": {"value": round(total_bytes / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                          "sample": f"{n1} steps, median {t1 * 1e3:.1f} ms/step"},
     }
+
+
+def cpu_baseline_ll(wl, x, y, M, scale_format, round_scale, total_bytes, budget_s):
+    """The oracle on the host cores for the low-latency step: padded layout
+    (serial), FP8 cast on dispatch and combine (OpenMP over tokens)."""
+    import oracle
+
+    E, Hc, H = wl.E, wl.Hc, x.shape[1]
+    fmt = SCALE_FORMATS[scale_format]
+    w = np.ascontiguousarray(wl.weights)
+    _, pos0, _, _ = oracle.layout_padded(wl.ids, E, M)
+    # padded buffers are allocated untouched; only the landed rows page in
+    codes = np.empty((E * M, H), np.uint8)
+    sshape = {0: ((E * M, H // 128), np.float32), 1: ((E, H // 128, M), np.float32),
+              2: ((E, H // 512, M), np.int32)}[fmt]
+    scales = np.empty(*sshape)
+    y_pad = np.empty((E * M, Hc), np.uint16)
+    y_pad[pos0.reshape(-1)] = y
+
+    def one():
+        _, pos, _, _ = oracle.layout_padded(wl.ids, E, M)
+        oracle.dispatch_fp8(x, pos, E * M, fmt, M, round_scale, codes=codes, scales=scales)
+        oracle.combine(y_pad, w, pos)
+
+    return _time_oracle(one, wl, total_bytes, budget_s,
+                        f"full low-latency {wl.name} steps (padded layout + fp8 cast dispatch "
+                        "+ combine)")
 
 
 def main():
@@ -312,18 +429,32 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ref", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--epilogue", action="store_true",
                     help="combine with the fused residual add + RMSNorm epilogue "
                          "(moe_combine_epilogue) instead of the plain combine")
+    ap.add_argument("--lowlatency", action="store_true",
+                    help="time the low-latency form instead: padded per-expert layout, "
+                         "bf16 -> e4m3 cast on dispatch, combine from the padded buffer")
+    ap.add_argument("--rows-per-expert", type=int, default=0,
+                    help="padded rows per expert for --lowlatency (default: N, no drops)")
+    ap.add_argument("--scale-format", choices=list(SCALE_FORMATS), default="cols",
+                    help="--lowlatency scales: rows, cols (column-major fp32) or ue8m0")
+    ap.add_argument("--round-scale", action="store_true",
+                    help="--lowlatency: round scales up to powers of two (implied by ue8m0)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench into profiles/traffic.json and exit (no GPU needed)")
     ap.add_argument("--traffic-command", default="",
                     help="the profiled command, recorded next to the figures")
     args = ap.parse_args()
+    workload_key = args.config + ("-lowlatency" if args.lowlatency else "")
     if args.traffic_from:
-        summarize_traffic(*args.traffic_from, args.config, args.traffic_command)
+        summarize_traffic(*args.traffic_from, workload_key, args.traffic_command)
         return
+    if args.lowlatency and args.epilogue:
+        raise SystemExit("--lowlatency and --epilogue are separate measurements")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -343,7 +474,14 @@ def main():
     N, K, E, Hc = wl.N, wl.K, wl.E, wl.Hc
     P = wl.payload_bytes()
     R = N * K
-    sets = [BufferSet(torch, mg, wl, y) for _ in range(max(1, args.sets))]
+    M = args.rows_per_expert or N
+    round_scale = args.round_scale or args.scale_format == "ue8m0"
+    if args.lowlatency:
+        x = mw.make_x(N, 7168, wl.seed + 104729)
+        sets = [LowLatencySet(torch, mg, wl, x, y, M, args.scale_format, round_scale)
+                for _ in range(max(1, args.sets))]
+    else:
+        sets = [BufferSet(torch, mg, wl, y) for _ in range(max(1, args.sets))]
     stream = torch.cuda.current_stream()
     calls = [s.calls(mg, wl, stream.cuda_stream, args.epilogue) for s in sets]
 
@@ -362,7 +500,9 @@ def main():
 
     def timed_pass(op_events):
         """K steps between two synchronizations; with op_events, a
-        timing-only event is also recorded before and after every op."""
+        timing-only event is also recorded before and after every op.
+        Returns the mean step time and, with op_events, the per-step op
+        times [K, 3]."""
         ev = [[hev.create() for _ in range(4)] for _ in range(args.steps)] if op_events else None
         t0, t1 = hev.create(), hev.create()
         torch.cuda.synchronize()
@@ -380,25 +520,75 @@ def main():
         step_ms = hev.ms(t0, t1) / args.steps
         op = None
         if op_events:
-            op = np.array([[hev.ms(e[j], e[j + 1]) for j in range(3)] for e in ev]).mean(axis=0)
+            op = np.array([[hev.ms(e[j], e[j + 1]) for j in range(3)] for e in ev])
         return step_ms, op
 
     # The headline figure: whole steps, nothing recorded between the ops.
     ms_per_step, _ = timed_pass(False)
-    # Per-op times (and the combine kernel's duration for the roofline) from
-    # a second timed pass with an event between the ops.
-    ms_per_step_op_events, op_ms = timed_pass(True)
+    # Per-op times (and the roofline kernel's duration) from a second timed
+    # pass with an event between the ops.
+    ms_per_step_op_events, op_all = timed_pass(True)
+    op_ms = op_all.mean(axis=0)
+
+    # The same steps captured once in a HIP graph (one step per buffer set)
+    # and replayed: the launch cost the host pays per op drops out.
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            cs = torch.cuda.current_stream().cuda_stream
+            gcalls = [st.calls(mg, wl, cs, args.epilogue) for st in sets]
+            for c in gcalls:
+                for fn, a in c:
+                    if fn(*a) != 0:
+                        raise mg.MoeError(-6, mg._lib.moe_last_error().decode())
+        reps = max(1, args.steps // len(sets))
+        for _ in range(2):
+            g.replay()
+        t0, t1 = hev.create(), hev.create()
+        torch.cuda.synchronize()
+        hev.record(t0, sh)
+        for _ in range(reps):
+            g.replay()
+        hev.record(t1, sh)
+        torch.cuda.synchronize()
+        graph_ms = hev.ms(t0, t1) / (reps * len(sets))
+        del g, gcalls
     hev.close()
 
-    b_lay, b_dis, b_com = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
+    if args.lowlatency:
+        b_lay, b_dis, b_com = ll_algorithmic_bytes(N, K, E, M, 7168, Hc, R, args.scale_format)
+    else:
+        b_lay, b_dis, b_com = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
     total = b_lay + b_dis + b_com
     value = total / (ms_per_step * 1e-3) / 1e9
-    combine_gbs = b_com / (op_ms[2] * 1e-3) / 1e9
-    ckernel = "combine_epilogue_kernel" if args.epilogue else "combine_kernel"
-    traffic = traffic_entry(ckernel, args.config)
+    # the roofline is taken on the longer of the two streaming kernels
+    if args.lowlatency and op_ms[1] > op_ms[2]:
+        rop, rkernel, rbytes = 1, "dispatch_fp8_kernel", b_dis
+    else:
+        rop, rbytes = 2, b_com
+        rkernel = "combine_epilogue_kernel" if args.epilogue else "combine_kernel"
+    roof_gbs = rbytes / (op_ms[rop] * 1e-3) / 1e9
+    traffic = traffic_entry(rkernel, workload_key)
+    if args.lowlatency:
+        workload = (f"{args.config} low-latency: N={N} tokens, top-{K} of {E} experts, padded "
+                    f"{M} rows per expert, bf16 hidden 7168 cast to e4m3 on dispatch with "
+                    f"{args.scale_format} scales per 128 channels"
+                    + (" (power-of-two)" if round_scale else "")
+                    + f", combine bf16 hidden {Hc}, fp32 accumulation")
+        metric = ("low-latency dispatch (fp8 cast) + combine effective HBM GB/s and tokens/s, "
+                  f"{N}×7168 top-{K}, 1 GPU")
+    else:
+        workload = (f"{args.config}: N={N} tokens, top-{K} of {E} experts, dispatch payload "
+                    f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields)}), "
+                    f"combine bf16 hidden {Hc}, fp32 accumulation"
+                    + (", fused residual add + RMSNorm epilogue" if args.epilogue else ""))
+        metric = METRIC
 
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -411,36 +601,45 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.config}: N={N} tokens, top-{K} of {E} experts, dispatch payload "
-                        f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields)}), "
-                        f"combine bf16 hidden {Hc}, fp32 accumulation"
-                        + (", fused residual add + RMSNorm epilogue" if args.epilogue else ""),
-            "tokens": N, "topk": K, "experts": E, "hidden": Hc, "payload_bytes": P,
+            "workload": workload,
+            "tokens": N, "topk": K, "experts": E, "hidden": Hc,
+            "payload_bytes": (7168 * 2 if args.lowlatency else P),
             "buffer_sets": len(sets), "algorithmic_bytes_per_step": total,
         },
         "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_with_op_events": round(ms_per_step_op_events, 5),
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
+        "per_op_us_p10_p50_p90": {
+            name: [round(float(np.percentile(op_all[:, j], q)) * 1e3, 2) for q in (10, 50, 90)]
+            for j, name in enumerate(("layout", "dispatch", "combine"))},
         "per_op_us": {"layout": round(op_ms[0] * 1e3, 2), "dispatch": round(op_ms[1] * 1e3, 2),
                       "combine": round(op_ms[2] * 1e3, 2)},
         "per_op_gbs": {"layout": round(b_lay / (op_ms[0] * 1e-3) / 1e9, 1),
                        "dispatch": round(b_dis / (op_ms[1] * 1e-3) / 1e9, 1),
-                       "combine": round(combine_gbs, 1)},
+                       "combine": round(b_com / (op_ms[2] * 1e-3) / 1e9, 1)},
         "roofline": {
-            "kernel": ckernel,
+            "kernel": rkernel,
             "bound": "hbm",
-            "achieved": round(combine_gbs, 1),
+            "achieved": round(roof_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(combine_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
-            "algorithmic_bytes_per_launch": b_com,
+            "algorithmic_bytes_per_launch": rbytes,
         },
     }
     if not args.no_copy_ref:
         result["copy_ref_gbs"] = round(copy_bandwidth(torch), 1)
+    if args.lowlatency:
+        result["config"]["rows_per_expert"] = M
+        result["config"]["scale_format"] = args.scale_format
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, y, total, args.cpu_seconds)
+        if args.lowlatency:
+            result["cpu_baseline"] = cpu_baseline_ll(wl, x, y, M, args.scale_format, round_scale,
+                                                     total, args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline(wl, y, total, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -35,7 +35,7 @@ constexpr int kThreads = 256;              // hist / assign workgroup
 constexpr int kWaves = kThreads / kWave;   // 4
 constexpr int kHEntries = 16384;           // bound on chunks * padded experts
 constexpr int kMaxChunks = 64;
-constexpr int kPrefetch = 16;              // 64-pair steps of ids held in registers
+constexpr int kPrefetch = 4;               // 64-pair steps of ids held in registers
 
 struct Plan {
     int32_t chunk;    // pairs per workgroup (multiple of kThreads)
@@ -216,12 +216,11 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
 
 // Per expert e (columns tid, tid+256, ... of H): pairs in chunks before b
 // (before_s) and in all chunks (total_s). C columns per thread and at most
-// 64/C chunks, so every load is issued before the first sum.
-template <int C>
+// R chunks, so every load is issued before the first sum.
+template <int C, int R>
 __device__ __forceinline__ void reduce_chunks(const int32_t* __restrict__ H, int32_t blocks,
                                               int32_t E, int b, int32_t* total_s,
                                               int32_t* before_s) {
-    constexpr int R = kMaxChunks / C;
     int32_t v[C][R];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -269,12 +268,21 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     // together; the ids stay in registers for both passes below.
     int32_t e_first[kPrefetch];
     load_ids(e_first, ids, stride, nk, K, first, 0, steps, lane);
-    if (E <= kThreads)
-        reduce_chunks<1>(H, blocks, E, b, total_s, base);
-    else if (E <= 2 * kThreads)
-        reduce_chunks<2>(H, blocks, E, b, total_s, base);
-    else
-        reduce_chunks<4>(H, blocks, E, b, total_s, base);
+    // Few chunks (small batches) take a short form of the reduction: the
+    // straight-line code a workgroup runs once is fetched into a cold
+    // instruction cache, so its length shows in small-batch latency.
+    if (blocks <= 16) {
+        if (E <= kThreads)
+            reduce_chunks<1, 16>(H, blocks, E, b, total_s, base);
+        else
+            reduce_chunks<4, 16>(H, blocks, E, b, total_s, base);
+    } else if (E <= kThreads) {
+        reduce_chunks<1, kMaxChunks>(H, blocks, E, b, total_s, base);
+    } else if (E <= 2 * kThreads) {
+        reduce_chunks<2, kMaxChunks / 2>(H, blocks, E, b, total_s, base);
+    } else {
+        reduce_chunks<4, kMaxChunks / 4>(H, blocks, E, b, total_s, base);
+    }
     for (int x = threadIdx.x; x < kWaves * E; x += kThreads) cnt[x] = 0;
     __syncthreads();
 
@@ -360,14 +368,23 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     }
 
     // Rows no pair landed in: past the used rows, and alignment padding.
+    if (M > 0) {
+        // padded form: every workgroup of the grid (which may exceed the
+        // chunks) takes a strided share of the E*M rows
+        for (int64_t r = (int64_t)b * kThreads + threadIdx.x; r < cap;
+             r += (int64_t)gridDim.x * kThreads) {
+            const int32_t e = (int32_t)((uint32_t)r / (uint32_t)M);
+            if ((int32_t)r - e * M >= min(total_s[e], M)) row_pair[r] = -1;
+        }
+        return;
+    }
     for (int64_t r = used_s + (int64_t)b * kThreads + threadIdx.x; r < cap;
          r += (int64_t)gridDim.x * kThreads)
         row_pair[r] = -1;
-    if (align > 1 || M > 0) {
+    if (align > 1) {
         for (int e = b; e < E; e += gridDim.x) {
             const int32_t hi = e + 1 < E ? start_s[e + 1] : used_s;
-            const int32_t filled = M > 0 ? min(total_s[e], M) : total_s[e];
-            for (int32_t r = start_s[e] + filled + threadIdx.x; r < hi; r += kThreads)
+            for (int32_t r = start_s[e] + total_s[e] + threadIdx.x; r < hi; r += kThreads)
                 row_pair[r] = -1;
         }
     }
@@ -479,7 +496,13 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     if (p.blocks > 0)
         layout_hist<<<p.blocks, kThreads, 0, stream>>>(ids, ids_row_stride, (uint32_t)nk,
                                                        (uint32_t)K, E, p.chunk, p.nbits, H, bad);
-    layout_assign<<<p.blocks > 0 ? p.blocks : 1, kThreads, 0, stream>>>(
+    // Workgroups past the chunks only mark unused rows: one per 2048 rows,
+    // at most 256.
+    int64_t grid = ceil_div<int64_t>(cap, 8 * kThreads);
+    if (grid > 256) grid = 256;
+    if (grid < p.blocks) grid = p.blocks;
+    if (grid < 1) grid = 1;
+    layout_assign<<<(uint32_t)grid, kThreads, 0, stream>>>(
         ids, ids_row_stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, 1, H, bad,
         counts, nullptr, status, pos, row_pair, cap, M);
     return check_launch("moe_get_layout_padded");

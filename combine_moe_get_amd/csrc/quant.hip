@@ -8,24 +8,21 @@
 // s = max(amax / 448, 2^-126), rounded up to a power of two with round_scale,
 // q = e4m3(x / s) with round to nearest even and saturation at +-448.
 //
-// Launch shape: one wave per (token, k, 512 channels). Lane i holds 8
-// channels (one 16-byte load); the 16 lanes of a 128-channel block find its
-// amax with four xor-shuffles, so every lane derives the same scale. Each
-// lane writes its 8 codes with one 8-byte non-temporal store (512 contiguous
-// bytes per wave). Workgroups are renumbered per XCD, as in the plain
-// dispatch, so the K waves re-reading a token's row share one L2.
+// The cast depends on the token only, so one wave quantises a (token, 1024
+// channels) slice once and writes it to the rows of all K pairs. Lane i
+// holds 16 channels (two 16-byte loads); the 8 lanes of a 128-channel block
+// exchange their partial amax with three DPP lane swaps, so every lane of
+// the block derives the same scale. Each destination row then takes one
+// 16-byte non-temporal store per lane: 1 KiB contiguous per wave and row.
 #include "internal.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kXcds = 8;
-constexpr int kChanPerWave = kWave * 8;   // 512
+constexpr int kChanPerLane = 16;
+constexpr int kChanPerWave = kWave * kChanPerLane;   // 1024
 constexpr int kBlock = 128;
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kLanesPerBlock = kBlock / kChanPerLane;  // 8
 
 struct Fp8Args {
     const uint16_t* x;
@@ -58,40 +55,54 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
     return sign | (c > 0x7Eu ? 0x7Eu : c);
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(const Fp8Args a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t per_xcd = gridDim.x / kXcds;
-    const uint32_t lb = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    const uint32_t gw = lb * kWavesPerBlock + threadIdx.x / kWave;
-    const uint32_t pair = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
-    if (pair >= (uint32_t)a.N * (uint32_t)a.K) return;
-    const int32_t seg = (int32_t)(gw - pair * (uint32_t)a.segs);
-    const int32_t t = __builtin_amdgcn_readfirstlane(pair / (uint32_t)a.K);
-    const int32_t p = a.pos ? a.pos[pair] : t;
-    if (p < 0) return;
+// max of v over the 8 lanes of an aligned lane group (DPP within a row of
+// 16 lanes: swap neighbours, swap pairs, then mirror the two quads).
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    return v;
+}
 
-    // The 16 lanes of a 128-channel block are either all inside H or all
-    // past it (H % 128 == 0); every lane takes part in the shuffles.
-    const int32_t c0 = seg * kChanPerWave + lane * 8;
+__device__ __forceinline__ uint32_t pack4(const float* f, float s) {
+    return e4m3_code(f[0] / s) | (e4m3_code(f[1] / s) << 8) | (e4m3_code(f[2] / s) << 16) |
+           (e4m3_code(f[3] / s) << 24);
+}
+
+__global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t gw = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
+    if (t >= (uint32_t)a.N) return;
+    const int32_t seg = (int32_t)(gw - t * (uint32_t)a.segs);
+
+    // Rows of the token's K pairs: lane k < K fetches pos[t*K + k].
+    int32_t pk = (int32_t)t;
+    if (a.pos != nullptr) pk = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
+
+    // The 8 lanes of a 128-channel block are either all inside H or all
+    // past it (H % 128 == 0); every lane takes part in the lane swaps.
+    const int32_t c0 = seg * kChanPerWave + lane * kChanPerLane;
     const bool active = c0 < a.H;
-    float f[8];
+    float f[16];
     if (active) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.xs + c0);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.xs + c0);
+        const u32x4 v0 = __builtin_nontemporal_load(src);
+        const u32x4 v1 = __builtin_nontemporal_load(src + 1);
+        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             f[2 * i] = __uint_as_float(w[i] << 16);
             f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) f[i] = 0.0f;
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = group8_max(amax);
 
     float s = amax / 448.0f;
     s = fmaxf(s, __uint_as_float(0x00800000u));      // at least 2^-126
@@ -99,34 +110,33 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(const Fp8Args a)
         const uint32_t sb = __float_as_uint(s);
         if (sb & 0x007FFFFFu) s = __uint_as_float((sb & 0x7F800000u) + 0x00800000u);
     }
-
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_code(f[i] / s) << (8 * i);
-        hi |= e4m3_code(f[4 + i] / s) << (8 * i);
-    }
-    if (active) {
-        const u32x2 codes = {lo, hi};
-        __builtin_nontemporal_store(codes, reinterpret_cast<u32x2*>(a.dst + (int64_t)p * a.ds + c0));
-    }
+    const u32x4 codes = {pack4(f, s), pack4(f + 4, s), pack4(f + 8, s), pack4(f + 12, s)};
 
     const int32_t b = c0 / kBlock;                   // this lane's block
     const int32_t nb = a.H / kBlock;
-    if (a.mode == MOE_SCALE_UE8M0) {
-        // the wave's 512 channels are exactly one word of four exponents
-        const uint32_t ex = __float_as_uint(s) >> 23;
-        const uint32_t word = __shfl(ex, 0, kWave) | (__shfl(ex, 16, kWave) << 8) |
-                              (__shfl(ex, 32, kWave) << 16) | (__shfl(ex, 48, kWave) << 24);
-        if (lane == 0 && active) {
-            const int64_t i = ((int64_t)(p / a.M) * (nb / 4) + seg) * a.M + p % a.M;
-            static_cast<uint32_t*>(a.scales)[i] = word;
+    // UE8M0: each 512 channels (32 lanes) form one word of four exponents,
+    // assembled in lanes 0 and 32 from the first lane of each block.
+    const uint32_t ex = __float_as_uint(s) >> 23;
+    const uint32_t up8 = __shfl_down(ex, 8, kWave), up16 = __shfl_down(ex, 16, kWave),
+                   up24 = __shfl_down(ex, 24, kWave);
+    const uint32_t word = ex | (up8 << 8) | (up16 << 16) | (up24 << 24);
+
+    for (int32_t k = 0; k < a.K; ++k) {
+        const int32_t p = __builtin_amdgcn_readlane(pk, k);
+        if (p < 0) continue;
+        if (active)
+            __builtin_nontemporal_store(codes, reinterpret_cast<u32x4*>(a.dst + (int64_t)p * a.ds + c0));
+        if (a.mode == MOE_SCALE_UE8M0) {
+            if ((lane & 31) == 0 && active) {
+                const int64_t i = ((int64_t)(p / a.M) * (nb / 4) + b / 4) * a.M + p % a.M;
+                static_cast<uint32_t*>(a.scales)[i] = word;
+            }
+        } else if ((lane & (kLanesPerBlock - 1)) == 0 && active) {
+            const int64_t i = a.mode == MOE_SCALE_ROWS
+                                  ? (int64_t)p * a.srs + b
+                                  : ((int64_t)(p / a.M) * nb + b) * a.M + p % a.M;
+            static_cast<float*>(a.scales)[i] = s;
         }
-    } else if ((lane & 15) == 0 && active) {
-        const int64_t i = a.mode == MOE_SCALE_ROWS
-                              ? (int64_t)p * a.srs + b
-                              : ((int64_t)(p / a.M) * nb + b) * a.M + p % a.M;
-        static_cast<float*>(a.scales)[i] = s;
     }
 }
 
@@ -146,7 +156,7 @@ extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, 
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: unknown scale_format %d", scale_format);
     if (H % kBlock != 0)
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: H=%d must be a multiple of 128", H);
-    if (scale_format == MOE_SCALE_UE8M0 && (!round_scale || H % kChanPerWave != 0))
+    if (scale_format == MOE_SCALE_UE8M0 && (!round_scale || H % (4 * kBlock) != 0))
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: ue8m0 scales need round_scale and H %% 512 == 0");
     if (scale_format != MOE_SCALE_ROWS && rows_per_expert < 1)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: column-major scales need rows_per_expert >= 1");
@@ -155,18 +165,18 @@ extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, 
     if (pos == nullptr && K != 1 && N > 0)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: pos == NULL (identity) requires K == 1");
     const int32_t segs = ceil_div<int32_t>(H, kChanPerWave);
-    const int64_t waves = (int64_t)N * K * segs;
+    const int64_t waves = (int64_t)N * segs;
     if ((int64_t)N * K >= ((int64_t)1 << 31) || waves >= ((int64_t)1 << 31))
-        return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8: N*K*(H/512) must be below 2^31");
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8: N*K and N*ceil(H/1024) must be below 2^31");
     if (N == 0 || H == 0) return ok();
     if (x == nullptr || dst == nullptr || scales == nullptr)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: NULL pointer");
     if (!aligned(x, 16) || x_row_stride % 8 != 0 || x_row_stride < H)
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: x must be 16-byte aligned with a row stride "
                     "that is a multiple of 8 elements and >= H");
-    if (!aligned(dst, 8) || dst_row_stride % 8 != 0 || dst_row_stride < H)
-        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: dst must be 8-byte aligned with a row stride "
-                    "that is a multiple of 8 bytes and >= H");
+    if (!aligned(dst, 16) || dst_row_stride % 16 != 0 || dst_row_stride < H)
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: dst must be 16-byte aligned with a row stride "
+                    "that is a multiple of 16 bytes and >= H");
     if (!aligned(scales, 4) || !aligned(pos, 4))
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: scales and pos must be 4-byte aligned");
 
@@ -185,9 +195,11 @@ extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, 
     a.srs = scale_row_stride;
     a.M = rows_per_expert;
     a.round_scale = round_scale ? 1 : 0;
-    const int64_t blocks =
-        ceil_div<int64_t>(ceil_div<int64_t>(waves, kWavesPerBlock), kXcds) * kXcds;
+    // Small batches (decode) launch one-wave workgroups to spread over more
+    // CUs; large ones four-wave workgroups.
+    const int threads = waves < 4096 ? kWave : 4 * kWave;
+    const int64_t blocks = ceil_div<int64_t>(waves, threads / kWave);
     clear_launch_error();
-    dispatch_fp8_kernel<<<(uint32_t)blocks, kThreads, 0, stream>>>(a);
+    dispatch_fp8_kernel<<<(uint32_t)blocks, threads, 0, stream>>>(a);
     return check_launch("moe_dispatch_fp8");
 }

@@ -225,7 +225,7 @@ int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
  *   MOE_SCALE_UE8M0  int32 word ((p/M)*(H/512) + b/4)*M + p%M, byte b%4 = biased
  *                    exponent of s (needs round_scale and H % 512 == 0)
  * x: bf16 bits, 16-byte aligned, row stride a multiple of 8 elements;
- * dst: 8-byte aligned, row stride a multiple of 8 bytes; scales 4-byte aligned.
+ * dst: 16-byte aligned, row stride a multiple of 16 bytes; scales 4-byte aligned.
  * H % 128 == 0. Rows no pair maps to are left untouched. Errors:
  * MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT, MOE_ERR_HIP.
  */

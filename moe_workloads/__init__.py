@@ -45,6 +45,7 @@ __all__ = [
     "make",
     "make_random",
     "make_y",
+    "make_x",
     "bf16_bits_from_f32",
     "uniform_distinct_ids",
 ]
@@ -118,6 +119,14 @@ def make_y(rows: int, hc: int, seed: int, chunk_rows: int = 8192) -> np.ndarray:
         r1 = min(rows, r0 + chunk_rows)
         out[r0:r1] = bf16_bits_from_f32(rng.standard_normal((r1 - r0, hc), dtype=np.float32))
     return out
+
+
+def make_x(rows: int, h: int, seed: int) -> np.ndarray:
+    """bf16 token activations [rows, h] as uint16 bits: N(0,1) entries times
+    a per-token magnitude exp(N(0,1)), so per-block scales vary by token."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp(rng.standard_normal((rows, 1))).astype(np.float32)
+    return bf16_bits_from_f32(rng.standard_normal((rows, h), dtype=np.float32) * mag)
 
 
 def uniform_distinct_ids(rng: np.random.Generator, n: int, k: int, e: int) -> np.ndarray:

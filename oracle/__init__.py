@@ -84,6 +84,15 @@ def lib():
     return _lib
 
 
+def set_threads(n: int) -> int:
+    """OpenMP threads for the oracle's parallel loops (per-token work, whose
+    results do not depend on the thread count); returns the previous count."""
+    L = lib()
+    prev = int(L.omp_get_max_threads())
+    L.omp_set_num_threads(int(n))
+    return prev
+
+
 class OracleError(RuntimeError):
     def __init__(self, code: int, what: str):
         super().__init__(f"{what}: oracle returned {code}")
@@ -235,20 +244,28 @@ SCALE_ROWS, SCALE_COLS, SCALE_UE8M0 = 0, 1, 2
 
 
 def dispatch_fp8(x: np.ndarray, pos: np.ndarray, rows: int, scale_mode: int = SCALE_ROWS,
-                 M: int = 0, round_scale: bool = False, fill: int = 0):
+                 M: int = 0, round_scale: bool = False, fill: int = 0,
+                 codes: np.ndarray = None, scales: np.ndarray = None):
     """Quantising dispatch of bf16 x [N, H] (bits). Returns (codes [rows, H]
     uint8, scales): fp32 [rows, H/128] (SCALE_ROWS), fp32 [rows/M, H/128, M]
-    (SCALE_COLS) or int32 [rows/M, H/512, M] (SCALE_UE8M0)."""
+    (SCALE_COLS) or int32 [rows/M, H/512, M] (SCALE_UE8M0). Given `codes`
+    and `scales` (contiguous, of those shapes), writes into them instead;
+    rows no pair lands on are left as they are."""
     assert x.dtype == np.uint16
     N, H = x.shape
     K = pos.shape[1]
-    codes = np.full((rows, H), fill, np.uint8)
     if scale_mode == SCALE_ROWS:
-        scales = np.zeros((rows, H // 128), np.float32)
+        sshape, sdtype = (rows, H // 128), np.float32
     elif scale_mode == SCALE_COLS:
-        scales = np.zeros((rows // M, H // 128, M), np.float32)
+        sshape, sdtype = (rows // M, H // 128, M), np.float32
     else:
-        scales = np.zeros((rows // M, H // 512, M), np.int32)
+        sshape, sdtype = (rows // M, H // 512, M), np.int32
+    if codes is None:
+        codes = np.full((rows, H), fill, np.uint8)
+    if scales is None:
+        scales = np.zeros(sshape, sdtype)
+    assert codes.shape == (rows, H) and codes.dtype == np.uint8 and codes.flags.c_contiguous
+    assert scales.shape == sshape and scales.dtype == sdtype and scales.flags.c_contiguous
     pos_c = np.ascontiguousarray(pos, dtype=np.int32)
     xb, xs = _row_view(x) if N else (0, H)
     rc = lib().oracle_dispatch_fp8(xb, xs, N, K, H, _ptr(pos_c), _ptr(codes), H, _ptr(scales),

@@ -207,7 +207,8 @@ def test_layout_padded_and_fp8_validation(lib):
     assert F(P, 256, 4, 2, 256, P, P, 256, P, 0, 1, 0, 0, 0) == lib.MOE_ERR_ARG           # row stride
     assert F(P, 256, 4, 2, 256, P, P, 256, P, 7, 2, 0, 0, 0) == lib.MOE_ERR_ARG           # format
     assert F(P + 8, 256, 4, 2, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN     # x alignment
-    assert F(P, 256, 4, 2, 256, P, P + 4, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN     # dst alignment
+    assert F(P, 256, 4, 2, 256, P, P + 8, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN     # dst alignment
+    assert F(P, 256, 4, 2, 256, P, P, 264, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN         # dst stride
     assert F(P, 256, 4, 2, 256, 0, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ARG           # identity, K=2
     assert F(P, 256, 4, 33, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_LIMIT
     assert F(P, 256, 0, 2, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_OK                # N = 0

@@ -153,3 +153,40 @@ def test_fp8_codes_decode_to_torch_float8(mg):
     xf = dev(x.view(np.int16)).view(torch.bfloat16).float()
     ok = (deq - xf).abs() <= xf.abs() * 2.0 ** -4 + scales.repeat_interleave(128, dim=1) * 2.0 ** -10
     assert bool(ok.all())
+
+
+@pytest.mark.parametrize("H,fmt", [(512, 2), (1536, 2), (640, 1), (1152, 0)])
+def test_fp8_partial_waves_all_formats(mg, H, fmt):
+    """One wave covers 1024 channels: H below or between multiples of 1024
+    leaves the upper lanes (or the upper UE8M0 word) of the last wave idle."""
+    rng = np.random.default_rng(H + fmt)
+    N, K, E, M = 300, 4, 16, 128
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[::7, 1] = -1                                  # masked pairs
+    x = _x(rng, N, H)
+    pos_d, pos = padded(mg, ids, E, M)               # some pairs dropped (M < counts)
+    say(f"fp8 partial waves H={H} format={fmt}")
+    rows = E * M
+    dst = torch.full((rows, H), 0x5A, dtype=torch.uint8, device="cuda")
+    shape = {0: (rows, H // 128), 1: (E, H // 128, M), 2: (E, H // 512, M)}[fmt]
+    scales = torch.zeros(shape, dtype=torch.int32 if fmt == 2 else torch.float32, device="cuda")
+    mg.moe_dispatch_fp8(dev(x.view(np.int16)).view(torch.bfloat16), pos_d, K, dst, scales, fmt, M,
+                        fmt == 2)
+    torch.cuda.synchronize()
+    codes, ref_scales = oracle.dispatch_fp8(x, pos, rows, fmt, M, fmt == 2, fill=0x5A)
+    assert np.array_equal(dst.cpu().numpy(), codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+
+
+def test_padded_layout_empty_batch(mg):
+    E, M = 64, 40
+    counts = torch.full((E,), 9, dtype=torch.int32, device="cuda")
+    row_pair = torch.zeros(E * M, dtype=torch.int32, device="cuda")
+    status = torch.full((2,), 9, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(mg.moe_layout_workspace_bytes(0, 8, E), 256), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    pos = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    mg.moe_get_layout_padded(ids, E, M, counts, pos, row_pair, ws, status)
+    torch.cuda.synchronize()
+    assert (counts.cpu() == 0).all() and (row_pair.cpu() == -1).all()
+    assert status.cpu().tolist() == [0, 0]
