@@ -449,7 +449,7 @@ def main():
     ap.add_argument("--traffic-command", default="",
                     help="the profiled command, recorded next to the figures")
     args = ap.parse_args()
-    workload_key = args.config + ("-lowlatency" if args.lowlatency else "")
+    workload_key = args.config + (f"-lowlatency-{args.scale_format}" if args.lowlatency else "")
     if args.traffic_from:
         summarize_traffic(*args.traffic_from, workload_key, args.traffic_command)
         return

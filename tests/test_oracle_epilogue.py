@@ -2,7 +2,7 @@
 
 Definition: biases added in fp32 after the top-k sum (DeepEP deep_ep.cpp,
 Buffer::intranode_combine takes bias_0 / bias_1 [num_recv_tokens, hidden];
-their position is this build's reading); with a residual, the fp32 sum plus
+their position is a reading of ours); with a residual, the fp32 sum plus
 residual is stored (bf16) as the new residual and RMS-normalised with gamma
 (vLLM branch compare ds-exp-2...ds-exp-ag, moe_rs_fused.cu, fused
 POLL + REDUCE + RESIDUAL + RMSNORM phase).

@@ -2,7 +2,7 @@
 
 The layout's plain definition (DeepEP deep_ep.cpp, Buffer::get_dispatch_layout
 counts; an expert-contiguous receive buffer as in Buffer::intranode_dispatch;
-ascending (token, k) within an expert, this build's reading) is a stable
+ascending (token, k) within an expert, a reading the pages leave open) is a stable
 counting sort. The oracle is checked against numpy's bincount / cumsum /
 stable argsort, a quadratic brute force, hand-worked fixtures and invariants.
 """

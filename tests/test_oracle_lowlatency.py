@@ -1,7 +1,7 @@
 """Pins of the oracle's low-latency dispatch forms (CPU only): the padded
 per-expert layout and the FP8 (e4m3) cast on dispatch with per-128-channel
 scales (DeepEP repository dump, deep_ep.cpp, Buffer::low_latency_dispatch;
-config.hpp, LowLatencyLayout). The cast's arithmetic is this build's reading
+config.hpp, LowLatencyLayout). The cast's arithmetic is a reading of ours
 (the kernel is not on the pages): amax/448 per block, at least 2^-126,
 optionally rounded up to a power of two; e4m3 round-to-nearest-even,
 saturating.
