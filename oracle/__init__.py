@@ -74,6 +74,11 @@ def lib():
         L.oracle_fp8_block_scale.restype = ctypes.c_float
         L.oracle_dispatch_fp8.argtypes = [P, i64, i32, i32, i32, P, P, i64, P, i32, i64, i32, i32]
         L.oracle_dispatch_fp8.restype = ctypes.c_int
+        L.oracle_dispatch_backward.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64]
+        L.oracle_dispatch_backward.restype = ctypes.c_int
+        L.oracle_combine_backward.argtypes = [P, i64, P, i64, P, i64, P, i32, i32, i32, P, i64, P,
+                                              i64]
+        L.oracle_combine_backward.restype = ctypes.c_int
         L.oracle_required_cap.argtypes = [i32, i32, i32, i32]
         L.oracle_required_cap.restype = i64
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -172,6 +177,59 @@ def combine(y: np.ndarray, w: np.ndarray, pos: np.ndarray) -> np.ndarray:
     if rc != OK:
         raise OracleError(rc, "combine")
     return out
+
+
+def dispatch_backward(grad_recv: np.ndarray, pos: np.ndarray,
+                      grad_recv_w: Optional[np.ndarray] = None):
+    """Backward of the dispatch: grad_x [N, H] (bf16 bits) = bf16(sum over
+    valid k, ascending, of grad_recv[pos[t,k]]) and, given grad_recv_w
+    [rows, K] fp32, grad_w [N, K] = the same sum of grad_recv_w rows (else
+    None)."""
+    assert grad_recv.dtype == np.uint16
+    N, K = pos.shape
+    H = grad_recv.shape[1]
+    grad_x = np.empty((N, H), np.uint16)
+    pos_c = np.ascontiguousarray(pos, dtype=np.int32)
+    gb, gs = _row_view(grad_recv) if grad_recv.shape[0] else (0, H)
+    grad_w = None
+    wb, ws = 0, K
+    if grad_recv_w is not None:
+        assert grad_recv_w.dtype == np.float32 and grad_recv_w.shape[1] >= K
+        wb, ws = _row_view(grad_recv_w) if grad_recv_w.shape[0] else (0, K)
+        grad_w = np.empty((N, K), np.float32)
+    rc = lib().oracle_dispatch_backward(gb, gs, wb if grad_recv_w is not None else None, ws,
+                                        _ptr(pos_c), N, K, H, _ptr(grad_x), H,
+                                        _ptr(grad_w) if grad_w is not None else None, K)
+    if rc != OK:
+        raise OracleError(rc, "dispatch_backward")
+    return grad_x, grad_w
+
+
+def combine_backward(grad_out: np.ndarray, w: np.ndarray, pos: np.ndarray, rows: int,
+                     y: Optional[np.ndarray] = None, fill: int = 0):
+    """Backward of the combine: grad_y [rows, Hc] (bf16 bits; rows no pair
+    lands on keep `fill`) with grad_y[pos[t,k]] = bf16(w[t,k] * grad_out[t])
+    and, given y, grad_w [N, K] fp32 = <grad_out[t], y[pos[t,k]]> formed in
+    double (0 for masked pairs; else None)."""
+    assert grad_out.dtype == np.uint16 and w.dtype == np.float32
+    N, K = pos.shape
+    Hc = grad_out.shape[1]
+    grad_y = np.full((rows, Hc), fill, np.uint16)
+    pos_c = np.ascontiguousarray(pos, dtype=np.int32)
+    gb, gs = _row_view(grad_out) if N else (0, Hc)
+    wb, ws = _row_view(w) if N else (0, K)
+    grad_w = None
+    yb, ys = None, Hc
+    if y is not None:
+        assert y.dtype == np.uint16 and y.shape[1] == Hc
+        yb, ys = _row_view(y) if y.shape[0] else (0, Hc)
+        grad_w = np.empty((N, K), np.float32)
+    rc = lib().oracle_combine_backward(gb, gs, wb, ws, yb, ys, _ptr(pos_c), N, K, Hc,
+                                       _ptr(grad_y) if rows else None, Hc,
+                                       _ptr(grad_w) if grad_w is not None else None, K)
+    if rc != OK:
+        raise OracleError(rc, "combine_backward")
+    return grad_y, grad_w
 
 
 def combine_acc(y: np.ndarray, w: np.ndarray, pos: np.ndarray) -> np.ndarray:

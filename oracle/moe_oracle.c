@@ -425,3 +425,86 @@ int oracle_dispatch_fp8(const uint16_t* x, int64_t x_row_stride, int32_t N, int3
     }
     return ORC_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward (DeepEP repository dump, README, "Example use in model training":
+ * the backward of a dispatch is a combine of the received rows' gradients,
+ * with the gradients of the received top-k weights combined alongside; the
+ * backward of a combine is a dispatch of the output gradient).
+ * With the forward  recv[pos[t,k]] = x[t]  and
+ * out[t] = sum_k w[t,k] * y[pos[t,k]], the chain rule gives:
+ *   dispatch backward: grad_x[t,h] = sum over valid k of grad_recv[pos[t,k],h]
+ *                      grad_w_in[t,j] = sum over valid k of grad_recv_w[pos[t,k],j]
+ *   combine backward:  grad_y[pos[t,k],h] = w[t,k] * grad_out[t,h]
+ *                      grad_w[t,k] = sum_h grad_out[t,h] * y[pos[t,k],h]
+ * Precision (readings): the sums over k are fp32 additions with k ascending
+ * starting at +0 (the combine's order), rounded once to bf16; grad_y is one
+ * fp32 product rounded to bf16; the dot products grad_w are formed in double
+ * and rounded once to fp32 (their order is not fixed anywhere). Masked pairs
+ * (pos < 0) contribute nothing and get grad_w = 0; rows of grad_y that no
+ * pair lands on are not written.
+ * ------------------------------------------------------------------------- */
+int oracle_dispatch_backward(const uint16_t* grad_recv, int64_t grad_recv_row_stride,
+                             const float* grad_recv_w, int64_t grad_recv_w_row_stride,
+                             const int32_t* pos, int32_t N, int32_t K, int32_t H,
+                             uint16_t* grad_x, int64_t grad_x_row_stride, float* grad_w,
+                             int64_t grad_w_row_stride) {
+    if (N < 0 || K < 1 || K > ORC_MAX_K || H < 0) return ORC_ERR_ARG;
+    if ((grad_recv_w == NULL) != (grad_w == NULL)) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t p = pos[(int64_t)t * K + k];
+                if (p < 0) continue;
+                acc = acc + oracle_bf16_to_f32(grad_recv[(int64_t)p * grad_recv_row_stride + h]);
+            }
+            grad_x[(int64_t)t * grad_x_row_stride + h] = oracle_f32_to_bf16(acc);
+        }
+        if (grad_w) {
+            for (int32_t j = 0; j < K; ++j) {
+                float acc = 0.0f;
+                for (int32_t k = 0; k < K; ++k) {
+                    int32_t p = pos[(int64_t)t * K + k];
+                    if (p < 0) continue;
+                    acc = acc + grad_recv_w[(int64_t)p * grad_recv_w_row_stride + j];
+                }
+                grad_w[(int64_t)t * grad_w_row_stride + j] = acc;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+int oracle_combine_backward(const uint16_t* grad_out, int64_t grad_out_row_stride, const float* w,
+                            int64_t w_row_stride, const uint16_t* y, int64_t y_row_stride,
+                            const int32_t* pos, int32_t N, int32_t K, int32_t Hc,
+                            uint16_t* grad_y, int64_t grad_y_row_stride, float* grad_w,
+                            int64_t grad_w_row_stride) {
+    if (N < 0 || K < 1 || K > ORC_MAX_K || Hc < 0) return ORC_ERR_ARG;
+    if (grad_w != NULL && y == NULL) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; ++t) {
+        const uint16_t* g = grad_out + (int64_t)t * grad_out_row_stride;
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t p = pos[(int64_t)t * K + k];
+            if (p < 0) {
+                if (grad_w) grad_w[(int64_t)t * grad_w_row_stride + k] = 0.0f;
+                continue;
+            }
+            float wk = w[(int64_t)t * w_row_stride + k];
+            for (int32_t h = 0; h < Hc; ++h)
+                grad_y[(int64_t)p * grad_y_row_stride + h] =
+                    oracle_f32_to_bf16(wk * oracle_bf16_to_f32(g[h]));
+            if (grad_w) {
+                double dot = 0.0;
+                const uint16_t* yr = y + (int64_t)p * y_row_stride;
+                for (int32_t h = 0; h < Hc; ++h)
+                    dot += (double)oracle_bf16_to_f32(g[h]) * (double)oracle_bf16_to_f32(yr[h]);
+                grad_w[(int64_t)t * grad_w_row_stride + k] = (float)dot;
+            }
+        }
+    }
+    return ORC_OK;
+}
