@@ -83,6 +83,11 @@ def _load():
     L.moe_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32,
                                        ctypes.POINTER(moe_epilogue), P, i64, P]
     L.moe_combine_epilogue.restype = ctypes.c_int
+    L.moe_dispatch_backward.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64, P]
+    L.moe_dispatch_backward.restype = ctypes.c_int
+    L.moe_combine_backward.argtypes = [P, i64, P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64,
+                                       P]
+    L.moe_combine_backward.restype = ctypes.c_int
     return L
 
 
@@ -266,6 +271,68 @@ def moe_combine(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor, out: 
     op, os_ = _rows(out, "out") if N else (0, Hc)
     _check(_lib.moe_combine(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc, op, os_,
                             _stream(stream)))
+
+
+def moe_dispatch_backward(grad_recv: torch.Tensor, pos: torch.Tensor, grad_x: torch.Tensor,
+                          grad_recv_w: Optional[torch.Tensor] = None,
+                          grad_w: Optional[torch.Tensor] = None, stream=None) -> None:
+    """grad_x [N, H] bf16 = sum over valid k of grad_recv[pos[t, k]] (fp32
+    accumulate); with grad_recv_w [rows, K] fp32, also grad_w [N, K] fp32 =
+    the same sum of grad_recv_w rows."""
+    if grad_recv.dtype != torch.bfloat16 or grad_x.dtype != torch.bfloat16:
+        raise TypeError("grad_recv and grad_x must be bfloat16")
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 2:
+        raise TypeError("pos must be a contiguous int32 [N, K] tensor")
+    if (grad_recv_w is None) != (grad_w is None):
+        raise ValueError("grad_recv_w and grad_w go together")
+    N, K = pos.shape
+    H = grad_x.shape[1]
+    if grad_recv.shape[1] != H or grad_x.shape[0] != N:
+        raise ValueError("shape mismatch between grad_recv, pos and grad_x")
+    gp, gs = _rows(grad_recv, "grad_recv") if grad_recv.shape[0] else (_dev(grad_recv, "grad_recv"), H)
+    xp, xs = _rows(grad_x, "grad_x") if N else (0, H)
+    wp, ws, op, os_ = 0, K, 0, K
+    if grad_w is not None:
+        if grad_recv_w.dtype != torch.float32 or grad_w.dtype != torch.float32:
+            raise TypeError("weight gradients must be float32")
+        if grad_recv_w.shape[1] < K or tuple(grad_w.shape[:1]) != (N,) or grad_w.shape[1] < K:
+            raise ValueError("grad_recv_w must be [rows, >= K] and grad_w [N, >= K]")
+        wp, ws = _rows(grad_recv_w, "grad_recv_w") if grad_recv_w.shape[0] else (_dev(grad_recv_w, "grad_recv_w"), K)
+        op, os_ = _rows(grad_w, "grad_w") if N else (0, K)
+    _check(_lib.moe_dispatch_backward(gp, gs, wp, ws, _dev(pos, "pos"), N, K, H, xp, xs, op, os_,
+                                      _stream(stream)))
+
+
+def moe_combine_backward(grad_out: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor,
+                         grad_y: torch.Tensor, y: Optional[torch.Tensor] = None,
+                         grad_w: Optional[torch.Tensor] = None, stream=None) -> None:
+    """grad_y[pos[t, k]] = bf16(weights[t, k] * grad_out[t]); with y and
+    grad_w [N, K] fp32, also grad_w[t, k] = <grad_out[t], y[pos[t, k]]>."""
+    if grad_out.dtype != torch.bfloat16 or grad_y.dtype != torch.bfloat16:
+        raise TypeError("grad_out and grad_y must be bfloat16")
+    if weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 2:
+        raise TypeError("pos must be a contiguous int32 [N, K] tensor")
+    if grad_w is not None and y is None:
+        raise ValueError("weight gradients need y")
+    N, K = pos.shape
+    Hc = grad_out.shape[1]
+    if grad_out.shape[0] != N or grad_y.shape[1] != Hc or tuple(weights.shape[:1]) != (N,):
+        raise ValueError("shape mismatch between grad_out, weights, pos and grad_y")
+    gp, gs = _rows(grad_out, "grad_out") if N else (0, Hc)
+    wp, ws = _rows(weights, "weights") if N else (0, K)
+    yp, ys = 0, Hc
+    if grad_w is not None:
+        if y.dtype != torch.bfloat16 or y.shape[1] != Hc:
+            raise TypeError("y must be bfloat16 [rows, Hc]")
+        if grad_w.dtype != torch.float32 or grad_w.shape[0] != N or grad_w.shape[1] < K:
+            raise TypeError("grad_w must be float32 [N, >= K]")
+        yp, ys = _rows(y, "y") if y.shape[0] else (_dev(y, "y"), Hc)
+    dp, ds = _rows(grad_y, "grad_y") if grad_y.shape[0] else (_dev(grad_y, "grad_y"), Hc)
+    op, os_ = (_rows(grad_w, "grad_w") if N else (0, K)) if grad_w is not None else (0, K)
+    _check(_lib.moe_combine_backward(gp, gs, wp, ws, yp, ys, _dev(pos, "pos"), N, K, Hc, dp, ds,
+                                     op, os_, _stream(stream)))
 
 
 def moe_combine_epilogue(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor,

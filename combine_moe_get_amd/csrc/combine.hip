@@ -73,22 +73,42 @@ __device__ __forceinline__ void store_words(uint16_t* p, const Words<W>& r) {
     }
 }
 
-template <int W>
+// Sums of K-wide fp32 rows over a token's pairs (the dispatch backward's
+// weight gradients): gin[pos[t,k], j] summed over valid k ascending into
+// gout[t, j], one lane per j.
+struct RowSums {
+    const float* gin;
+    int64_t gins;
+    float* gout;
+    int64_t gouts;
+};
+
+// UNIT: every weight is 1 (the dispatch backward): acc + y, which is what
+// fmaf(1, y, acc) computes, without loading weights.
+template <int W, bool UNIT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint16_t* __restrict__ y, int64_t ys, const float* __restrict__ w, int64_t wst,
     const int32_t* __restrict__ pos, int32_t N, int32_t K, int32_t V, int32_t segs,
-    uint16_t* __restrict__ out, int64_t os) {
+    uint16_t* __restrict__ out, int64_t os, const RowSums rs) {
     constexpr int E = 2 * W;   // bf16 elements per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int32_t t = __builtin_amdgcn_readfirstlane((int32_t)(gw / segs));
     if (t >= N) return;
     const int32_t seg = (int32_t)(gw - (int64_t)t * segs);
+    const int32_t* prow = pos + (int64_t)t * K;
+    if (UNIT && rs.gout != nullptr && seg == 0 && lane < K) {
+        float a = 0.0f;
+        for (int32_t k = 0; k < K; ++k) {
+            const int32_t p = prow[k];
+            if (p >= 0) a = a + rs.gin[(int64_t)p * rs.gins + lane];
+        }
+        rs.gout[(int64_t)t * rs.gouts + lane] = a;
+    }
     const int32_t v = seg * kWave + lane;
     if (v >= V) return;
 
-    const int32_t* prow = pos + (int64_t)t * K;
-    const float* wrow = w + (int64_t)t * wst;
+    const float* wrow = UNIT ? nullptr : w + (int64_t)t * wst;
     const int64_t col = (int64_t)v * E;
 
     float acc[E];
@@ -103,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         for (int j = 0; j < kBatch; ++j) {
             const int k = k0 + j;
             p[j] = k < K ? prow[k] : -1;
-            wk[j] = k < K ? wrow[k] : 0.0f;
+            wk[j] = UNIT ? 1.0f : (k < K ? wrow[k] : 0.0f);
             if (p[j] >= 0) val[j] = load_words<W>(y + (int64_t)p[j] * ys + col);
         }
 #pragma unroll
@@ -111,8 +131,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
             if (p[j] < 0) continue;
 #pragma unroll
             for (int q = 0; q < W; ++q) {
-                acc[2 * q] = __builtin_fmaf(wk[j], lo_bf16(val[j].w[q]), acc[2 * q]);
-                acc[2 * q + 1] = __builtin_fmaf(wk[j], hi_bf16(val[j].w[q]), acc[2 * q + 1]);
+                if (UNIT) {
+                    acc[2 * q] = acc[2 * q] + lo_bf16(val[j].w[q]);
+                    acc[2 * q + 1] = acc[2 * q + 1] + hi_bf16(val[j].w[q]);
+                } else {
+                    acc[2 * q] = __builtin_fmaf(wk[j], lo_bf16(val[j].w[q]), acc[2 * q]);
+                    acc[2 * q + 1] = __builtin_fmaf(wk[j], hi_bf16(val[j].w[q]), acc[2 * q + 1]);
+                }
             }
         }
     }
@@ -266,6 +291,120 @@ __global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const Epi
     }
 }
 
+// ---------------------------------------------------------------------------
+// Combine backward: the dual of the combine is a dispatch of the output
+// gradient, scaled by each pair's weight, plus the weights' gradients
+//   grad_y[pos[t,k], h] = bf16_rne(w[t,k] * grad_out[t,h])       (fp32 product)
+//   grad_w[t,k]         = sum_h grad_out[t,h] * y[pos[t,k], h]   (fp32)
+// (DeepEP repository dump, README, "Example use in model training": the
+// backward of the combine is a dispatch). One workgroup per token: its
+// gradient row stays in registers while the K expert rows stream through;
+// each lane keeps one fp32 FMA chain per pair over its channels, the 64
+// lanes of a wave are summed by a fixed butterfly and the waves in index
+// order, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+
+struct BackwardArgs {
+    const uint16_t* g;   // grad_out [N, Hc]
+    int64_t gs;
+    const float* w;
+    int64_t wst;
+    const uint16_t* y;   // NULL: no weight gradients
+    int64_t ys;
+    const int32_t* pos;
+    int32_t N, K, V;     // V = Hc / 8
+    uint16_t* gy;
+    int64_t gys;
+    float* gw;
+    int64_t gws;
+};
+
+template <int VPT>
+__global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const BackwardArgs a) {
+    __shared__ float part[kEpiWaves][kBatch];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int32_t t = blockIdx.x;
+    const int32_t* prow = a.pos + (int64_t)t * a.K;
+    const float* wrow = a.w + (int64_t)t * a.wst;
+    const bool want_w = a.gw != nullptr;
+
+    // the token's gradient row, kept as packed bf16 (half the registers of
+    // fp32; unpacking is a shift or a mask)
+    Words<4> g[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int32_t v = threadIdx.x + j * kEpiThreads;
+        if (v < a.V) {
+            g[j] = load_words<4>(a.g + (int64_t)t * a.gs + (int64_t)v * 8);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) g[j].w[q] = 0u;
+        }
+    }
+
+    for (int k0 = 0; k0 < a.K; k0 += kBatch) {
+        int32_t p[kBatch];
+        float wk[kBatch], d[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int k = k0 + i;
+            p[i] = k < a.K ? prow[k] : -1;
+            wk[i] = k < a.K ? wrow[k] : 0.0f;
+            d[i] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int32_t v = threadIdx.x + j * kEpiThreads;
+            if (v >= a.V) continue;
+            const int64_t col = (int64_t)v * 8;
+            Words<4> yv[kBatch];
+            if (want_w) {
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (p[i] >= 0) yv[i] = load_words<4>(a.y + (int64_t)p[i] * a.ys + col);
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (p[i] < 0) continue;
+                float o[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    o[2 * q] = wk[i] * lo_bf16(g[j].w[q]);
+                    o[2 * q + 1] = wk[i] * hi_bf16(g[j].w[q]);
+                }
+                store_bf16x8(a.gy + (int64_t)p[i] * a.gys + col, o);
+                if (want_w) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        d[i] = __builtin_fmaf(lo_bf16(g[j].w[q]), lo_bf16(yv[i].w[q]), d[i]);
+                        d[i] = __builtin_fmaf(hi_bf16(g[j].w[q]), hi_bf16(yv[i].w[q]), d[i]);
+                    }
+                }
+            }
+        }
+        if (!want_w) continue;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) d[i] += __shfl_xor(d[i], off, kWave);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) part[wave][i] = d[i];
+        }
+        __syncthreads();
+        if (threadIdx.x < kBatch && k0 + (int)threadIdx.x < a.K) {
+            const int i = threadIdx.x;
+            float sum = 0.0f;
+#pragma unroll
+            for (int wv = 0; wv < kEpiWaves; ++wv) sum += part[wv][i];
+            a.gw[(int64_t)t * a.gws + k0 + i] = prow[k0 + i] >= 0 ? sum : 0.0f;
+        }
+        __syncthreads();   // part is rewritten by the next batch
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -300,14 +439,61 @@ extern "C" int moe_combine(const void* y, int64_t y_row_stride, const float* w,
                     (long long)blocks);
     const auto* yy = static_cast<const uint16_t*>(y);
     auto* oo = static_cast<uint16_t*>(out);
+    const RowSums none = {nullptr, 0, nullptr, 0};
     clear_launch_error();
     if (vec16)
-        combine_kernel<4><<<(uint32_t)blocks, kThreads, 0, stream>>>(
-            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride);
+        combine_kernel<4, false><<<(uint32_t)blocks, kThreads, 0, stream>>>(
+            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none);
     else
-        combine_kernel<1><<<(uint32_t)blocks, kThreads, 0, stream>>>(
-            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride);
+        combine_kernel<1, false><<<(uint32_t)blocks, kThreads, 0, stream>>>(
+            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none);
     return check_launch("moe_combine");
+}
+
+extern "C" int moe_dispatch_backward(const void* grad_recv, int64_t grad_recv_row_stride,
+                                     const float* grad_recv_w, int64_t grad_recv_w_row_stride,
+                                     const int32_t* pos, int32_t N, int32_t K, int32_t H,
+                                     void* grad_x, int64_t grad_x_row_stride, float* grad_w,
+                                     int64_t grad_w_row_stride, hipStream_t stream) {
+    if (N < 0 || K < 1 || H < 0)
+        return fail(MOE_ERR_ARG, "moe_dispatch_backward: need N >= 0, K >= 1, H >= 0");
+    if (K > MOE_MAX_TOPK)
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_backward: K=%d > %d", K, MOE_MAX_TOPK);
+    if ((int64_t)N * K >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_backward: N*K must be below 2^31");
+    if ((grad_recv_w == nullptr) != (grad_w == nullptr))
+        return fail(MOE_ERR_ARG, "moe_dispatch_backward: grad_recv_w and grad_w go together");
+    if (N == 0 || (H == 0 && grad_w == nullptr)) return ok();
+    if (pos == nullptr || (H > 0 && (grad_recv == nullptr || grad_x == nullptr)))
+        return fail(MOE_ERR_ARG, "moe_dispatch_backward: NULL pointer");
+    if (grad_w != nullptr && (grad_recv_w_row_stride < K || grad_w_row_stride < K))
+        return fail(MOE_ERR_ARG, "moe_dispatch_backward: weight-gradient row strides must be >= K");
+    if (H > 0 && (grad_recv_row_stride < H || grad_x_row_stride < H))
+        return fail(MOE_ERR_ARG, "moe_dispatch_backward: row strides must be >= H");
+    if ((H & 1) || (H > 0 && (!aligned(grad_recv, 4) || !aligned(grad_x, 4))) ||
+        (grad_recv_row_stride & 1) || (grad_x_row_stride & 1) || !aligned(pos, 4) ||
+        !aligned(grad_recv_w, 4) || !aligned(grad_w, 4))
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_backward: H and the bf16 strides must be even; "
+                    "all pointers 4-byte aligned");
+    const bool vec16 = (H % 8 == 0) && aligned(grad_recv, 16) && aligned(grad_x, 16) &&
+                       (grad_recv_row_stride % 8 == 0) && (grad_x_row_stride % 8 == 0);
+    const int32_t V = H / (vec16 ? 8 : 2);
+    const int32_t segs = V > 0 ? ceil_div<int32_t>(V, kWave) : 1;   // H = 0: weights only
+    const int64_t blocks = ceil_div<int64_t>((int64_t)N * segs, kWavesPerBlock);
+    if (blocks >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_backward: launch of %lld workgroups too large",
+                    (long long)blocks);
+    const auto* gr = static_cast<const uint16_t*>(grad_recv);
+    auto* gx = static_cast<uint16_t*>(grad_x);
+    const RowSums rs = {grad_recv_w, grad_recv_w_row_stride, grad_w, grad_w_row_stride};
+    clear_launch_error();
+    if (vec16)
+        combine_kernel<4, true><<<(uint32_t)blocks, kThreads, 0, stream>>>(
+            gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride, rs);
+    else
+        combine_kernel<1, true><<<(uint32_t)blocks, kThreads, 0, stream>>>(
+            gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride, rs);
+    return check_launch("moe_dispatch_backward");
 }
 
 
@@ -387,4 +573,70 @@ extern "C" int moe_combine_epilogue(const void* y, int64_t y_row_stride, const f
     else
         combine_epilogue_kernel<8><<<N, kEpiThreads, 0, stream>>>(a);
     return check_launch("moe_combine_epilogue");
+}
+
+extern "C" int moe_combine_backward(const void* grad_out, int64_t grad_out_row_stride,
+                                    const float* w, int64_t w_row_stride, const void* y,
+                                    int64_t y_row_stride, const int32_t* pos, int32_t N,
+                                    int32_t K, int32_t Hc, void* grad_y, int64_t grad_y_row_stride,
+                                    float* grad_w, int64_t grad_w_row_stride,
+                                    hipStream_t stream) {
+    if (N < 0 || K < 1 || Hc < 0)
+        return fail(MOE_ERR_ARG, "moe_combine_backward: need N >= 0, K >= 1, Hc >= 0");
+    if (K > MOE_MAX_TOPK)
+        return fail(MOE_ERR_LIMIT, "moe_combine_backward: K=%d > %d", K, MOE_MAX_TOPK);
+    if ((int64_t)N * K >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_combine_backward: N*K must be below 2^31");
+    // At most 4 vectors per lane: with 8 (Hc above 32768) the 1024-thread
+    // workgroup's 128-register limit would spill.
+    if (Hc > kEpiThreads * 8 * 4)
+        return fail(MOE_ERR_LIMIT, "moe_combine_backward: Hc=%d > %d", Hc, kEpiThreads * 8 * 4);
+    if (grad_w != nullptr && y == nullptr && Hc > 0)
+        return fail(MOE_ERR_ARG, "moe_combine_backward: weight gradients need y");
+    if (N == 0 || (Hc == 0 && grad_w == nullptr)) return ok();
+    if (w == nullptr || pos == nullptr ||
+        (Hc > 0 && (grad_out == nullptr || grad_y == nullptr || (grad_w && y == nullptr))))
+        return fail(MOE_ERR_ARG, "moe_combine_backward: NULL pointer");
+    if (w_row_stride < K || (grad_w != nullptr && grad_w_row_stride < K))
+        return fail(MOE_ERR_ARG, "moe_combine_backward: w and grad_w row strides must be >= K");
+    if (Hc % 8 != 0 || !aligned(w, 4) || !aligned(pos, 4) || !aligned(grad_w, 4))
+        return fail(MOE_ERR_ALIGN, "moe_combine_backward: Hc must be a multiple of 8; w, pos and "
+                    "grad_w 4-byte aligned");
+    struct Row { const void* p; int64_t stride; const char* name; };
+    const Row rows[] = {{grad_out, grad_out_row_stride, "grad_out"},
+                        {grad_y, grad_y_row_stride, "grad_y"},
+                        {grad_w ? y : nullptr, y_row_stride, "y"}};
+    for (const Row& r : rows) {
+        if (r.p == nullptr) continue;
+        if (!aligned(r.p, 16) || r.stride % 8 != 0)
+            return fail(MOE_ERR_ALIGN, "moe_combine_backward: %s must be 16-byte aligned with a "
+                        "row stride that is a multiple of 8 elements", r.name);
+        if (r.stride < Hc)
+            return fail(MOE_ERR_ARG, "moe_combine_backward: %s row stride < Hc", r.name);
+    }
+
+    BackwardArgs a;
+    a.g = static_cast<const uint16_t*>(grad_out);
+    a.gs = grad_out_row_stride;
+    a.w = w;
+    a.wst = w_row_stride;
+    a.y = grad_w ? static_cast<const uint16_t*>(y) : nullptr;
+    a.ys = y_row_stride;
+    a.pos = pos;
+    a.N = N;
+    a.K = K;
+    a.V = Hc / 8;
+    a.gy = static_cast<uint16_t*>(grad_y);
+    a.gys = grad_y_row_stride;
+    a.gw = grad_w;
+    a.gws = grad_w_row_stride;
+    const int vpt = ceil_div<int32_t>(a.V, kEpiThreads);
+    clear_launch_error();
+    if (vpt <= 1)
+        combine_backward_kernel<1><<<N, kEpiThreads, 0, stream>>>(a);
+    else if (vpt <= 2)
+        combine_backward_kernel<2><<<N, kEpiThreads, 0, stream>>>(a);
+    else
+        combine_backward_kernel<4><<<N, kEpiThreads, 0, stream>>>(a);
+    return check_launch("moe_combine_backward");
 }

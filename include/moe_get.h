@@ -284,6 +284,60 @@ int moe_combine_epilogue(const void* y, int64_t y_row_stride, const float* w,
                          int32_t Hc, const moe_epilogue* ep, void* out, int64_t out_row_stride,
                          hipStream_t stream);
 
+/*
+ * Backward of the dispatch (DeepEP repository dump, README, "Example use in
+ * model training": the backward of a dispatch is a combine of the received
+ * rows' gradients, with the received top-k weights' gradients combined
+ * alongside). For the forward recv[pos[t,k]] = x[t]:
+ *     grad_x[t,h] = bf16(fp32 sum over valid k, ascending, from +0, of
+ *                        grad_recv[pos[t,k], h])
+ *     grad_w[t,j] = fp32 sum over valid k, ascending, of grad_recv_w[pos[t,k], j]
+ * (j < K: the weights row every received row carried). Masked pairs
+ * (pos < 0) add nothing; an all-masked token gets +0. grad_recv_w and
+ * grad_w are both NULL (no weight gradients) or both given. Results are
+ * bit-exact with that definition.
+ *
+ * grad_recv [rows, H] and grad_x [N, H] are bf16 with row strides in
+ * elements (>= H, even; 16-byte vectors when both are 16-byte aligned with
+ * strides and H multiples of 8), grad_recv_w [rows, >= K] and grad_w
+ * [N, >= K] fp32 with row strides in floats. pos is moe_get_layout's (or
+ * moe_get_layout_padded's). Limits: 1 <= K <= 32, N*K < 2^31. Errors:
+ * MOE_ERR_ARG (NULL pointer, only one of grad_recv_w / grad_w, stride below
+ * its row), MOE_ERR_ALIGN (odd H or stride, pointer not 4-byte aligned),
+ * MOE_ERR_LIMIT, MOE_ERR_HIP.
+ */
+int moe_dispatch_backward(const void* grad_recv, int64_t grad_recv_row_stride,
+                          const float* grad_recv_w, int64_t grad_recv_w_row_stride,
+                          const int32_t* pos, int32_t N, int32_t K, int32_t H, void* grad_x,
+                          int64_t grad_x_row_stride, float* grad_w, int64_t grad_w_row_stride,
+                          hipStream_t stream);
+
+/*
+ * Backward of the combine (same README passage: the backward of a combine
+ * is a dispatch). For the forward out[t] = sum_k w[t,k] * y[pos[t,k]]:
+ *     grad_y[pos[t,k], h] = bf16(w[t,k] * grad_out[t,h])   (one fp32 product)
+ *     grad_w[t,k] = sum_h grad_out[t,h] * y[pos[t,k], h]   (fp32)
+ * grad_y is bit-exact with that definition; rows of grad_y that no pair
+ * lands on are not written. grad_w is 0 for masked pairs; otherwise each
+ * lane of a 1024-thread workgroup keeps an fp32 FMA chain over its channels
+ * (8 per 16-byte vector), then a fixed butterfly over the 64 lanes of a wave
+ * and the 16 waves in order: within (8*ceil(Hc/8192) + 22) * 2^-24 *
+ * sum_h |grad_out[t,h] * y[pos[t,k],h]| of the exact value, and the same on
+ * every run. grad_w == NULL skips the weight gradients (y may then be NULL
+ * and is not read).
+ *
+ * grad_out [N, Hc], y [rows, Hc] and grad_y [rows, Hc] are bf16, 16-byte
+ * aligned with row strides multiples of 8 elements and >= Hc; Hc a multiple
+ * of 8. w [N, >= K] and grad_w [N, >= K] fp32. Limits: Hc <= 32768,
+ * 1 <= K <= 32. Errors: MOE_ERR_ARG (NULL pointer, grad_w without y, stride
+ * below its row), MOE_ERR_ALIGN, MOE_ERR_LIMIT, MOE_ERR_HIP.
+ */
+int moe_combine_backward(const void* grad_out, int64_t grad_out_row_stride, const float* w,
+                         int64_t w_row_stride, const void* y, int64_t y_row_stride,
+                         const int32_t* pos, int32_t N, int32_t K, int32_t Hc, void* grad_y,
+                         int64_t grad_y_row_stride, float* grad_w, int64_t grad_w_row_stride,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,3 +212,32 @@ def test_layout_padded_and_fp8_validation(lib):
     assert F(P, 256, 4, 2, 256, 0, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ARG           # identity, K=2
     assert F(P, 256, 4, 33, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_LIMIT
     assert F(P, 256, 0, 2, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_OK                # N = 0
+
+
+def test_backward_validation(lib):
+    L = lib._lib
+    P = 0x10000
+    D = L.moe_dispatch_backward
+    # (grad_recv, grs, grad_recv_w, grws, pos, N, K, H, grad_x, gxs, grad_w, gws, stream)
+    assert D(P, 64, P, 8, P, 4, 0, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ARG        # K = 0
+    assert D(P, 64, P, 8, P, 4, 33, 64, P, 64, P, 33, 0) == lib.MOE_ERR_LIMIT    # K > 32
+    assert D(P, 64, P, 8, P, 4, 8, 64, P, 64, 0, 8, 0) == lib.MOE_ERR_ARG        # w grads unpaired
+    assert D(P, 64, 0, 8, P, 4, 8, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ARG
+    assert D(P, 64, P, 4, P, 4, 8, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ARG        # grws < K
+    assert D(P, 32, 0, 8, P, 4, 8, 64, P, 64, 0, 8, 0) == lib.MOE_ERR_ARG        # stride < H
+    assert D(P, 64, 0, 8, P, 4, 8, 63, P, 64, 0, 8, 0) == lib.MOE_ERR_ALIGN      # odd H
+    assert D(P + 2, 64, 0, 8, P, 4, 8, 64, P, 64, 0, 8, 0) == lib.MOE_ERR_ALIGN  # grad_recv
+    assert D(0, 64, 0, 8, P, 4, 8, 64, P, 64, 0, 8, 0) == lib.MOE_ERR_ARG        # NULL
+    assert D(P, 64, 0, 8, P, 0, 8, 64, P, 64, 0, 8, 0) == lib.MOE_OK             # N = 0
+    C = L.moe_combine_backward
+    # (grad_out, gos, w, ws, y, ys, pos, N, K, Hc, grad_y, gys, grad_w, gws, stream)
+    assert C(P, 64, P, 8, P, 64, P, 4, 0, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ARG        # K = 0
+    assert C(P, 64, P, 8, 0, 64, P, 4, 8, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ARG        # grad_w, no y
+    assert C(P, 32776, P, 8, P, 32776, P, 4, 8, 32776, P, 32776, P, 8, 0) == lib.MOE_ERR_LIMIT
+    assert C(P, 64, P, 8, P, 64, P, 4, 8, 60, P, 64, P, 8, 0) == lib.MOE_ERR_ALIGN      # Hc % 8
+    assert C(P + 8, 64, P, 8, P, 64, P, 4, 8, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ALIGN  # grad_out
+    assert C(P, 64, P, 8, P, 60, P, 4, 8, 56, P, 64, P, 8, 0) == lib.MOE_ERR_ALIGN      # y stride
+    assert C(P, 64, P, 4, P, 64, P, 4, 8, 64, P, 64, P, 8, 0) == lib.MOE_ERR_ARG        # ws < K
+    assert C(P, 64, P, 8, P, 64, P, 4, 8, 64, 0, 64, P, 8, 0) == lib.MOE_ERR_ARG        # NULL grad_y
+    assert C(P, 64, P, 8, 0, 64, P, 0, 8, 64, P, 64, 0, 8, 0) == lib.MOE_OK             # N = 0
+    assert C(P, 64, P, 8, 0, 64, P, 4, 8, 0, P, 64, 0, 8, 0) == lib.MOE_OK              # Hc = 0, no w
