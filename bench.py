@@ -69,6 +69,7 @@ KERNEL_SOURCES = {
     "layout_hist": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
     "layout_assign": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
     "dispatch_fp8_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
+    "combine_backward_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
@@ -320,6 +321,52 @@ class LowLatencySet:
         return (L.moe_get_layout_padded, lay), (L.moe_dispatch_fp8, dis), (L.moe_combine, com)
 
 
+def bwd_algorithmic_bytes(N, K, H, Hc, R):
+    """Minimum bytes of the backward step. Combine backward: grad_out, w and
+    pos in, y read for the weight gradients, grad_y and grad_w out. Dispatch
+    backward: grad_recv and grad_recv_w rows in, pos, grad_x and grad_w out."""
+    combine_bwd = N * Hc * 2 + 8 * N * K + R * Hc * 2 + R * Hc * 2 + 4 * N * K
+    dispatch_bwd = R * H * 2 + 4 * N * K + R * K * 4 + N * H * 2 + 4 * N * K
+    return combine_bwd, dispatch_bwd
+
+
+class BackwardSet:
+    """Device buffers of one backward step on the forward's layout: combine
+    backward (grad_out -> grad_y rows and grad_w) and dispatch backward
+    (grad_recv rows -> grad_x, grad_recv_w rows -> grad_w_in)."""
+
+    def __init__(self, torch, mg, wl, host):
+        d = "cuda"
+        N, K, E, Hc = wl.N, wl.K, wl.E, wl.Hc
+        H = host["grad_recv"].shape[1]
+        self.H = H
+        bf = lambda a: torch.from_numpy(a.view(np.int16)).to(d).view(torch.bfloat16)
+        self.ids = torch.from_numpy(np.ascontiguousarray(wl.ids)).to(d)
+        self.w = torch.from_numpy(np.ascontiguousarray(wl.weights)).to(d)
+        lay = mg.layout(self.ids, E)       # the forward's layout, computed once
+        torch.cuda.synchronize()
+        self.pos = lay.pos
+        self.y = bf(host["y"])
+        self.grad_out = bf(host["grad_out"])
+        self.grad_recv = bf(host["grad_recv"])
+        self.grad_recv_w = torch.from_numpy(host["grad_recv_w"]).to(d)
+        R = N * K
+        self.grad_y = torch.empty((R, Hc), dtype=torch.bfloat16, device=d)
+        self.grad_w = torch.empty((N, K), dtype=torch.float32, device=d)
+        self.grad_x = torch.empty((N, H), dtype=torch.bfloat16, device=d)
+        self.grad_w_in = torch.empty((N, K), dtype=torch.float32, device=d)
+
+    def calls(self, mg, wl, stream, epilogue=False):
+        L = mg._lib
+        N, K, Hc, H = wl.N, wl.K, wl.Hc, self.H
+        cb = (self.grad_out.data_ptr(), Hc, self.w.data_ptr(), K, self.y.data_ptr(), Hc,
+              self.pos.data_ptr(), N, K, Hc, self.grad_y.data_ptr(), Hc, self.grad_w.data_ptr(), K,
+              stream)
+        db = (self.grad_recv.data_ptr(), H, self.grad_recv_w.data_ptr(), K, self.pos.data_ptr(),
+              N, K, H, self.grad_x.data_ptr(), H, self.grad_w_in.data_ptr(), K, stream)
+        return (L.moe_combine_backward, cb), (L.moe_dispatch_backward, db)
+
+
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     """A plain device copy (read + write) of `nbytes`: the achievable-HBM
     reference next to the 8 TB/s spec."""
@@ -418,6 +465,21 @@ def cpu_baseline_ll(wl, x, y, M, scale_format, round_scale, total_bytes, budget_
                         "+ combine)")
 
 
+def cpu_baseline_bwd(wl, host, total_bytes, budget_s):
+    """The oracle on the host cores for the backward step (OpenMP over tokens)."""
+    import oracle
+
+    _, _, pos, _, _ = oracle.layout(wl.ids, wl.E)
+    w = np.ascontiguousarray(wl.weights)
+
+    def one():
+        oracle.combine_backward(host["grad_out"], w, pos, wl.N * wl.K, y=host["y"])
+        oracle.dispatch_backward(host["grad_recv"], pos, host["grad_recv_w"])
+
+    return _time_oracle(one, wl, total_bytes, budget_s,
+                        f"full {wl.name} backward steps (combine backward + dispatch backward)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,18 +505,22 @@ def main():
                     help="--lowlatency scales: rows, cols (column-major fp32) or ue8m0")
     ap.add_argument("--round-scale", action="store_true",
                     help="--lowlatency: round scales up to powers of two (implied by ue8m0)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward instead: combine backward (grad_y, grad_w) + "
+                         "dispatch backward (grad_x, weight gradients) on the forward's layout")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench into profiles/traffic.json and exit (no GPU needed)")
     ap.add_argument("--traffic-command", default="",
                     help="the profiled command, recorded next to the figures")
     args = ap.parse_args()
-    workload_key = args.config + (f"-lowlatency-{args.scale_format}" if args.lowlatency else "")
+    workload_key = args.config + (f"-lowlatency-{args.scale_format}" if args.lowlatency else
+                                  "-backward" if args.backward else "")
     if args.traffic_from:
         summarize_traffic(*args.traffic_from, workload_key, args.traffic_command)
         return
-    if args.lowlatency and args.epilogue:
-        raise SystemExit("--lowlatency and --epilogue are separate measurements")
+    if args.lowlatency + args.epilogue + args.backward > 1:
+        raise SystemExit("--lowlatency, --epilogue and --backward are separate measurements")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -480,8 +546,27 @@ def main():
         x = mw.make_x(N, 7168, wl.seed + 104729)
         sets = [LowLatencySet(torch, mg, wl, x, y, M, args.scale_format, round_scale)
                 for _ in range(max(1, args.sets))]
+        names = ("layout", "dispatch", "combine")
+        op_bytes = ll_algorithmic_bytes(N, K, E, M, 7168, Hc, R, args.scale_format)
+        kernels = {"dispatch": "dispatch_fp8_kernel", "combine": "combine_kernel"}
+    elif args.backward:
+        rng = np.random.default_rng(wl.seed + 7)
+        host = {"y": y, "grad_out": mw.make_y(N, Hc, wl.seed + 11),
+                "grad_recv": mw.make_y(R, 7168, wl.seed + 13),
+                "grad_recv_w": rng.standard_normal((R, K)).astype(np.float32)}
+        sets = [BackwardSet(torch, mg, wl, host) for _ in range(max(1, args.sets))]
+        names = ("combine_backward", "dispatch_backward")
+        op_bytes = bwd_algorithmic_bytes(N, K, 7168, Hc, R)
+        # the dispatch backward is the combine kernel in its unit-weight form
+        kernels = {"combine_backward": "combine_backward_kernel",
+                   "dispatch_backward": "combine_kernel"}
     else:
         sets = [BufferSet(torch, mg, wl, y) for _ in range(max(1, args.sets))]
+        names = ("layout", "dispatch", "combine")
+        op_bytes = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
+        kernels = {"dispatch": "dispatch_kernel",
+                   "combine": "combine_epilogue_kernel" if args.epilogue else "combine_kernel"}
+    nops = len(names)
     stream = torch.cuda.current_stream()
     calls = [s.calls(mg, wl, stream.cuda_stream, args.epilogue) for s in sets]
 
@@ -502,8 +587,8 @@ def main():
         """K steps between two synchronizations; with op_events, a
         timing-only event is also recorded before and after every op.
         Returns the mean step time and, with op_events, the per-step op
-        times [K, 3]."""
-        ev = [[hev.create() for _ in range(4)] for _ in range(args.steps)] if op_events else None
+        times [K, ops]."""
+        ev = [[hev.create() for _ in range(nops + 1)] for _ in range(args.steps)] if op_events else None
         t0, t1 = hev.create(), hev.create()
         torch.cuda.synchronize()
         hev.record(t0, sh)
@@ -520,7 +605,7 @@ def main():
         step_ms = hev.ms(t0, t1) / args.steps
         op = None
         if op_events:
-            op = np.array([[hev.ms(e[j], e[j + 1]) for j in range(3)] for e in ev])
+            op = np.array([[hev.ms(e[j], e[j + 1]) for j in range(nops)] for e in ev])
         return step_ms, op
 
     # The headline figure: whole steps, nothing recorded between the ops.
@@ -558,18 +643,11 @@ def main():
         del g, gcalls
     hev.close()
 
-    if args.lowlatency:
-        b_lay, b_dis, b_com = ll_algorithmic_bytes(N, K, E, M, 7168, Hc, R, args.scale_format)
-    else:
-        b_lay, b_dis, b_com = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
-    total = b_lay + b_dis + b_com
+    total = sum(op_bytes)
     value = total / (ms_per_step * 1e-3) / 1e9
-    # the roofline is taken on the longer of the two streaming kernels
-    if args.lowlatency and op_ms[1] > op_ms[2]:
-        rop, rkernel, rbytes = 1, "dispatch_fp8_kernel", b_dis
-    else:
-        rop, rbytes = 2, b_com
-        rkernel = "combine_epilogue_kernel" if args.epilogue else "combine_kernel"
+    # the roofline is taken on the longest of the streaming kernels
+    rop = max((j for j, n in enumerate(names) if n in kernels), key=lambda j: op_ms[j])
+    rkernel, rbytes = kernels[names[rop]], op_bytes[rop]
     roof_gbs = rbytes / (op_ms[rop] * 1e-3) / 1e9
     traffic = traffic_entry(rkernel, workload_key)
     if args.lowlatency:
@@ -579,6 +657,13 @@ def main():
                     + (" (power-of-two)" if round_scale else "")
                     + f", combine bf16 hidden {Hc}, fp32 accumulation")
         metric = ("low-latency dispatch (fp8 cast) + combine effective HBM GB/s and tokens/s, "
+                  f"{N}×7168 top-{K}, 1 GPU")
+    elif args.backward:
+        workload = (f"{args.config} backward: N={N} tokens, top-{K} of {E} experts, combine "
+                    f"backward (bf16 grad_out {Hc} -> grad_y rows, fp32 weight gradients from y) "
+                    f"+ dispatch backward (bf16 grad rows 7168 -> grad_x, fp32 top-{K} weight "
+                    f"gradient rows -> grad_w)")
+        metric = ("combine backward + dispatch backward effective HBM GB/s and tokens/s, "
                   f"{N}×7168 top-{K}, 1 GPU")
     else:
         workload = (f"{args.config}: N={N} tokens, top-{K} of {E} experts, dispatch payload "
@@ -603,7 +688,7 @@ def main():
         "config": {
             "workload": workload,
             "tokens": N, "topk": K, "experts": E, "hidden": Hc,
-            "payload_bytes": (7168 * 2 if args.lowlatency else P),
+            "payload_bytes": (7168 * 2 if args.lowlatency or args.backward else P),
             "buffer_sets": len(sets), "algorithmic_bytes_per_step": total,
         },
         "tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
@@ -612,12 +697,10 @@ def main():
         "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
         "per_op_us_p10_p50_p90": {
             name: [round(float(np.percentile(op_all[:, j], q)) * 1e3, 2) for q in (10, 50, 90)]
-            for j, name in enumerate(("layout", "dispatch", "combine"))},
-        "per_op_us": {"layout": round(op_ms[0] * 1e3, 2), "dispatch": round(op_ms[1] * 1e3, 2),
-                      "combine": round(op_ms[2] * 1e3, 2)},
-        "per_op_gbs": {"layout": round(b_lay / (op_ms[0] * 1e-3) / 1e9, 1),
-                       "dispatch": round(b_dis / (op_ms[1] * 1e-3) / 1e9, 1),
-                       "combine": round(b_com / (op_ms[2] * 1e-3) / 1e9, 1)},
+            for j, name in enumerate(names)},
+        "per_op_us": {name: round(op_ms[j] * 1e3, 2) for j, name in enumerate(names)},
+        "per_op_gbs": {name: round(op_bytes[j] / (op_ms[j] * 1e-3) / 1e9, 1)
+                       for j, name in enumerate(names)},
         "roofline": {
             "kernel": rkernel,
             "bound": "hbm",
@@ -638,6 +721,8 @@ def main():
         if args.lowlatency:
             result["cpu_baseline"] = cpu_baseline_ll(wl, x, y, M, args.scale_format, round_scale,
                                                      total, args.cpu_seconds)
+        elif args.backward:
+            result["cpu_baseline"] = cpu_baseline_bwd(wl, host, total, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline(wl, y, total, args.cpu_seconds)
     print(json.dumps(result), flush=True)
