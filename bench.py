@@ -203,9 +203,19 @@ class BufferSet:
 
     def __init__(self, torch, mg, wl, y_bits):
         d = "cuda"
-        self.ids = torch.from_numpy(np.ascontiguousarray(wl.ids)).to(d)
-        self.w = torch.from_numpy(np.ascontiguousarray(wl.weights)).to(d)
-        self.srcs = [torch.from_numpy(a).to(d) for _, a in wl.fields]
+        if wl.records is not None:
+            # record mode: one 16-B-aligned record per token moves whole; the
+            # ids and weights are read in place from inside the records
+            rec = torch.from_numpy(wl.records).to(d)
+            self.srcs = [rec]
+            self.ids = rec.view(torch.int32)[:, :wl.K]
+            self.w = rec.view(torch.float32)[:, 8:8 + wl.K]
+            self.ids_stride = self.w_stride = rec.shape[1] // 4
+        else:
+            self.ids = torch.from_numpy(np.ascontiguousarray(wl.ids)).to(d)
+            self.w = torch.from_numpy(np.ascontiguousarray(wl.weights)).to(d)
+            self.srcs = [torch.from_numpy(a).to(d) for _, a in wl.fields]
+            self.ids_stride = self.w_stride = wl.K
         self.y = torch.from_numpy(y_bits.view(np.int16)).to(d).view(torch.bfloat16)
         N, K, E = wl.N, wl.K, wl.E
         self.cap = cap = mg.moe_required_capacity(N, K, E, 1)
@@ -230,13 +240,13 @@ class BufferSet:
         for i, (s, t) in enumerate(zip(self.srcs, self.dsts)):
             fields[i] = mg.moe_field(s.data_ptr(), s.stride(0), t.data_ptr(), t.stride(0), s.shape[1])
         self._fields = fields
-        lay = (self.ids.data_ptr(), K, N, K, E, 1, self.counts.data_ptr(), self.offsets.data_ptr(),
+        lay = (self.ids.data_ptr(), self.ids_stride, N, K, E, 1, self.counts.data_ptr(), self.offsets.data_ptr(),
                self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap, self.ws.data_ptr(),
                self.ws.numel(), self.status.data_ptr(), stream)
         dis = (fields, len(self.srcs), N, K, self.pos.data_ptr(), stream)
         if not epilogue:
-            com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K,
-                   wl.Hc, self.out.data_ptr(), wl.Hc, stream)
+            com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), self.w_stride, self.pos.data_ptr(),
+                   N, K, wl.Hc, self.out.data_ptr(), wl.Hc, stream)
             return (L.moe_get_layout, lay), (L.moe_dispatch, dis), (L.moe_combine, com)
         import ctypes
 
@@ -245,8 +255,8 @@ class BufferSet:
         ep.gamma, ep.eps = self.gamma.data_ptr(), 1e-6
         ep.residual_out, ep.residual_out_row_stride = self.residual_out.data_ptr(), wl.Hc
         self._ep = ep
-        com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K, wl.Hc,
-               ctypes.byref(ep), self.out.data_ptr(), wl.Hc, stream)
+        com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), self.w_stride, self.pos.data_ptr(), N,
+               K, wl.Hc, ctypes.byref(ep), self.out.data_ptr(), wl.Hc, stream)
         return (L.moe_get_layout, lay), (L.moe_dispatch, dis), (L.moe_combine_epilogue, com)
 
 
@@ -392,8 +402,8 @@ def cpu_baseline(wl, y, total_bytes, budget_s):
     `budget_s` seconds of work are done."""
     import oracle
 
-    srcs = [a for _, a in wl.fields]
-    w = np.ascontiguousarray(wl.weights)
+    srcs = [wl.records] if wl.records is not None else [a for _, a in wl.fields]
+    w = wl.weights                       # read in place (strided inside records)
     dsts = [np.empty((wl.N * wl.K, a.shape[1]), np.uint8) for a in srcs]
 
     def one():
@@ -486,7 +496,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="prefill",
-                    choices=["tiny", "decode", "prefill", "skewed"])
+                    choices=["tiny", "decode", "prefill", "skewed", "large"])
     ap.add_argument("--sets", type=int, default=2, help="rotating buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -667,7 +677,7 @@ def main():
                   f"{N}×7168 top-{K}, 1 GPU")
     else:
         workload = (f"{args.config}: N={N} tokens, top-{K} of {E} experts, dispatch payload "
-                    f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields)}), "
+                    f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields) or 'one record: ids, weights, 3584 B hidden, 448 B scales; ids and weights read in place'}), "
                     f"combine bf16 hidden {Hc}, fp32 accumulation"
                     + (", fused residual add + RMSNorm epilogue" if args.epilogue else ""))
         metric = METRIC

@@ -35,7 +35,11 @@ constexpr int kThreads = 256;              // hist / assign workgroup
 constexpr int kWaves = kThreads / kWave;   // 4
 constexpr int kHEntries = 16384;           // bound on chunks * padded experts
 constexpr int kMaxChunks = 64;
-constexpr int kPrefetch = 4;               // 64-pair steps of ids held in registers
+// 64-pair steps of ids held in registers per batch: 4 for small chunks
+// (short straight-line code, see reduce_chunks), 16 for large ones (one
+// load round instead of four per pass).
+constexpr int kBatchSmall = 4;
+constexpr int kBatchLarge = 16;
 
 struct Plan {
     int32_t chunk;    // pairs per workgroup (multiple of kThreads)
@@ -92,15 +96,16 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool valid, int
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
-// Loads the expert ids of 64-pair steps s0 .. s0+kPrefetch-1 of a wave's
+// Loads the expert ids of 64-pair steps s0 .. s0+B-1 of a wave's
 // quarter (-1 past the quarter or past the last pair). All loads are issued
 // before any is used.
-__device__ __forceinline__ void load_ids(int32_t (&e_reg)[kPrefetch],
+template <int B>
+__device__ __forceinline__ void load_ids(int32_t (&e_reg)[B],
                                          const int32_t* __restrict__ ids, int64_t stride,
                                          uint32_t nk, uint32_t K, uint32_t first, int s0,
                                          int steps, int lane) {
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
+    for (int j = 0; j < B; ++j) {
         const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
         e_reg[j] = (s0 + j < steps && i < nk) ? load_id(ids, stride, i, K) : -1;
     }
@@ -108,12 +113,13 @@ __device__ __forceinline__ void load_ids(int32_t (&e_reg)[kPrefetch],
 
 // Adds one batch of steps to the wave's counts cnt_row[e]; returns the number
 // of ids >= E in the batch.
-__device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[kPrefetch], int s0,
+template <int B>
+__device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[B], int s0,
                                                int steps, int32_t E, int nbits, int32_t* cnt_row,
                                                int lane) {
     int32_t bad = 0;
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
+    for (int j = 0; j < B; ++j) {
         if (s0 + j < steps) {   // wave-uniform
             const int32_t e = e_reg[j];
             const bool valid = e >= 0 && e < E;
@@ -130,14 +136,15 @@ __device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[kPrefetch]
 // expert plus the number of lower lanes in the same step with that expert.
 // In the padded form (M > 0) expert e's segment is rows e*M .. e*M+M-1 and
 // a pair ranked past it is dropped (pos = -1).
-__device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[kPrefetch], int s0, int steps,
+template <int B>
+__device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[B], int s0, int steps,
                                            int32_t E, int nbits, int32_t* base_row,
                                            uint32_t first, uint32_t nk, int lane,
                                            int32_t* __restrict__ pos,
                                            int32_t* __restrict__ row_pair, int64_t cap,
                                            int32_t M) {
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
+    for (int j = 0; j < B; ++j) {
         if (s0 + j < steps) {   // wave-uniform
             const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
             const int32_t e = e_reg[j];
@@ -155,6 +162,7 @@ __device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[kPrefetch], in
     }
 }
 
+template <int B>
 __global__ __launch_bounds__(kThreads) void layout_hist(const int32_t* __restrict__ ids,
                                                         int64_t stride, uint32_t nk, uint32_t K,
                                                         int32_t E, int32_t chunk, int nbits,
@@ -168,14 +176,14 @@ __global__ __launch_bounds__(kThreads) void layout_hist(const int32_t* __restric
     const int steps = quarter / kWave;
     const uint32_t first = (uint32_t)blockIdx.x * chunk + wave * quarter;
 
-    int32_t e_reg[kPrefetch];
+    int32_t e_reg[B];
     load_ids(e_reg, ids, stride, nk, K, first, 0, steps, lane);
     for (int x = threadIdx.x; x < kWaves * E; x += kThreads) cnt[x] = 0;
     __syncthreads();
 
     int32_t* row = cnt + wave * E;
     int32_t bad = count_batch(e_reg, 0, steps, E, nbits, row, lane);
-    for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
+    for (int s0 = B; s0 < steps; s0 += B) {
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
         bad += count_batch(e_reg, s0, steps, E, nbits, row, lane);
     }
@@ -244,6 +252,7 @@ __device__ __forceinline__ void reduce_chunks(const int32_t* __restrict__ H, int
     }
 }
 
+template <int B>
 __global__ __launch_bounds__(kThreads) void layout_assign(
     const int32_t* __restrict__ ids, int64_t stride, uint32_t nk, uint32_t K, int32_t E,
     int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
 
     // The ids of the first batch and the chunk histograms are fetched
     // together; the ids stay in registers for both passes below.
-    int32_t e_first[kPrefetch];
+    int32_t e_first[B];
     load_ids(e_first, ids, stride, nk, K, first, 0, steps, lane);
     // Few chunks (small batches) take a short form of the reduction: the
     // straight-line code a workgroup runs once is fetched into a cold
@@ -341,8 +350,8 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     // Per-wave counts of this chunk.
     int32_t* mine = cnt + wave * E;
     count_batch(e_first, 0, steps, E, nbits, mine, lane);
-    for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
-        int32_t e_reg[kPrefetch];
+    for (int s0 = B; s0 < steps; s0 += B) {
+        int32_t e_reg[B];
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
         count_batch(e_reg, s0, steps, E, nbits, mine, lane);
     }
@@ -361,8 +370,8 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     __syncthreads();
 
     rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M);
-    for (int s0 = kPrefetch; s0 < steps; s0 += kPrefetch) {
-        int32_t e_reg[kPrefetch];
+    for (int s0 = B; s0 < steps; s0 += B) {
+        int32_t e_reg[B];
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
         rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M);
     }
@@ -394,6 +403,34 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
 }  // namespace moe
 
 using namespace moe;
+
+// Both launches of a layout. B, the 64-pair steps of ids a wave holds per
+// batch, follows the chunk size: 4 steps when a wave's quarter has at most
+// 4 (short code for small batches), else 16 (fewer dependent load rounds).
+template <int B>
+static void launch_layout_b(const Plan& p, uint32_t assign_grid, const int32_t* ids, int64_t stride,
+                     int64_t nk, int32_t K, int32_t E, int32_t align, int32_t* H, int32_t* bad,
+                     int32_t* counts, int32_t* offsets, int32_t* status, int32_t* pos,
+                     int32_t* row_pair, int64_t cap, int32_t M, hipStream_t stream) {
+    if (p.blocks > 0)
+        layout_hist<B><<<p.blocks, kThreads, 0, stream>>>(ids, stride, (uint32_t)nk, (uint32_t)K,
+                                                          E, p.chunk, p.nbits, H, bad);
+    layout_assign<B><<<assign_grid, kThreads, 0, stream>>>(
+        ids, stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H, bad,
+        counts, offsets, status, pos, row_pair, cap, M);
+}
+
+static void launch_layout(const Plan& p, uint32_t assign_grid, const int32_t* ids, int64_t stride,
+                   int64_t nk, int32_t K, int32_t E, int32_t align, int32_t* H, int32_t* bad,
+                   int32_t* counts, int32_t* offsets, int32_t* status, int32_t* pos,
+                   int32_t* row_pair, int64_t cap, int32_t M, hipStream_t stream) {
+    if (p.chunk / kThreads > kBatchSmall)
+        launch_layout_b<kBatchLarge>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
+                                     offsets, status, pos, row_pair, cap, M, stream);
+    else
+        launch_layout_b<kBatchSmall>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
+                                     offsets, status, pos, row_pair, cap, M, stream);
+}
 
 extern "C" int64_t moe_required_capacity(int32_t N, int32_t K, int32_t E, int32_t align) {
     if (N < 0 || K < 1 || E < 1 || align < 1) return -1;
@@ -450,12 +487,8 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
     clear_launch_error();
     int32_t* H = static_cast<int32_t*>(workspace);
     int32_t* bad = H + (int64_t)p.blocks * E;
-    if (p.blocks > 0)
-        layout_hist<<<p.blocks, kThreads, 0, stream>>>(ids, ids_row_stride, (uint32_t)nk,
-                                                       (uint32_t)K, E, p.chunk, p.nbits, H, bad);
-    layout_assign<<<p.blocks > 0 ? p.blocks : 1, kThreads, 0, stream>>>(
-        ids, ids_row_stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H,
-        bad, counts, offsets, status, pos, row_pair, cap, 0);
+    launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
+                  counts, offsets, status, pos, row_pair, cap, 0, stream);
     return check_launch("moe_get_layout");
 }
 
@@ -493,17 +526,13 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     clear_launch_error();
     int32_t* H = static_cast<int32_t*>(workspace);
     int32_t* bad = H + (int64_t)p.blocks * E;
-    if (p.blocks > 0)
-        layout_hist<<<p.blocks, kThreads, 0, stream>>>(ids, ids_row_stride, (uint32_t)nk,
-                                                       (uint32_t)K, E, p.chunk, p.nbits, H, bad);
     // Workgroups past the chunks only mark unused rows: one per 2048 rows,
     // at most 256.
     int64_t grid = ceil_div<int64_t>(cap, 8 * kThreads);
     if (grid > 256) grid = 256;
     if (grid < p.blocks) grid = p.blocks;
     if (grid < 1) grid = 1;
-    layout_assign<<<(uint32_t)grid, kThreads, 0, stream>>>(
-        ids, ids_row_stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, 1, H, bad,
-        counts, nullptr, status, pos, row_pair, cap, M);
+    launch_layout(p, (uint32_t)grid, ids, ids_row_stride, nk, K, E, 1, H, bad, counts, nullptr,
+                  status, pos, row_pair, cap, M, stream);
     return check_launch("moe_get_layout_padded");
 }
