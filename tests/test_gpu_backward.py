@@ -215,3 +215,72 @@ def test_backward_errors(mg):
         mg.moe_dispatch_backward(torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda"), pos,
                                  torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda"),
                                  grad_recv_w=torch.zeros((8, 2), device="cuda"))
+
+
+def test_graph_capture_lowlatency_and_backward(mg):
+    """Padded layout -> FP8 dispatch -> combine -> combine backward ->
+    dispatch backward captured once and replayed on new inputs (eager work
+    and a synchronization between replays); every replay equals the eager
+    calls on the same inputs."""
+    N, K, E, H, M = 96, 4, 16, 512, 96
+    rows = E * M
+    ids_s = torch.zeros((N, K), dtype=torch.int32, device="cuda")
+    x_s = torch.zeros((N, H), dtype=torch.bfloat16, device="cuda")
+    w_s = torch.zeros((N, K), dtype=torch.float32, device="cuda")
+    y_s = torch.zeros((rows, H), dtype=torch.bfloat16, device="cuda")
+    g_s = torch.zeros((N, H), dtype=torch.bfloat16, device="cuda")
+    gr_s = torch.zeros((rows, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(mg.moe_layout_workspace_bytes(N, K, E), 256), dtype=torch.uint8, device="cuda")
+
+    def buffers():
+        return dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+                    pos=torch.empty((N, K), dtype=torch.int32, device="cuda"),
+                    row_pair=torch.empty(rows, dtype=torch.int32, device="cuda"),
+                    status=torch.empty(2, dtype=torch.int32, device="cuda"),
+                    codes=torch.zeros((rows, H), dtype=torch.uint8, device="cuda"),
+                    scales=torch.zeros((E, H // 128, M), dtype=torch.float32, device="cuda"),
+                    out=torch.empty((N, H), dtype=torch.bfloat16, device="cuda"),
+                    gy=torch.zeros((rows, H), dtype=torch.bfloat16, device="cuda"),
+                    gw=torch.empty((N, K), dtype=torch.float32, device="cuda"),
+                    gx=torch.empty((N, H), dtype=torch.bfloat16, device="cuda"))
+
+    def step(b):
+        mg.moe_get_layout_padded(ids_s, E, M, b["counts"], b["pos"], b["row_pair"], ws, b["status"])
+        mg.moe_dispatch_fp8(x_s, b["pos"], K, b["codes"], b["scales"], mg.MOE_SCALE_COLS, M, False)
+        mg.moe_combine(y_s, w_s, b["pos"], b["out"])
+        mg.moe_combine_backward(g_s, w_s, b["pos"], b["gy"], y=y_s, grad_w=b["gw"])
+        mg.moe_dispatch_backward(gr_s, b["pos"], b["gx"])
+
+    gb = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(gb)                                          # warm up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(gb)
+    for rep in range(4):
+        say(f"graph replay {rep}")
+        rng = np.random.default_rng(300 + rep)
+        ids = mw.uniform_distinct_ids(rng, N, K, E)
+        ids[rng.random((N, K)) < 0.1] = -1
+        ids_s.copy_(dev(ids))
+        x_s.copy_(dev_bf16(bits(rng.standard_normal((N, H)) * 4)))
+        w_s.copy_(dev(rng.standard_normal((N, K)).astype(np.float32)))
+        y_s.copy_(dev_bf16(bits(rng.standard_normal((rows, H)))))
+        g_s.copy_(dev_bf16(bits(rng.standard_normal((N, H)))))
+        gr_s.copy_(dev_bf16(bits(rng.standard_normal((rows, H)))))
+        for t in gb.values():                             # no stale rows or scale slots
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eb = buffers()
+        step(eb)
+        torch.cuda.synchronize()
+        for name in gb:
+            a, b = gb[name], eb[name]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), (rep, name)
