@@ -70,6 +70,7 @@ KERNEL_SOURCES = {
     "layout_assign": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
     "dispatch_fp8_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
     "combine_backward_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
+    "dispatch_fp8_padded_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
@@ -281,8 +282,9 @@ class LowLatencySet:
     rows per expert), bf16 -> e4m3 cast on dispatch with per-128-channel
     scales, combine reading the expert outputs from the padded buffer."""
 
-    def __init__(self, torch, mg, wl, x_bits, y_bits, M, scale_format, round_scale):
+    def __init__(self, torch, mg, wl, x_bits, y_bits, M, scale_format, round_scale, fused=False):
         d = "cuda"
+        self.fused = fused
         N, K, E, Hc = wl.N, wl.K, wl.E, wl.Hc
         H = x_bits.shape[1]
         self.M, self.H, self.fmt = M, H, SCALE_FORMATS[scale_format]
@@ -328,6 +330,12 @@ class LowLatencySet:
                self.scales.data_ptr(), self.fmt, srs, M, self.round_scale, stream)
         com = (self.y.data_ptr(), Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K, Hc,
                self.out.data_ptr(), Hc, stream)
+        if self.fused:
+            fu = (self.ids.data_ptr(), K, N, K, E, M, self.x.data_ptr(), H, H,
+                  self.counts.data_ptr(), self.pos.data_ptr(), self.row_pair.data_ptr(),
+                  self.status.data_ptr(), self.codes.data_ptr(), H, self.scales.data_ptr(),
+                  self.fmt, srs, self.round_scale, stream)
+            return (L.moe_dispatch_fp8_padded, fu), (L.moe_combine, com)
         return (L.moe_get_layout_padded, lay), (L.moe_dispatch_fp8, dis), (L.moe_combine, com)
 
 
@@ -515,6 +523,9 @@ def main():
                     help="--lowlatency scales: rows, cols (column-major fp32) or ue8m0")
     ap.add_argument("--round-scale", action="store_true",
                     help="--lowlatency: round scales up to powers of two (implied by ue8m0)")
+    ap.add_argument("--fused", action="store_true",
+                    help="--lowlatency: the padded layout and the FP8 dispatch in one launch "
+                         "(moe_dispatch_fp8_padded; N*K <= 8192)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward instead: combine backward (grad_y, grad_w) + "
                          "dispatch backward (grad_x, weight gradients) on the forward's layout")
@@ -526,11 +537,15 @@ def main():
     args = ap.parse_args()
     workload_key = args.config + (f"-lowlatency-{args.scale_format}" if args.lowlatency else
                                   "-backward" if args.backward else "")
+    if args.fused:
+        workload_key += "-fused"
     if args.traffic_from:
         summarize_traffic(*args.traffic_from, workload_key, args.traffic_command)
         return
     if args.lowlatency + args.epilogue + args.backward > 1:
         raise SystemExit("--lowlatency, --epilogue and --backward are separate measurements")
+    if args.fused and not args.lowlatency:
+        raise SystemExit("--fused is a form of --lowlatency")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -554,11 +569,15 @@ def main():
     round_scale = args.round_scale or args.scale_format == "ue8m0"
     if args.lowlatency:
         x = mw.make_x(N, 7168, wl.seed + 104729)
-        sets = [LowLatencySet(torch, mg, wl, x, y, M, args.scale_format, round_scale)
+        sets = [LowLatencySet(torch, mg, wl, x, y, M, args.scale_format, round_scale, args.fused)
                 for _ in range(max(1, args.sets))]
         names = ("layout", "dispatch", "combine")
         op_bytes = ll_algorithmic_bytes(N, K, E, M, 7168, Hc, R, args.scale_format)
         kernels = {"dispatch": "dispatch_fp8_kernel", "combine": "combine_kernel"}
+        if args.fused:
+            names = ("layout+dispatch", "combine")
+            op_bytes = (op_bytes[0] + op_bytes[1], op_bytes[2])
+            kernels = {"layout+dispatch": "dispatch_fp8_padded_kernel", "combine": "combine_kernel"}
     elif args.backward:
         rng = np.random.default_rng(wl.seed + 7)
         host = {"y": y, "grad_out": mw.make_y(N, Hc, wl.seed + 11),
@@ -661,7 +680,8 @@ def main():
     roof_gbs = rbytes / (op_ms[rop] * 1e-3) / 1e9
     traffic = traffic_entry(rkernel, workload_key)
     if args.lowlatency:
-        workload = (f"{args.config} low-latency: N={N} tokens, top-{K} of {E} experts, padded "
+        workload = (f"{args.config} low-latency{' (layout and dispatch fused)' if args.fused else ''}: "
+                    f"N={N} tokens, top-{K} of {E} experts, padded "
                     f"{M} rows per expert, bf16 hidden 7168 cast to e4m3 on dispatch with "
                     f"{args.scale_format} scales per 128 channels"
                     + (" (power-of-two)" if round_scale else "")

@@ -6,7 +6,7 @@ The functions named like the C ABI (``moe_get_layout``, ``moe_dispatch``,
 device pointers plus ``torch.cuda.current_stream()`` to the library; every
 step of the path runs in the library's HIP kernels. PyTorch provides device
 memory and streams only. There is no CPU path: importing this package fails
-if the library has not been built (``python -m combine_moe_get_amd.build``).
+if the library has not been built (``python combine_moe_get_amd/build.py``).
 
 Convenience wrappers (``layout``, ``dispatch``, ``combine``,
 ``pack_records``, ``unpack_records``) allocate outputs with torch and call the
@@ -43,7 +43,7 @@ _ERR_NAMES = {MOE_ERR_ARG: "MOE_ERR_ARG", MOE_ERR_ALIGN: "MOE_ERR_ALIGN",
               MOE_ERR_WORKSPACE: "MOE_ERR_WORKSPACE", MOE_ERR_HIP: "MOE_ERR_HIP"}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m combine_moe_get_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python combine_moe_get_amd/build.py` "
                       "(there is no fallback path)")
 
 
@@ -83,6 +83,9 @@ def _load():
     L.moe_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32,
                                        ctypes.POINTER(moe_epilogue), P, i64, P]
     L.moe_combine_epilogue.restype = ctypes.c_int
+    L.moe_dispatch_fp8_padded.argtypes = [P, i64, i32, i32, i32, i32, P, i64, i32, P, P, P, P, P,
+                                          i64, P, i32, i64, i32, P]
+    L.moe_dispatch_fp8_padded.restype = ctypes.c_int
     L.moe_dispatch_backward.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64, P]
     L.moe_dispatch_backward.restype = ctypes.c_int
     L.moe_combine_backward.argtypes = [P, i64, P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64,
@@ -91,7 +94,11 @@ def _load():
     return L
 
 
-_lib = _load()
+try:
+    _lib = _load()
+except AttributeError as exc:   # a library built from older sources
+    raise ImportError(f"{LIB_PATH} lacks an entry point ({exc}); rebuild it with "
+                      "`python combine_moe_get_amd/build.py`") from None
 
 
 class MoeError(RuntimeError):
@@ -271,6 +278,45 @@ def moe_combine(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor, out: 
     op, os_ = _rows(out, "out") if N else (0, Hc)
     _check(_lib.moe_combine(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc, op, os_,
                             _stream(stream)))
+
+
+def moe_dispatch_fp8_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: int,
+                            x: torch.Tensor, counts: torch.Tensor, pos: torch.Tensor,
+                            row_pair: torch.Tensor, status: torch.Tensor, dst: torch.Tensor,
+                            scales: torch.Tensor, scale_format: int = MOE_SCALE_COLS,
+                            round_scale: bool = False, stream=None) -> None:
+    """moe_get_layout_padded + moe_dispatch_fp8 in one launch (N*K <= 8192)."""
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise TypeError("ids must be int32 [N, K]")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if dst.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("dst must be uint8 or float8_e4m3fn")
+    for t, n in ((counts, "counts"), (pos, "pos"), (row_pair, "row_pair"), (status, "status")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    N, K = ids.shape
+    E, M = num_experts, rows_per_expert
+    H = x.shape[1]
+    if x.shape[0] != N or pos.numel() != N * K or counts.numel() < E or \
+            row_pair.numel() < E * M or status.numel() < 2:
+        raise ValueError("shape mismatch between ids, x, counts, pos, row_pair and status")
+    ip, istr = _rows(ids, "ids") if N else (0, K)
+    xp, xs = _rows(x, "x") if N else (0, H)
+    dp, ds = _rows(dst, "dst") if dst.shape[0] else (0, H)
+    if scale_format == MOE_SCALE_ROWS:
+        if scales.dtype != torch.float32 or scales.dim() != 2 or scales.stride(1) != 1:
+            raise TypeError("row scales must be float32 [rows, >= H/128] with contiguous rows")
+        srs = scales.stride(0)
+    else:
+        if not scales.is_contiguous():
+            raise TypeError("column-major scales must be a contiguous tensor")
+        srs = 0
+    _check(_lib.moe_dispatch_fp8_padded(ip, istr, N, K, E, M, xp, xs, H, _dev(counts, "counts"),
+                                        _dev(pos, "pos"), _dev(row_pair, "row_pair"),
+                                        _dev(status, "status"), dp, ds, _dev(scales, "scales"),
+                                        scale_format, srs, int(bool(round_scale)),
+                                        _stream(stream)))
 
 
 def moe_dispatch_backward(grad_recv: torch.Tensor, pos: torch.Tensor, grad_x: torch.Tensor,

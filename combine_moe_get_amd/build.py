@@ -1,6 +1,9 @@
 """Build libmoe_get.so (the C-ABI HIP library) in-tree for gfx950.
 
-    python -m combine_moe_get_amd.build
+    python combine_moe_get_amd/build.py
+
+(run as a script, so that the package -- which loads the library -- is not
+imported before the library exists)
 
 Every source is compiled with hipcc for gfx950 only, without fast-math and
 with FP contraction off (the combine's FMAs are explicit), and with packed

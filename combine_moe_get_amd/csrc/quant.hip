@@ -69,22 +69,13 @@ __device__ __forceinline__ uint32_t pack4(const float* f, float s) {
            (e4m3_code(f[3] / s) << 24);
 }
 
-__global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t gw = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const uint32_t t = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
-    if (t >= (uint32_t)a.N) return;
-    const int32_t seg = (int32_t)(gw - t * (uint32_t)a.segs);
-
-    // Rows of the token's K pairs: lane k < K fetches pos[t*K + k].
-    int32_t pk = (int32_t)t;
-    if (a.pos != nullptr) pk = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
-
-    // The 8 lanes of a 128-channel block are either all inside H or all
-    // past it (H % 128 == 0); every lane takes part in the lane swaps.
+// Loads this lane's 16 channels of segment seg (1024 channels) of token t;
+// lanes past H get zeros. The 8 lanes of a 128-channel block are either all
+// inside H or all past it (H % 128 == 0).
+__device__ __forceinline__ bool load_segment(const Fp8Args& a, uint32_t t, int32_t seg, int lane,
+                                             float (&f)[16]) {
     const int32_t c0 = seg * kChanPerWave + lane * kChanPerLane;
     const bool active = c0 < a.H;
-    float f[16];
     if (active) {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.xs + c0);
         const u32x4 v0 = __builtin_nontemporal_load(src);
@@ -99,6 +90,15 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) f[i] = 0.0f;
     }
+    return active;
+}
+
+// Quantises a loaded segment once and stores it, with its scales, to the
+// rows of the token's K pairs: lane k < K holds the row of pair k in pk (-1:
+// not dispatched). Every lane takes part in the lane swaps.
+__device__ __forceinline__ void cast_and_store(const Fp8Args& a, int32_t seg, int lane,
+                                               int32_t pk, const float (&f)[16], bool active) {
+    const int32_t c0 = seg * kChanPerWave + lane * kChanPerLane;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
@@ -140,10 +140,227 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
     }
 }
 
+__global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t gw = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
+    if (t >= (uint32_t)a.N) return;
+    const int32_t seg = (int32_t)(gw - t * (uint32_t)a.segs);
+
+    // Rows of the token's K pairs: lane k < K fetches pos[t*K + k].
+    int32_t pk = (int32_t)t;
+    if (a.pos != nullptr) pk = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
+    float f[16];
+    const bool active = load_segment(a, t, seg, lane, f);
+    cast_and_store(a, seg, lane, pk, f, active);
+}
+
+// ---------------------------------------------------------------------------
+// Padded layout and FP8 dispatch in one launch, for small batches. In the
+// padded layout pair (t, k) with expert e lands on row e*M + r, where r is the
+// number of earlier pairs in (t, k) order with the same expert (r >= M:
+// dropped): no global offsets are needed, so every workgroup can find its
+// token's rows from one pass over the batch's ids. Workgroup (t, g) takes
+// token t and the 1024-channel segments 4g .. 4g+3 (one per wave):
+//   1. one pass over all N*K ids: per-expert totals in LDS (integer atomics,
+//      so the totals do not depend on their order) and, for the token's K
+//      experts, the matches among earlier tokens;
+//   2. r(t, k) = matches(e_k) + (earlier k' < k of the token with e_k' = e_k);
+//      workgroup (t, 0) writes pos and row_pair of the token's pairs;
+//   3. workgroup 0 writes counts and status from the totals; every expert's
+//      unused rows are marked -1 by workgroup e mod (number of workgroups);
+//   4. each wave casts and stores its segment (cast_and_store), whose
+//      channels it loaded before step 1.
+// Used and unused rows are disjoint sets derived from the same totals, so
+// no two workgroups write the same row_pair entry.
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedThreads = 256;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedMaxPairs = 8192;
+
+struct FusedArgs {
+    const int32_t* ids;
+    int64_t ids_stride;
+    int32_t E, groups;   // groups: workgroups per token
+    int32_t* counts;
+    int32_t* pos;
+    int32_t* row_pair;
+    int32_t* status;
+};
+
+__global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(const Fp8Args a,
+                                                                            const FusedArgs f) {
+    __shared__ int32_t tot[MOE_MAX_EXPERTS];
+    __shared__ int32_t hits[MOE_MAX_TOPK];
+    __shared__ int32_t rows[MOE_MAX_TOPK];
+    __shared__ int32_t tok_e[MOE_MAX_TOPK];
+    __shared__ int32_t nbad_s, drop_s;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const uint32_t t = blockIdx.x / (uint32_t)f.groups;
+    const int32_t g = (int32_t)(blockIdx.x - t * (uint32_t)f.groups);
+    const int32_t K = a.K, E = f.E, M = a.M;
+    const int32_t nk = a.N * K;
+    // N = 0 launches one workgroup for counts, status and row_pair only
+    const bool has_token = t < (uint32_t)a.N;
+    const int32_t* idrow = f.ids + (int64_t)t * f.ids_stride;
+
+    // The token's channels do not depend on the layout: their loads are
+    // issued first and complete during the count pass.
+    const int32_t seg = g * kFusedWaves + wave;
+    const bool casts = has_token && seg < a.segs;
+    float xv[16];
+    bool active = false;
+    if (casts) active = load_segment(a, t, seg, lane, xv);
+
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) tot[e] = 0;
+    if (threadIdx.x < MOE_MAX_TOPK) hits[threadIdx.x] = 0;
+    if ((int32_t)threadIdx.x < K) tok_e[threadIdx.x] = has_token ? idrow[threadIdx.x] : -1;
+    if (threadIdx.x == 0) nbad_s = drop_s = 0;
+    __syncthreads();
+
+    // 1. totals, bad ids, and matches of the token's experts before token t
+    const int32_t before = (int32_t)t * K;
+    int32_t nbad = 0;
+    for (int32_t i = threadIdx.x; i < nk; i += kFusedThreads) {
+        const int32_t ti = i / K;
+        const int32_t v = f.ids[(int64_t)ti * f.ids_stride + (i - ti * K)];
+        if (v >= E) {
+            ++nbad;
+        } else if (v >= 0) {
+            atomicAdd(&tot[v], 1);
+            if (i < before)
+                for (int32_t k = 0; k < K; ++k)
+                    if (v == tok_e[k]) atomicAdd(&hits[k], 1);
+        }
+    }
+    if (nbad) atomicAdd(&nbad_s, nbad);
+    __syncthreads();
+
+    // 2. the token's rows
+    if (has_token && (int32_t)threadIdx.x < K) {
+        const int32_t k = threadIdx.x;
+        const int32_t e = tok_e[k];
+        int32_t p = -1;
+        if (e >= 0 && e < E) {
+            int32_t r = hits[k];
+            for (int32_t j = 0; j < k; ++j) r += tok_e[j] == e;
+            if (r < M) p = e * M + r;
+        }
+        rows[k] = p;
+        if (g == 0) {
+            f.pos[(int64_t)t * K + k] = p;
+            if (p >= 0) f.row_pair[p] = (int32_t)t * K + k;
+        }
+    }
+
+    // 3. counts and status (workgroup 0), unused rows (spread by expert)
+    const uint32_t B = gridDim.x;
+    if (blockIdx.x == 0) {
+        int32_t d = 0;
+        for (int e = threadIdx.x; e < E; e += kFusedThreads) {
+            f.counts[e] = min(tot[e], M);
+            d += max(tot[e] - M, 0);
+        }
+        if (d) atomicAdd(&drop_s, d);
+    }
+    for (int32_t e = blockIdx.x; e < E; e += (int32_t)B)
+        for (int32_t r = min(tot[e], M) + threadIdx.x; r < M; r += kFusedThreads)
+            f.row_pair[(int64_t)e * M + r] = -1;
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        f.status[0] = nbad_s;
+        f.status[1] = drop_s;
+    }
+
+    // 4. cast and store this workgroup's segments
+    if (!casts) return;
+    const int32_t pk = lane < K ? rows[lane] : -1;
+    cast_and_store(a, seg, lane, pk, xv, active);
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
+                                       int32_t K, int32_t E, int32_t M, const void* x,
+                                       int64_t x_row_stride, int32_t H, int32_t* counts,
+                                       int32_t* pos, int32_t* row_pair, int32_t* status, void* dst,
+                                       int64_t dst_row_stride, void* scales, int32_t scale_format,
+                                       int64_t scale_row_stride, int32_t round_scale,
+                                       hipStream_t stream) {
+    if (N < 0 || K < 1 || E < 1 || M < 1 || H < 0)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: need N >= 0, K >= 1, E >= 1, M >= 1, "
+                    "H >= 0");
+    if (K > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8_padded: K=%d E=%d beyond K <= %d, E <= %d",
+                    K, E, MOE_MAX_TOPK, MOE_MAX_EXPERTS);
+    if ((int64_t)N * K > kFusedMaxPairs)
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8_padded: N*K=%lld above %d (use "
+                    "moe_get_layout_padded + moe_dispatch_fp8)", (long long)N * K, kFusedMaxPairs);
+    if ((int64_t)E * M >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8_padded: E*M must be below 2^31");
+    if (scale_format < MOE_SCALE_ROWS || scale_format > MOE_SCALE_UE8M0)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: unknown scale_format %d", scale_format);
+    if (H % kBlock != 0)
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: H=%d must be a multiple of 128", H);
+    if (scale_format == MOE_SCALE_UE8M0 && (!round_scale || H % (4 * kBlock) != 0))
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: ue8m0 scales need round_scale and "
+                    "H %% 512 == 0");
+    if (scale_format == MOE_SCALE_ROWS && scale_row_stride < H / kBlock)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: scale_row_stride < H/128");
+    if (counts == nullptr || row_pair == nullptr || status == nullptr)
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: counts, row_pair and status must not "
+                    "be NULL");
+    if (N > 0 && (ids == nullptr || pos == nullptr || ids_row_stride < K))
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: NULL ids/pos or ids_row_stride < K");
+    if (N > 0 && H > 0 && (x == nullptr || dst == nullptr || scales == nullptr))
+        return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: NULL pointer");
+    if (!aligned(x, 16) || x_row_stride % 8 != 0 || (N > 0 && H > 0 && x_row_stride < H))
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: x must be 16-byte aligned with a row "
+                    "stride that is a multiple of 8 elements and >= H");
+    if (!aligned(dst, 16) || dst_row_stride % 16 != 0 || (N > 0 && H > 0 && dst_row_stride < H))
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: dst must be 16-byte aligned with a "
+                    "row stride that is a multiple of 16 bytes and >= H");
+    if (!aligned(scales, 4) || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(pos, 4) ||
+        !aligned(row_pair, 4) || !aligned(status, 4))
+        return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: int32 and scale pointers must be "
+                    "4-byte aligned");
+
+    Fp8Args a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.xs = x_row_stride;
+    a.N = N;
+    a.K = K;
+    a.H = H;
+    a.segs = ceil_div<int32_t>(H, kChanPerWave);
+    a.pos = nullptr;
+    a.dst = static_cast<uint8_t*>(dst);
+    a.ds = dst_row_stride;
+    a.scales = scales;
+    a.mode = scale_format;
+    a.srs = scale_row_stride;
+    a.M = M;
+    a.round_scale = round_scale ? 1 : 0;
+    FusedArgs f;
+    f.ids = ids;
+    f.ids_stride = ids_row_stride;
+    f.E = E;
+    f.groups = a.segs > 0 ? ceil_div<int32_t>(a.segs, kFusedWaves) : 1;
+    f.counts = counts;
+    f.pos = pos;
+    f.row_pair = row_pair;
+    f.status = status;
+    // N = 0 still runs one workgroup: counts, status and every row_pair
+    // entry are outputs.
+    const int64_t blocks = N > 0 ? (int64_t)N * f.groups : 1;
+    clear_launch_error();
+    dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
+    return check_launch("moe_dispatch_fp8_padded");
+}
 
 extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K,
                                 int32_t H, const int32_t* pos, void* dst, int64_t dst_row_stride,

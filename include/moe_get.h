@@ -285,6 +285,32 @@ int moe_combine_epilogue(const void* y, int64_t y_row_stride, const float* w,
                          hipStream_t stream);
 
 /*
+ * Padded layout and FP8 dispatch in one launch, for small (decode-sized)
+ * batches: the same results as moe_get_layout_padded(ids, ..., E, M, counts,
+ * pos, row_pair, ..., status) followed by moe_dispatch_fp8(x, ..., pos, dst,
+ * ..., scales, scale_format, ..., M, round_scale), bit for bit, without the
+ * layout's workspace. In the padded layout the row of a pair needs no global
+ * offsets (expert e starts at e*M), so every workgroup finds its token's rows
+ * from one pass over the batch's ids; the launch count at decode drops from
+ * three to one. Cited passages: those of moe_get_layout_padded and
+ * moe_dispatch_fp8 (DeepEP repository dump, deep_ep.cpp,
+ * Buffer::low_latency_dispatch).
+ *
+ * Arguments, layouts and alignment are those of the two calls it replaces
+ * (ids with a row stride in elements; x bf16; dst, scales as in
+ * moe_dispatch_fp8 with rows_per_expert = M; status[2]). counts, row_pair and
+ * status are written even when N = 0. Limits: N*K <= 8192 (larger batches:
+ * the two calls), 1 <= K <= 32, 1 <= E <= 1024, M >= 1, E*M < 2^31,
+ * H % 128 == 0. Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT,
+ * MOE_ERR_HIP.
+ */
+int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                            int32_t E, int32_t M, const void* x, int64_t x_row_stride, int32_t H,
+                            int32_t* counts, int32_t* pos, int32_t* row_pair, int32_t* status,
+                            void* dst, int64_t dst_row_stride, void* scales, int32_t scale_format,
+                            int64_t scale_row_stride, int32_t round_scale, hipStream_t stream);
+
+/*
  * Backward of the dispatch (DeepEP repository dump, README, "Example use in
  * model training": the backward of a dispatch is a combine of the received
  * rows' gradients, with the received top-k weights' gradients combined

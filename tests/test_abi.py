@@ -241,3 +241,37 @@ def test_backward_validation(lib):
     assert C(P, 64, P, 8, P, 64, P, 4, 8, 64, 0, 64, P, 8, 0) == lib.MOE_ERR_ARG        # NULL grad_y
     assert C(P, 64, P, 8, 0, 64, P, 0, 8, 64, P, 64, 0, 8, 0) == lib.MOE_OK             # N = 0
     assert C(P, 64, P, 8, 0, 64, P, 4, 8, 0, P, 64, 0, 8, 0) == lib.MOE_OK              # Hc = 0, no w
+
+
+def test_fused_padded_fp8_validation(lib):
+    F = lib._lib.moe_dispatch_fp8_padded
+    P = 0x10000
+    # (ids, istr, N, K, E, M, x, xs, H, counts, pos, row_pair, status, dst, ds, scales, fmt, srs, round, stream)
+    ok = lambda **kw: [kw.get(n, d) for n, d in (
+        ("ids", P), ("istr", 8), ("N", 16), ("K", 8), ("E", 32), ("M", 16), ("x", P), ("xs", 256),
+        ("H", 256), ("counts", P), ("pos", P), ("rp", P), ("st", P), ("dst", P), ("ds", 256),
+        ("sc", P), ("fmt", 1), ("srs", 0), ("rnd", 0), ("stream", 0))]
+    assert F(*ok(N=1025)) == lib.MOE_ERR_LIMIT            # N*K > 8192
+    assert F(*ok(K=33)) == lib.MOE_ERR_LIMIT
+    assert F(*ok(M=0)) == lib.MOE_ERR_ARG
+    assert F(*ok(H=200)) == lib.MOE_ERR_ALIGN              # H % 128
+    assert F(*ok(fmt=2, rnd=0)) == lib.MOE_ERR_ARG         # ue8m0 needs round_scale
+    assert F(*ok(fmt=0, srs=1)) == lib.MOE_ERR_ARG         # row scale stride
+    assert F(*ok(st=0)) == lib.MOE_ERR_ARG
+    assert F(*ok(istr=4)) == lib.MOE_ERR_ARG               # ids stride < K
+    assert F(*ok(x=P + 8)) == lib.MOE_ERR_ALIGN
+    assert F(*ok(ds=264)) == lib.MOE_ERR_ALIGN
+    assert F(*ok(pos=P + 2)) == lib.MOE_ERR_ALIGN
+
+
+def test_builder_loads_without_the_package():
+    """build() must work when the library is missing or stale: the builder
+    is loaded by path, without importing the package that loads the library."""
+    code = ("import importlib.util, sys\n"
+            f"spec = importlib.util.spec_from_file_location('b', {os.path.join(ROOT, 'combine_moe_get_amd', 'build.py')!r})\n"
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+            "assert callable(m.build) and 'combine_moe_get_amd' not in sys.modules\n")
+    r = subprocess.run(["python3", "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
+    assert "spec_from_file_location" in src and "from combine_moe_get_amd import build" not in src

@@ -190,3 +190,66 @@ def test_padded_layout_empty_batch(mg):
     torch.cuda.synchronize()
     assert (counts.cpu() == 0).all() and (row_pair.cpu() == -1).all()
     assert status.cpu().tolist() == [0, 0]
+
+
+def _fused_case(mg, ids, E, M, x_bits, fmt, round_scale, fill=0x3C):
+    """moe_dispatch_fp8_padded against the oracle's padded layout followed by
+    its FP8 dispatch: every output bit-exact, untouched rows keep `fill`."""
+    N, K = ids.shape
+    H = x_bits.shape[1]
+    rows = E * M
+    counts = torch.full((E,), -9, dtype=torch.int32, device="cuda")
+    pos = torch.full((N, K), -9, dtype=torch.int32, device="cuda")
+    row_pair = torch.full((rows,), -9, dtype=torch.int32, device="cuda")
+    status = torch.full((2,), -9, dtype=torch.int32, device="cuda")
+    dst = torch.full((rows, H), fill, dtype=torch.uint8, device="cuda")
+    shape = {0: (rows, H // 128), 1: (E, H // 128, M), 2: (E, H // 512, M)}[fmt]
+    scales = torch.zeros(shape, dtype=torch.int32 if fmt == 2 else torch.float32, device="cuda")
+    mg.moe_dispatch_fp8_padded(dev(ids), E, M, dev(x_bits.view(np.int16)).view(torch.bfloat16),
+                               counts, pos, row_pair, status, dst, scales, fmt, round_scale)
+    torch.cuda.synchronize()
+    c, p, rp, st = oracle.layout_padded(ids, E, M)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(pos.cpu().numpy(), p)
+    assert np.array_equal(row_pair.cpu().numpy(), rp)
+    assert tuple(status.cpu().tolist()) == st
+    codes, ref_scales = oracle.dispatch_fp8(x_bits, p, rows, fmt, M, round_scale, fill=fill)
+    assert np.array_equal(dst.cpu().numpy(), codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,round_scale", [(0, False), (1, False), (1, True), (2, True)])
+def test_fused_padded_fp8_decode(mg, fmt, round_scale):
+    rng = np.random.default_rng(60 + fmt)
+    N, K, E, H, M = 128, 8, 256, 7168, 128
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    say(f"fused decode format={fmt} round_scale={round_scale}")
+    _fused_case(mg, ids, E, M, _x(rng, N, H), fmt, round_scale)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_padded_fp8_random(mg, seed):
+    """Drops (M below the counts), masked and out-of-range ids, duplicate
+    experts within a token, H not a multiple of 1024."""
+    rng = np.random.default_rng(400 + seed)
+    N = int(rng.choice([1, 7, 60, 300]))
+    K = int(rng.choice([1, 3, 8, 32]))
+    E = int(rng.choice([1, 5, 16, 64]))
+    M = int(rng.choice([1, 3, max(1, N * K // max(E, 1))]))
+    H = int(rng.choice([128, 640, 1536]))
+    ids = rng.integers(-1, E + 2, size=(N, K)).astype(np.int32)
+    fmt = int(rng.integers(0, 3)) if H % 512 == 0 else int(rng.integers(0, 2))
+    say(f"fused random seed={seed} N={N} K={K} E={E} M={M} H={H} format={fmt}")
+    _fused_case(mg, ids, E, M, _x(rng, N, H), fmt, fmt == 2)
+
+
+def test_fused_padded_fp8_largest_and_empty(mg):
+    rng = np.random.default_rng(77)
+    N, K, E, H, M = 1024, 8, 64, 512, 100          # N*K = 8192, the limit; drops
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    say("fused largest batch")
+    _fused_case(mg, ids, E, M, _x(rng, N, H), 1, False)
+    say("fused empty batch")
+    _fused_case(mg, np.zeros((0, 8), np.int32), 16, 4, np.zeros((0, 256), np.uint16), 0, False)
+    with pytest.raises(mg.MoeError):
+        _fused_case(mg, np.zeros((1025, 8), np.int32), 16, 4, np.zeros((1025, 256), np.uint16), 0, False)
