@@ -22,22 +22,31 @@ def _expected(src, pos, rows, fill):
     return out
 
 
+# The first SAMPLE tokens of each workload (its routing and payload recipe,
+# at a size whose receive buffers stay small): the full sizes run in the
+# GPU parity tests, and the oracle's code path does not depend on N.
+SAMPLE = 512
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed"])
 def test_matches_fancy_indexing(orc, name):
     w = mw.make(name)
-    _, _, pos, _, _ = orc.layout(w.ids, w.E)
-    srcs = [a for _, a in w.fields]
+    n = min(w.N, SAMPLE)
+    ids = w.ids[:n]
+    _, _, pos, _, _ = orc.layout(ids, w.E)
+    srcs = [a[:n] for _, a in w.fields]
     dsts = orc.dispatch(srcs, pos, w.K, fill=0xA5)
     for s, d in zip(srcs, dsts):
-        assert np.array_equal(d, _expected(s, pos, w.N * w.K, 0xA5))
+        assert np.array_equal(d, _expected(s, pos, n * w.K, 0xA5))
 
 
 def test_large_records(orc):
     w = mw.make("large")
-    _, _, pos, row_pair, _ = orc.layout(w.ids, w.E)
-    (d,) = orc.dispatch([w.records], pos, w.K)
+    n = SAMPLE
+    _, _, pos, row_pair, _ = orc.layout(w.ids[:n], w.E)   # ids read in place from the records
+    (d,) = orc.dispatch([w.records[:n]], pos, w.K)
     # row r holds the record of token row_pair[r] // K
-    assert np.array_equal(d, w.records[row_pair // w.K])
+    assert np.array_equal(d, w.records[:n][row_pair // w.K])
 
 
 @pytest.mark.parametrize("seed", range(10))
