@@ -275,3 +275,15 @@ def test_builder_loads_without_the_package():
     assert r.returncode == 0, r.stderr
     src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
     assert "spec_from_file_location" in src and "from combine_moe_get_amd import build" not in src
+
+
+def test_c_program_builds_against_the_header(tmp_path):
+    """The C ABI check program (tests/c_abi) compiles and links from plain C
+    against the header, the library and the oracle."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("cb", os.path.join(ROOT, "tests", "c_abi", "build.py"))
+    cb = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(cb)
+    out = cb.build(str(tmp_path / "abi_check"))
+    assert os.path.exists(out)
