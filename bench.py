@@ -71,6 +71,7 @@ KERNEL_SOURCES = {
     "dispatch_fp8_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
     "combine_backward_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
     "dispatch_fp8_padded_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
+    "layout_dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
@@ -202,8 +203,9 @@ class HipEvents:
 class BufferSet:
     """Device inputs and outputs of one step."""
 
-    def __init__(self, torch, mg, wl, y_bits):
+    def __init__(self, torch, mg, wl, y_bits, fused=False):
         d = "cuda"
+        self.fused = fused
         if wl.records is not None:
             # record mode: one 16-B-aligned record per token moves whole; the
             # ids and weights are read in place from inside the records
@@ -245,6 +247,13 @@ class BufferSet:
                self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap, self.ws.data_ptr(),
                self.ws.numel(), self.status.data_ptr(), stream)
         dis = (fields, len(self.srcs), N, K, self.pos.data_ptr(), stream)
+        if self.fused:
+            ld = (self.ids.data_ptr(), self.ids_stride, N, K, E, 1, self.counts.data_ptr(),
+                  self.offsets.data_ptr(), self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap,
+                  self.status.data_ptr(), fields, len(self.srcs), stream)
+            com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), self.w_stride, self.pos.data_ptr(),
+                   N, K, wl.Hc, self.out.data_ptr(), wl.Hc, stream)
+            return (L.moe_layout_dispatch, ld), (L.moe_combine, com)
         if not epilogue:
             com = (self.y.data_ptr(), wl.Hc, self.w.data_ptr(), self.w_stride, self.pos.data_ptr(),
                    N, K, wl.Hc, self.out.data_ptr(), wl.Hc, stream)
@@ -524,8 +533,8 @@ def main():
     ap.add_argument("--round-scale", action="store_true",
                     help="--lowlatency: round scales up to powers of two (implied by ue8m0)")
     ap.add_argument("--fused", action="store_true",
-                    help="--lowlatency: the padded layout and the FP8 dispatch in one launch "
-                         "(moe_dispatch_fp8_padded; N*K <= 8192)")
+                    help="layout and dispatch in one launch for small batches (N*K <= 8192): "
+                         "moe_layout_dispatch, or with --lowlatency moe_dispatch_fp8_padded")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward instead: combine backward (grad_y, grad_w) + "
                          "dispatch backward (grad_x, weight gradients) on the forward's layout")
@@ -544,8 +553,8 @@ def main():
         return
     if args.lowlatency + args.epilogue + args.backward > 1:
         raise SystemExit("--lowlatency, --epilogue and --backward are separate measurements")
-    if args.fused and not args.lowlatency:
-        raise SystemExit("--fused is a form of --lowlatency")
+    if args.fused and (args.epilogue or args.backward):
+        raise SystemExit("--fused applies to the plain and the low-latency step")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -590,11 +599,15 @@ def main():
         kernels = {"combine_backward": "combine_backward_kernel",
                    "dispatch_backward": "combine_kernel"}
     else:
-        sets = [BufferSet(torch, mg, wl, y) for _ in range(max(1, args.sets))]
+        sets = [BufferSet(torch, mg, wl, y, args.fused) for _ in range(max(1, args.sets))]
         names = ("layout", "dispatch", "combine")
         op_bytes = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
         kernels = {"dispatch": "dispatch_kernel",
                    "combine": "combine_epilogue_kernel" if args.epilogue else "combine_kernel"}
+        if args.fused:
+            names = ("layout+dispatch", "combine")
+            op_bytes = (op_bytes[0] + op_bytes[1], op_bytes[2])
+            kernels = {"layout+dispatch": "layout_dispatch_kernel", "combine": "combine_kernel"}
     nops = len(names)
     stream = torch.cuda.current_stream()
     calls = [s.calls(mg, wl, stream.cuda_stream, args.epilogue) for s in sets]
@@ -696,7 +709,8 @@ def main():
         metric = ("combine backward + dispatch backward effective HBM GB/s and tokens/s, "
                   f"{N}×7168 top-{K}, 1 GPU")
     else:
-        workload = (f"{args.config}: N={N} tokens, top-{K} of {E} experts, dispatch payload "
+        workload = (f"{args.config}{' (layout and dispatch fused)' if args.fused else ''}: "
+                    f"N={N} tokens, top-{K} of {E} experts, dispatch payload "
                     f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields) or 'one record: ids, weights, 3584 B hidden, 448 B scales; ids and weights read in place'}), "
                     f"combine bf16 hidden {Hc}, fp32 accumulation"
                     + (", fused residual add + RMSNorm epilogue" if args.epilogue else ""))

@@ -83,6 +83,9 @@ def _load():
     L.moe_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32,
                                        ctypes.POINTER(moe_epilogue), P, i64, P]
     L.moe_combine_epilogue.restype = ctypes.c_int
+    L.moe_layout_dispatch.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P,
+                                      ctypes.POINTER(moe_field), i32, P]
+    L.moe_layout_dispatch.restype = ctypes.c_int
     L.moe_dispatch_fp8_padded.argtypes = [P, i64, i32, i32, i32, i32, P, i64, i32, P, P, P, P, P,
                                           i64, P, i32, i64, i32, P]
     L.moe_dispatch_fp8_padded.restype = ctypes.c_int
@@ -242,9 +245,18 @@ def moe_dispatch(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor],
 
     ``pos=None`` is the identity (K must be 1). Tensors are 2-D with
     contiguous rows; each field's row size in bytes must match."""
+    N = srcs[0].shape[0] if len(srcs) else 0
+    arr = _fields(srcs, dsts, N)
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()
+                            or pos.numel() != N * K):
+        raise ValueError("pos must be a contiguous int32 [N, K] tensor")
+    _check(_lib.moe_dispatch(arr, len(srcs), N, K, _dev(pos, "pos"), _stream(stream)))
+
+
+def _fields(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor], N: int):
+    """moe_field array of matching source [N, ...] / destination tensors."""
     if len(srcs) != len(dsts) or not 1 <= len(srcs) <= MAX_FIELDS:
         raise ValueError("need 1..4 matching source / destination fields")
-    N = srcs[0].shape[0]
     arr = (moe_field * len(srcs))()
     for i, (s, d) in enumerate(zip(srcs, dsts)):
         if s.shape[0] != N:
@@ -254,10 +266,7 @@ def moe_dispatch(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor],
         if sb != db:
             raise ValueError(f"field {i}: source rows {sb} B, destination rows {db} B")
         arr[i] = moe_field(sp, ss, dp, ds, sb)
-    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()
-                            or pos.numel() != N * K):
-        raise ValueError("pos must be a contiguous int32 [N, K] tensor")
-    _check(_lib.moe_dispatch(arr, len(srcs), N, K, _dev(pos, "pos"), _stream(stream)))
+    return arr
 
 
 def moe_combine(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor, out: torch.Tensor,
@@ -278,6 +287,29 @@ def moe_combine(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tensor, out: 
     op, os_ = _rows(out, "out") if N else (0, Hc)
     _check(_lib.moe_combine(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc, op, os_,
                             _stream(stream)))
+
+
+def moe_layout_dispatch(ids: torch.Tensor, num_experts: int, align: int, counts: torch.Tensor,
+                        offsets: torch.Tensor, pos: torch.Tensor, row_pair: torch.Tensor,
+                        status: Optional[torch.Tensor], srcs: Sequence[torch.Tensor],
+                        dsts: Sequence[torch.Tensor], stream=None) -> None:
+    """moe_get_layout + moe_dispatch in one launch (N*K <= 8192)."""
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise TypeError("ids must be int32 [N, K]")
+    N, K = ids.shape
+    for t, n in ((counts, "counts"), (offsets, "offsets"), (pos, "pos"), (row_pair, "row_pair")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
+        raise TypeError("status must be an int32 tensor")
+    if counts.numel() < num_experts or offsets.numel() < num_experts + 1 or pos.numel() != N * K:
+        raise ValueError("counts, offsets or pos too small")
+    fields = _fields(srcs, dsts, N)
+    ip, istr = _rows(ids, "ids") if N else (0, K)
+    _check(_lib.moe_layout_dispatch(ip, istr, N, K, num_experts, align, _dev(counts, "counts"),
+                                    _dev(offsets, "offsets"), _dev(pos, "pos"),
+                                    _dev(row_pair, "row_pair"), row_pair.numel(),
+                                    _dev(status, "status"), fields, len(srcs), _stream(stream)))
 
 
 def moe_dispatch_fp8_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: int,

@@ -15,8 +15,9 @@
 // Workgroups are handed to the 8 XCDs round-robin, each XCD with its own L2,
 // so the kernel renumbers them: XCD x runs the x-th contiguous eighth of the
 // work, which keeps all waves of a token on one XCD and its re-reads in that
-// L2 (without this, measured source reads were 4x the source bytes). Every load and store instruction of a wave covers
-// 64 consecutive vectors of one row (1 KiB with 16-byte vectors). Measured
+// L2 (without this, measured source reads were 4x the source bytes). Every
+// load and store instruction of a wave covers 64 consecutive vectors of one
+// row (1 KiB with 16-byte vectors). Measured
 // on MI355X at the prefill shape, this many-short-waves form writes faster
 // than one wave storing each loaded vector K times, and only with
 // non-temporal stores.
@@ -76,39 +77,202 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a
     __builtin_nontemporal_store(val, reinterpret_cast<VecT*>(dst + (int64_t)p * ds + inner));
 }
 
+// ---------------------------------------------------------------------------
+// Layout and dispatch in one launch, for small batches (N*K <= 8192). The
+// row of pair (t, k) with expert e is offsets[e] + r, r the number of
+// earlier pairs in (t, k) order with expert e; offsets is the exclusive scan
+// of the aligned per-expert totals. Both come from one pass over the batch's
+// ids, cheap enough at this size for every workgroup to make it itself.
+// Workgroup (t, g) takes token t and the 64-vector segments 4g .. 4g+3 of its
+// concatenated fields (one per wave):
+//   1. its segment loads are issued first; then one pass over all ids gives
+//      the per-expert totals (LDS integer atomics: order-independent), the
+//      out-of-range count and the matches of the token's K experts among
+//      earlier tokens;
+//   2. the offsets: an exclusive scan of the aligned totals over E <= 1024;
+//   3. the token's rows; workgroup (t, 0) writes pos and row_pair, workgroup
+//      0 counts, offsets and status, and the unused rows (alignment padding
+//      of expert e by workgroup e mod grid, rows past the used ones by all)
+//      are marked -1 -- used and unused rows are disjoint sets derived from
+//      the same totals;
+//   4. each wave stores its vectors to the K rows (non-temporal).
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedMaxPairs = 8192;
+
+struct FusedLayout {
+    const int32_t* ids;
+    int64_t ids_stride;
+    int32_t E, align, groups;
+    int64_t cap;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* pos;
+    int32_t* row_pair;
+    int32_t* status;
+};
+
+template <typename VecT>
+__global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const DispatchArgs a,
+                                                                   const FusedLayout f) {
+    __shared__ int32_t tot[MOE_MAX_EXPERTS];
+    __shared__ int32_t off[MOE_MAX_EXPERTS + 1];
+    __shared__ int32_t hits[MOE_MAX_TOPK];
+    __shared__ int32_t rows[MOE_MAX_TOPK];
+    __shared__ int32_t tok_e[MOE_MAX_TOPK];
+    __shared__ int32_t wave_sums[kWavesPerBlock];
+    __shared__ int32_t nbad_s;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const uint32_t t = blockIdx.x / (uint32_t)f.groups;
+    const int32_t g = (int32_t)(blockIdx.x - t * (uint32_t)f.groups);
+    const int32_t K = a.K, E = f.E;
+    const int32_t nk = a.N * K;
+    const bool has_token = t < (uint32_t)a.N;   // N = 0: one workgroup, layout outputs only
+
+    // 1. this wave's vector of the token's payload, loaded before the count
+    const int32_t seg = g * kWavesPerBlock + wave;
+    const int32_t v = seg * kWave + lane;
+    const bool moves = has_token && v < a.V;
+    const int f1 = v >= a.vend[0], f2 = v >= a.vend[1], f3 = v >= a.vend[2];
+    const char* src = f3 ? a.src[3] : f2 ? a.src[2] : f1 ? a.src[1] : a.src[0];
+    char* dst = f3 ? a.dst[3] : f2 ? a.dst[2] : f1 ? a.dst[1] : a.dst[0];
+    const int64_t ss = f3 ? a.sstride[3] : f2 ? a.sstride[2] : f1 ? a.sstride[1] : a.sstride[0];
+    const int64_t ds = f3 ? a.dstride[3] : f2 ? a.dstride[2] : f1 ? a.dstride[1] : a.dstride[0];
+    const int32_t v0 = f3 ? a.vend[2] : f2 ? a.vend[1] : f1 ? a.vend[0] : 0;
+    const int64_t inner = (int64_t)(v - v0) * sizeof(VecT);
+    VecT val{};
+    if (moves) val = *reinterpret_cast<const VecT*>(src + (int64_t)t * ss + inner);
+
+    for (int e = threadIdx.x; e < E; e += kThreads) tot[e] = 0;
+    if (threadIdx.x < MOE_MAX_TOPK) hits[threadIdx.x] = 0;
+    if ((int32_t)threadIdx.x < K)
+        tok_e[threadIdx.x] = has_token ? f.ids[(int64_t)t * f.ids_stride + threadIdx.x] : -1;
+    if (threadIdx.x == 0) nbad_s = 0;
+    __syncthreads();
+
+    const int32_t before = (int32_t)t * K;
+    int32_t nbad = 0;
+    for (int32_t i = threadIdx.x; i < nk; i += kThreads) {
+        const int32_t ti = i / K;
+        const int32_t e = f.ids[(int64_t)ti * f.ids_stride + (i - ti * K)];
+        if (e >= E) {
+            ++nbad;
+        } else if (e >= 0) {
+            atomicAdd(&tot[e], 1);
+            if (i < before)
+                for (int32_t k = 0; k < K; ++k)
+                    if (e == tok_e[k]) atomicAdd(&hits[k], 1);
+        }
+    }
+    if (nbad) atomicAdd(&nbad_s, nbad);
+    __syncthreads();
+
+    // 2. offsets: thread i scans experts 4i .. 4i+3 (E <= 1024)
+    int32_t mine[4], sum4 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = threadIdx.x * 4 + j;
+        const int32_t c = e < E ? tot[e] : 0;
+        mine[j] = (int32_t)(((int64_t)c + f.align - 1) / f.align * f.align);
+        sum4 += mine[j];
+    }
+    int32_t x = sum4;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    int32_t run = x - sum4, used = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        run += w < wave ? wave_sums[w] : 0;
+        used += wave_sums[w];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = threadIdx.x * 4 + j;
+        if (e < E) off[e] = run;
+        run += mine[j];
+    }
+    if (threadIdx.x == 0) off[E] = used;
+    __syncthreads();
+
+    // 3. rows of the token's pairs; layout outputs
+    if (has_token && (int32_t)threadIdx.x < K) {
+        const int32_t k = threadIdx.x;
+        const int32_t e = tok_e[k];
+        int32_t p = -1;
+        if (e >= 0 && e < E) {
+            int32_t r = hits[k];
+            for (int32_t j = 0; j < k; ++j) r += tok_e[j] == e;
+            p = off[e] + r;
+        }
+        rows[k] = p;
+        if (g == 0) {
+            f.pos[(int64_t)t * K + k] = p;
+            if (p >= 0) f.row_pair[p] = (int32_t)t * K + k;
+        }
+    }
+    if (blockIdx.x == 0) {
+        for (int e = threadIdx.x; e < E; e += kThreads) {
+            f.counts[e] = tot[e];
+            f.offsets[e] = off[e];
+        }
+        if (threadIdx.x == 0) {
+            f.offsets[E] = used;
+            if (f.status != nullptr) f.status[0] = nbad_s;
+        }
+    }
+    const uint32_t B = gridDim.x;
+    if (f.align > 1)
+        for (int32_t e = blockIdx.x; e < E; e += (int32_t)B)
+            for (int32_t r = off[e] + tot[e] + threadIdx.x; r < off[e + 1]; r += kThreads)
+                f.row_pair[r] = -1;
+    for (int64_t r = used + (int64_t)blockIdx.x * kThreads + threadIdx.x; r < f.cap;
+         r += (int64_t)B * kThreads)
+        f.row_pair[r] = -1;
+    __syncthreads();
+
+    // 4. the token's vectors to its K rows
+    if (!moves) return;
+    for (int32_t k = 0; k < K; ++k) {
+        const int32_t p = rows[k];
+        if (p >= 0)
+            __builtin_nontemporal_store(val, reinterpret_cast<VecT*>(dst + (int64_t)p * ds + inner));
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
 
-extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N, int32_t K,
-                            const int32_t* pos, hipStream_t stream) {
+// Validates the payload fields and fills a's field tables (vector ends in
+// units of 16 or 4 bytes, *all16 says which). Returns MOE_OK or an error set
+// through fail() with `who` as its prefix.
+static int prepare_fields(const moe_field* fields, int32_t nfields, int32_t N, DispatchArgs& a,
+                          bool* all16_out, int64_t* total_out, const char* who) {
     if (fields == nullptr || nfields < 1 || nfields > MOE_MAX_FIELDS)
-        return fail(MOE_ERR_ARG, "moe_dispatch: need 1..%d fields (got %d%s)", MOE_MAX_FIELDS,
+        return fail(MOE_ERR_ARG, "%s: need 1..%d fields (got %d%s)", who, MOE_MAX_FIELDS,
                     nfields, fields ? "" : ", NULL array");
-    if (N < 0 || K < 1) return fail(MOE_ERR_ARG, "moe_dispatch: need N >= 0, K >= 1");
-    if (K > MOE_MAX_TOPK) return fail(MOE_ERR_LIMIT, "moe_dispatch: K=%d > %d", K, MOE_MAX_TOPK);
-    if ((int64_t)N * K >= ((int64_t)1 << 31))
-        return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K must be below 2^31");
-    if (pos == nullptr && K != 1 && N > 0)
-        return fail(MOE_ERR_ARG, "moe_dispatch: pos == NULL (identity) requires K == 1");
-    if (!aligned(pos, 4)) return fail(MOE_ERR_ALIGN, "moe_dispatch: pos must be 4-byte aligned");
-
     bool all16 = true;
     int64_t total_bytes = 0;
     for (int f = 0; f < nfields; ++f) {
         const moe_field& d = fields[f];
-        if (d.row_bytes < 0) return fail(MOE_ERR_ARG, "moe_dispatch: field %d row_bytes < 0", f);
+        if (d.row_bytes < 0) return fail(MOE_ERR_ARG, "%s: field %d row_bytes < 0", who, f);
         if (d.row_bytes > 0 && N > 0 && (d.src == nullptr || d.dst == nullptr))
-            return fail(MOE_ERR_ARG, "moe_dispatch: field %d has a NULL pointer", f);
+            return fail(MOE_ERR_ARG, "%s: field %d has a NULL pointer", who, f);
         if (!aligned(d.src, 4) || !aligned(d.dst, 4) || !aligned(d.src_row_stride, 4) ||
             !aligned(d.dst_row_stride, 4) || !aligned(d.row_bytes, 4))
-            return fail(MOE_ERR_ALIGN, "moe_dispatch: field %d pointers, strides and row_bytes "
-                        "must be multiples of 4 bytes", f);
+            return fail(MOE_ERR_ALIGN, "%s: field %d pointers, strides and row_bytes must be "
+                        "multiples of 4 bytes", who, f);
         if (N > 1 && d.src_row_stride < d.row_bytes)
-            return fail(MOE_ERR_ARG, "moe_dispatch: field %d src_row_stride < row_bytes", f);
+            return fail(MOE_ERR_ARG, "%s: field %d src_row_stride < row_bytes", who, f);
         if (d.dst_row_stride < d.row_bytes)
-            return fail(MOE_ERR_ARG, "moe_dispatch: field %d dst_row_stride < row_bytes", f);
+            return fail(MOE_ERR_ARG, "%s: field %d dst_row_stride < row_bytes", who, f);
         all16 = all16 && aligned(d.src, 16) && aligned(d.dst, 16) &&
                 aligned(d.src_row_stride, 16) && aligned(d.dst_row_stride, 16) &&
                 aligned(d.row_bytes, 16);
@@ -116,11 +280,8 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     }
     const int vb = all16 ? 16 : 4;
     if (total_bytes / vb >= ((int64_t)1 << 30))
-        return fail(MOE_ERR_LIMIT, "moe_dispatch: %lld payload bytes per token is too large",
+        return fail(MOE_ERR_LIMIT, "%s: %lld payload bytes per token is too large", who,
                     (long long)total_bytes);
-    if (N == 0 || total_bytes == 0) return ok();
-
-    DispatchArgs a{};
     int32_t vend = 0;
     for (int f = 0; f < MOE_MAX_FIELDS; ++f) {
         if (f < nfields) {
@@ -132,11 +293,31 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
         }
         a.vend[f] = vend;
     }
+    a.V = vend;
+    a.segs = ceil_div<int32_t>(vend, kWave);
+    *all16_out = all16;
+    *total_out = total_bytes;
+    return MOE_OK;
+}
+
+extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N, int32_t K,
+                            const int32_t* pos, hipStream_t stream) {
+    if (N < 0 || K < 1) return fail(MOE_ERR_ARG, "moe_dispatch: need N >= 0, K >= 1");
+    if (K > MOE_MAX_TOPK) return fail(MOE_ERR_LIMIT, "moe_dispatch: K=%d > %d", K, MOE_MAX_TOPK);
+    if ((int64_t)N * K >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K must be below 2^31");
+    if (pos == nullptr && K != 1 && N > 0)
+        return fail(MOE_ERR_ARG, "moe_dispatch: pos == NULL (identity) requires K == 1");
+    if (!aligned(pos, 4)) return fail(MOE_ERR_ALIGN, "moe_dispatch: pos must be 4-byte aligned");
+    DispatchArgs a{};
+    bool all16 = true;
+    int64_t total_bytes = 0;
+    const int rc = prepare_fields(fields, nfields, N, a, &all16, &total_bytes, "moe_dispatch");
+    if (rc != MOE_OK) return rc;
+    if (N == 0 || total_bytes == 0) return ok();
     a.pos = pos;
     a.N = N;
     a.K = K;
-    a.V = vend;
-    a.segs = ceil_div<int32_t>(vend, kWave);
     const int64_t waves = (int64_t)N * K * a.segs;
     if (waves >= ((int64_t)1 << 31))
         return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K*segments=%lld waves must be below 2^31",
@@ -148,4 +329,63 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     else
         dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a);
     return check_launch("moe_dispatch");
+}
+
+extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N,
+                                   int32_t K, int32_t E, int32_t align, int32_t* counts,
+                                   int32_t* offsets, int32_t* pos, int32_t* row_pair, int64_t cap,
+                                   int32_t* status, const moe_field* fields, int32_t nfields,
+                                   hipStream_t stream) {
+    if (N < 0 || K < 1 || E < 1 || align < 1)
+        return fail(MOE_ERR_ARG, "moe_layout_dispatch: need N >= 0, K >= 1, E >= 1, align >= 1");
+    if (K > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_LIMIT, "moe_layout_dispatch: K=%d E=%d beyond K <= %d, E <= %d", K, E,
+                    MOE_MAX_TOPK, MOE_MAX_EXPERTS);
+    if ((int64_t)N * K > kFusedMaxPairs)
+        return fail(MOE_ERR_LIMIT, "moe_layout_dispatch: N*K=%lld above %d (use moe_get_layout + "
+                    "moe_dispatch)", (long long)N * K, kFusedMaxPairs);
+    const int64_t need = moe_required_capacity(N, K, E, align);
+    if (cap < need)
+        return fail(MOE_ERR_CAPACITY, "moe_layout_dispatch: cap=%lld below the worst case %lld",
+                    (long long)cap, (long long)need);
+    if (cap >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_layout_dispatch: cap must be below 2^31");
+    if (counts == nullptr || offsets == nullptr || (cap > 0 && row_pair == nullptr))
+        return fail(MOE_ERR_ARG, "moe_layout_dispatch: counts, offsets and row_pair must not be "
+                    "NULL");
+    if (N > 0 && (ids == nullptr || pos == nullptr || ids_row_stride < K))
+        return fail(MOE_ERR_ARG, "moe_layout_dispatch: NULL ids/pos or ids_row_stride < K");
+    if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pos, 4) ||
+        !aligned(row_pair, 4) || !aligned(status, 4))
+        return fail(MOE_ERR_ALIGN, "moe_layout_dispatch: int32 pointers must be 4-byte aligned");
+    DispatchArgs a{};
+    bool all16 = true;
+    int64_t total_bytes = 0;
+    const int rc = prepare_fields(fields, nfields, N, a, &all16, &total_bytes,
+                                  "moe_layout_dispatch");
+    if (rc != MOE_OK) return rc;
+    a.pos = nullptr;
+    a.N = N;
+    a.K = K;
+    FusedLayout f;
+    f.ids = ids;
+    f.ids_stride = ids_row_stride;
+    f.E = E;
+    f.align = align;
+    f.groups = a.segs > 0 ? ceil_div<int32_t>(a.segs, kWavesPerBlock) : 1;
+    f.cap = cap;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.pos = pos;
+    f.row_pair = row_pair;
+    f.status = status;
+    // N = 0 still runs one workgroup: counts, offsets, status and row_pair
+    // are outputs.
+    const int64_t blocks = N > 0 ? (int64_t)N * f.groups : 1;
+    clear_launch_error();
+    if (all16)
+        layout_dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
+    else
+        layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
+    return check_launch("moe_layout_dispatch");
 }

@@ -285,6 +285,28 @@ int moe_combine_epilogue(const void* y, int64_t y_row_stride, const float* w,
                          hipStream_t stream);
 
 /*
+ * Layout and dispatch in one launch, for small (decode-sized) batches: the
+ * same results as moe_get_layout(ids, ..., E, align, counts, offsets, pos,
+ * row_pair, cap, ..., status) followed by moe_dispatch(fields, nfields, N, K,
+ * pos), bit for bit, without the layout's workspace. Every workgroup derives
+ * the offsets and its token's rows from one pass over the batch's ids, so the
+ * three launches of the two calls become one. Cited passages: those of
+ * moe_get_layout and moe_dispatch (DeepEP repository dump, deep_ep.cpp,
+ * Buffer::get_dispatch_layout, Buffer::intranode_dispatch).
+ *
+ * Arguments, layouts and alignment are those of the two calls (status may be
+ * NULL). counts, offsets and row_pair are written even when N = 0. Limits:
+ * N*K <= 8192 (larger batches: the two calls), 1 <= K <= 32,
+ * 1 <= E <= 1024, cap >= moe_required_capacity(N, K, E, align), cap < 2^31.
+ * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT, MOE_ERR_CAPACITY,
+ * MOE_ERR_HIP.
+ */
+int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                        int32_t E, int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
+                        int32_t* row_pair, int64_t cap, int32_t* status, const moe_field* fields,
+                        int32_t nfields, hipStream_t stream);
+
+/*
  * Padded layout and FP8 dispatch in one launch, for small (decode-sized)
  * batches: the same results as moe_get_layout_padded(ids, ..., E, M, counts,
  * pos, row_pair, ..., status) followed by moe_dispatch_fp8(x, ..., pos, dst,

@@ -287,3 +287,19 @@ def test_c_program_builds_against_the_header(tmp_path):
     spec.loader.exec_module(cb)
     out = cb.build(str(tmp_path / "abi_check"))
     assert os.path.exists(out)
+
+
+def test_layout_dispatch_validation(lib):
+    F = lib._lib.moe_layout_dispatch
+    P = 0x10000
+    fld = (lib.moe_field * 1)(lib.moe_field(P, 64, P, 64, 64))
+    # (ids, istr, N, K, E, align, counts, offsets, pos, row_pair, cap, status, fields, nf, stream)
+    assert F(P, 8, 1025, 8, 64, 1, P, P, P, P, 8200, P, fld, 1, 0) == lib.MOE_ERR_LIMIT   # N*K > 8192
+    assert F(P, 8, 16, 8, 64, 1, P, P, P, P, 100, P, fld, 1, 0) == lib.MOE_ERR_CAPACITY
+    assert F(P, 8, 16, 8, 1025, 1, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_LIMIT
+    assert F(P, 8, 16, 8, 64, 0, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_ARG       # align 0
+    assert F(P, 4, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_ARG       # ids stride
+    assert F(P + 2, 8, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_ALIGN
+    assert F(P, 8, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 0, 0) == lib.MOE_ERR_ARG       # no fields
+    bad = (lib.moe_field * 1)(lib.moe_field(P + 2, 64, P, 64, 64))
+    assert F(P, 8, 16, 8, 64, 1, P, P, P, P, 128, P, bad, 1, 0) == lib.MOE_ERR_ALIGN

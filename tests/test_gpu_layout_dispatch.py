@@ -1,0 +1,99 @@
+"""GPU parity of moe_layout_dispatch (layout and dispatch in one launch for
+batches of at most 8192 pairs) against the oracle's layout followed by its
+dispatch. Bar: every output bit-exact; rows past the used ones and alignment
+padding keep their canary bytes in the receive buffers and -1 in row_pair."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_moe_get_amd as m
+
+    return m
+
+
+def say(msg):
+    print(f"[gpu-layout-dispatch] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check(mg, ids, E, align, srcs, cap=None, ids_view=None, fill=0xC3):
+    """ids: int32 [N, K] (the GPU reads ids_view when given: a strided
+    device view); srcs: uint8 [N, bytes] fields."""
+    N, K = ids.shape
+    if cap is None:
+        cap = max(oracle.required_cap(N, K, E, align), 0)
+    counts = torch.full((E,), -9, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -9, dtype=torch.int32, device="cuda")
+    pos = torch.full((N, K), -9, dtype=torch.int32, device="cuda")
+    row_pair = torch.full((cap,), -9, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    d_srcs = [dev(s) for s in srcs]
+    d_dsts = [torch.full((cap, s.shape[1]), fill, dtype=torch.uint8, device="cuda") for s in srcs]
+    mg.moe_layout_dispatch(dev(ids) if ids_view is None else ids_view, E, align, counts, offsets,
+                           pos, row_pair, status, d_srcs, d_dsts)
+    torch.cuda.synchronize()
+    c, o, p, rp, st = oracle.layout(ids, E, align, cap=cap)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(pos.cpu().numpy(), p)
+    assert np.array_equal(row_pair.cpu().numpy(), rp)
+    assert int(status.cpu()[0]) == st
+    for r, d in zip(oracle.dispatch(srcs, p, K, rows=cap, fill=fill), d_dsts):
+        assert np.array_equal(d.cpu().numpy(), r)
+
+
+def test_decode_workload(mg):
+    wl = mw.make("decode")
+    say("decode workload")
+    check(mg, wl.ids, wl.E, 1, [a for _, a in wl.fields])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random(mg, seed):
+    """Masks, out-of-range and repeated ids, align > 1, spare capacity, the
+    4-byte and 16-byte payload paths."""
+    rng = np.random.default_rng(600 + seed)
+    N = int(rng.choice([1, 9, 64, 200, 1024]))
+    K = int(rng.choice([1, 2, 8, 8]))
+    E = int(rng.choice([1, 7, 64, 256, 1024]))
+    align = int(rng.choice([1, 1, 4, 16]))
+    ids = rng.integers(-1, E + 2, size=(N, K)).astype(np.int32)
+    sizes = (96, 16, 32) if seed % 3 else (20, 8, 4 * K)        # 16-byte or 4-byte path
+    srcs = [rng.integers(0, 256, size=(N, b), dtype=np.uint8) for b in sizes]
+    cap = oracle.required_cap(N, K, E, align) + int(rng.integers(0, 40))
+    say(f"random seed={seed} N={N} K={K} E={E} align={align} sizes={sizes}")
+    check(mg, ids, E, align, srcs, cap=cap)
+
+
+def test_records_with_ids_read_in_place(mg):
+    """Record mode: one 4096-byte field per token, the ids read from inside
+    the records (row stride 1024 int32)."""
+    wl = mw.make("large")
+    n = 1024                                      # N*K = 8192, the limit
+    rec = np.ascontiguousarray(wl.records[:n])
+    d_rec = dev(rec)
+    ids_view = d_rec.view(torch.int32)[:, :wl.K]
+    say("records, ids in place")
+    check(mg, wl.ids[:n].copy(), wl.E, 1, [rec], ids_view=ids_view)
+
+
+def test_empty_and_limit(mg):
+    say("empty batch")
+    check(mg, np.zeros((0, 8), np.int32), 32, 4, [np.zeros((0, 64), np.uint8)], cap=100)
+    with pytest.raises(mg.MoeError):
+        check(mg, np.zeros((1025, 8), np.int32), 32, 1, [np.zeros((1025, 64), np.uint8)])
