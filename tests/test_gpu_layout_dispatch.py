@@ -97,3 +97,64 @@ def test_empty_and_limit(mg):
     check(mg, np.zeros((0, 8), np.int32), 32, 4, [np.zeros((0, 64), np.uint8)], cap=100)
     with pytest.raises(mg.MoeError):
         check(mg, np.zeros((1025, 8), np.int32), 32, 1, [np.zeros((1025, 64), np.uint8)])
+
+
+def test_graph_capture_of_the_one_launch_forms(mg):
+    """moe_layout_dispatch -> combine and moe_dispatch_fp8_padded captured
+    once and replayed on new inputs (eager work and a synchronization between
+    replays); every replay equals the eager calls on the same inputs."""
+    N, K, E, H, M, P = 100, 8, 32, 512, 60, 256
+    cap = oracle.required_cap(N, K, E, 4)
+    ids_s = torch.zeros((N, K), dtype=torch.int32, device="cuda")
+    src_s = torch.zeros((N, P), dtype=torch.uint8, device="cuda")
+    x_s = torch.zeros((N, H), dtype=torch.bfloat16, device="cuda")
+    w_s = torch.zeros((N, K), dtype=torch.float32, device="cuda")
+    y_s = torch.zeros((cap, 64), dtype=torch.bfloat16, device="cuda")
+
+    def buffers():
+        i32 = lambda *s: torch.zeros(s, dtype=torch.int32, device="cuda")
+        return dict(counts=i32(E), offsets=i32(E + 1), pos=i32(N, K), row_pair=i32(cap),
+                    status=i32(1), recv=torch.zeros((cap, P), dtype=torch.uint8, device="cuda"),
+                    out=torch.zeros((N, 64), dtype=torch.bfloat16, device="cuda"),
+                    pcounts=i32(E), ppos=i32(N, K), prow_pair=i32(E * M), pstatus=i32(2),
+                    codes=torch.zeros((E * M, H), dtype=torch.uint8, device="cuda"),
+                    scales=torch.zeros((E, H // 512, M), dtype=torch.int32, device="cuda"))
+
+    def step(b):
+        mg.moe_layout_dispatch(ids_s, E, 4, b["counts"], b["offsets"], b["pos"], b["row_pair"],
+                               b["status"], [src_s], [b["recv"]])
+        mg.moe_combine(y_s, w_s, b["pos"], b["out"])
+        mg.moe_dispatch_fp8_padded(ids_s, E, M, x_s, b["pcounts"], b["ppos"], b["prow_pair"],
+                                   b["pstatus"], b["codes"], b["scales"], mg.MOE_SCALE_UE8M0, True)
+
+    gb = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(gb)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(gb)
+    for rep in range(4):
+        say(f"graph replay {rep}")
+        rng = np.random.default_rng(700 + rep)
+        ids = rng.integers(-1, E + 1, size=(N, K)).astype(np.int32)
+        ids_s.copy_(dev(ids))
+        src_s.copy_(dev(rng.integers(0, 256, size=(N, P), dtype=np.uint8)))
+        x_s.copy_(dev(mw.bf16_bits_from_f32(rng.standard_normal((N, H)).astype(np.float32)).view(np.int16)).view(torch.bfloat16))
+        w_s.copy_(dev(rng.standard_normal((N, K)).astype(np.float32)))
+        y_s.copy_(dev(mw.bf16_bits_from_f32(rng.standard_normal((cap, 64)).astype(np.float32)).view(np.int16)).view(torch.bfloat16))
+        for t in gb.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eb = buffers()
+        step(eb)
+        torch.cuda.synchronize()
+        for name in gb:
+            a, b = gb[name], eb[name]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), (rep, name)
