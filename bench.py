@@ -448,6 +448,12 @@ def _time_oracle(one, wl, total_bytes, budget_s, what):
         return float(np.median(times)), len(times)
 
     cores = int(oracle.lib().omp_get_max_threads())
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     t, n = run(budget_s)
     prev = oracle.set_threads(1)
     try:
@@ -459,6 +465,7 @@ def _time_oracle(one, wl, total_bytes, budget_s, what):
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
+        "cpu_model": cpu_model,
         "sample": f"{n} {what}, median {t * 1e3:.1f} ms/step, {wl.N / t:.0f} tokens/s",
         "single_thread": {"value": round(total_bytes / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
                           "sample": f"{n1} steps, median {t1 * 1e3:.1f} ms/step"},
@@ -510,7 +517,7 @@ def cpu_baseline_bwd(wl, host, total_bytes, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="prefill",
                     choices=["tiny", "decode", "prefill", "skewed", "large"])
