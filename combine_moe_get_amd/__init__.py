@@ -83,6 +83,12 @@ def _load():
     L.moe_combine_epilogue.argtypes = [P, i64, P, i64, P, i32, i32, i32,
                                        ctypes.POINTER(moe_epilogue), P, i64, P]
     L.moe_combine_epilogue.restype = ctypes.c_int
+    L.moe_record_offsets.argtypes = [P, i32, P]
+    L.moe_record_offsets.restype = i64
+    L.moe_pack_records.argtypes = [ctypes.POINTER(moe_field), i32, i32, P, i64, P]
+    L.moe_pack_records.restype = ctypes.c_int
+    L.moe_unpack_records.argtypes = [P, i64, i32, ctypes.POINTER(moe_field), i32, P]
+    L.moe_unpack_records.restype = ctypes.c_int
     L.moe_layout_dispatch.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P,
                                       ctypes.POINTER(moe_field), i32, P]
     L.moe_layout_dispatch.restype = ctypes.c_int
@@ -520,42 +526,57 @@ def combine(y: torch.Tensor, weights: torch.Tensor, lay: Layout,
 
 def record_offsets(row_bytes: Sequence[int]) -> Tuple[List[int], int]:
     """16-byte aligned offset of each field inside a per-token record and the
-    record size rounded up to 16 bytes (fields in the given order)."""
-    offs, cur = [], 0
-    for b in row_bytes:
-        cur = (cur + 15) & ~15
-        offs.append(cur)
-        cur += b
-    return offs, (cur + 15) & ~15
-
-
-def _field_views(records: torch.Tensor, tensors: Sequence[torch.Tensor]) -> List[torch.Tensor]:
-    offs, _ = record_offsets([t.shape[1] * t.element_size() for t in tensors])
-    return [records[:, o:o + t.shape[1] * t.element_size()] for o, t in zip(offs, tensors)]
+    record size rounded up to 16 bytes (fields in the given order), from the
+    library's moe_record_offsets."""
+    n = len(row_bytes)
+    rb = (ctypes.c_int64 * max(n, 1))(*row_bytes)
+    offs = (ctypes.c_int64 * max(n, 1))()
+    size = _lib.moe_record_offsets(rb, n, offs)
+    if size < 0:
+        _check(int(size))
+    return list(offs[:n]), int(size)
 
 
 def _bytes2d(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.uint8) if t.dim() == 2 else t.reshape(t.shape[0], -1).view(torch.uint8)
 
 
+def _record_fields(tensors: Sequence[torch.Tensor], as_src: bool):
+    arr = (moe_field * len(tensors))()
+    for i, t in enumerate(tensors):
+        p, s, b = _as_bytes2d(t, f"field {i}")
+        arr[i] = moe_field(p, s, 0, 0, b) if as_src else moe_field(0, 0, p, s, b)
+    return arr
+
+
 def pack_records(tensors: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
     """Pack per-token tensors (e.g. ids, weights, hidden, scales) into one
-    uint8 record per token, each field at a 16-byte aligned offset."""
+    uint8 record per token, each field at a 16-byte aligned offset
+    (moe_pack_records)."""
+    if not 1 <= len(tensors) <= MAX_FIELDS:
+        raise ValueError("need 1..4 tensors")
     N = tensors[0].shape[0]
     b = [_bytes2d(t) for t in tensors]
+    if any(x.shape[0] != N for x in b):
+        raise ValueError("all tensors need the same number of tokens")
     _, rec_bytes = record_offsets([x.shape[1] for x in b])
     rec = torch.zeros((N, rec_bytes), dtype=torch.uint8, device=tensors[0].device)
-    moe_dispatch(b, _field_views(rec, b), None, 1, stream)
+    _check(_lib.moe_pack_records(_record_fields(b, True), len(b), N, _dev(rec, "records"),
+                                 rec_bytes, _stream(stream)))
     return rec
 
 
 def unpack_records(records: torch.Tensor, like: Sequence[torch.Tensor],
                    stream=None) -> List[torch.Tensor]:
     """Inverse of ``pack_records``: tensors shaped like ``like`` (row count
-    taken from ``records``)."""
+    taken from ``records``; moe_unpack_records)."""
+    if not 1 <= len(like) <= MAX_FIELDS:
+        raise ValueError("need 1..4 tensors")
     N = records.shape[0]
     outs = [torch.empty((N,) + tuple(t.shape[1:]), dtype=t.dtype, device=records.device)
             for t in like]
     b = [_bytes2d(o) for o in outs]
-    moe_dispatch(_field_views(records, b), b, None, 1, stream)
+    rp, rs = _rows(records, "records") if N else (0, records.shape[1])
+    _check(_lib.moe_unpack_records(rp, rs, N, _record_fields(b, False), len(b),
+                                   _stream(stream)))
     return outs

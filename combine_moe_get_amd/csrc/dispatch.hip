@@ -389,3 +389,67 @@ extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, i
         layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
     return check_launch("moe_layout_dispatch");
 }
+
+extern "C" int64_t moe_record_offsets(const int64_t* row_bytes, int32_t nfields,
+                                      int64_t* offsets) {
+    if (row_bytes == nullptr || nfields < 1 || nfields > MOE_MAX_FIELDS)
+        return fail(MOE_ERR_ARG, "moe_record_offsets: need 1..%d fields", MOE_MAX_FIELDS);
+    int64_t cur = 0;
+    for (int f = 0; f < nfields; ++f) {
+        if (row_bytes[f] < 0 || row_bytes[f] % 4 != 0)
+            return fail(MOE_ERR_ARG, "moe_record_offsets: field %d row_bytes must be a "
+                        "non-negative multiple of 4", f);
+        cur = (cur + 15) / 16 * 16;
+        if (offsets != nullptr) offsets[f] = cur;
+        cur += row_bytes[f];
+    }
+    ok();
+    return (cur + 15) / 16 * 16;
+}
+
+// Pack and unpack are the identity dispatch (K = 1, pos = NULL) with one
+// side of every field redirected into the record buffer.
+static int record_fields(const moe_field* fields, int32_t nfields, const void* records,
+                         int64_t record_row_stride, bool pack, moe_field* out, const char* who) {
+    if (fields == nullptr || nfields < 1 || nfields > MOE_MAX_FIELDS)
+        return fail(MOE_ERR_ARG, "%s: need 1..%d fields", who, MOE_MAX_FIELDS);
+    int64_t rb[MOE_MAX_FIELDS], off[MOE_MAX_FIELDS];
+    for (int f = 0; f < nfields; ++f) rb[f] = fields[f].row_bytes;
+    const int64_t rec = moe_record_offsets(rb, nfields, off);
+    if (rec < 0) return (int)rec;
+    if (record_row_stride < rec)
+        return fail(MOE_ERR_ARG, "%s: record_row_stride=%lld below the record size %lld", who,
+                    (long long)record_row_stride, (long long)rec);
+    for (int f = 0; f < nfields; ++f) {
+        char* slot = static_cast<char*>(const_cast<void*>(records)) + off[f];
+        out[f] = fields[f];
+        if (pack) {
+            out[f].dst = slot;
+            out[f].dst_row_stride = record_row_stride;
+        } else {
+            out[f].src = slot;
+            out[f].src_row_stride = record_row_stride;
+        }
+    }
+    return MOE_OK;
+}
+
+extern "C" int moe_pack_records(const moe_field* fields, int32_t nfields, int32_t N,
+                                void* records, int64_t record_row_stride, hipStream_t stream) {
+    if (N > 0 && records == nullptr) return fail(MOE_ERR_ARG, "moe_pack_records: NULL records");
+    moe_field f[MOE_MAX_FIELDS];
+    const int rc = record_fields(fields, nfields, records, record_row_stride, true, f,
+                                 "moe_pack_records");
+    if (rc != MOE_OK) return rc;
+    return moe_dispatch(f, nfields, N, 1, nullptr, stream);
+}
+
+extern "C" int moe_unpack_records(const void* records, int64_t record_row_stride, int32_t N,
+                                  const moe_field* fields, int32_t nfields, hipStream_t stream) {
+    if (N > 0 && records == nullptr) return fail(MOE_ERR_ARG, "moe_unpack_records: NULL records");
+    moe_field f[MOE_MAX_FIELDS];
+    const int rc = record_fields(fields, nfields, records, record_row_stride, false, f,
+                                 "moe_unpack_records");
+    if (rc != MOE_OK) return rc;
+    return moe_dispatch(f, nfields, N, 1, nullptr, stream);
+}

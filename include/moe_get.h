@@ -285,6 +285,32 @@ int moe_combine_epilogue(const void* y, int64_t y_row_stride, const float* w,
                          hipStream_t stream);
 
 /*
+ * Per-token records: up to 4 fields (e.g. ids, weights, hidden, scales) at
+ * 16-byte aligned offsets inside one record per token, the packing of the
+ * vLLM branch compare ds-exp-2...ds-exp-ag (moe_allgather.cu, make_desc),
+ * here one record per token as the packed-record workload has it.
+ *
+ * moe_record_offsets (host only, no GPU): offsets[f] = the offset of field f
+ * (the running end rounded up to 16); returns the record size (the end
+ * rounded up to 16), or a negative MOE_ERR_ARG when nfields is outside 1..4
+ * or a row_bytes is negative or not a multiple of 4. offsets may be NULL.
+ *
+ * moe_pack_records: for every token t and field f, copies fields[f].row_bytes
+ * bytes from fields[f].src + t*fields[f].src_row_stride to records +
+ * t*record_row_stride + offsets[f] (the fields' dst members are ignored).
+ * moe_unpack_records: the reverse, into fields[f].dst + t*dst_row_stride
+ * (src members ignored). Both are moe_dispatch with K = 1 and pos = NULL on
+ * redirected fields, with its alignment rules (16-byte alignment of the
+ * records, their stride and the fields gives the 16-byte path) and errors;
+ * record_row_stride must be at least the record size (MOE_ERR_ARG).
+ */
+int64_t moe_record_offsets(const int64_t* row_bytes, int32_t nfields, int64_t* offsets);
+int moe_pack_records(const moe_field* fields, int32_t nfields, int32_t N, void* records,
+                     int64_t record_row_stride, hipStream_t stream);
+int moe_unpack_records(const void* records, int64_t record_row_stride, int32_t N,
+                       const moe_field* fields, int32_t nfields, hipStream_t stream);
+
+/*
  * Layout and dispatch in one launch, for small (decode-sized) batches: the
  * same results as moe_get_layout(ids, ..., E, align, counts, offsets, pos,
  * row_pair, cap, ..., status) followed by moe_dispatch(fields, nfields, N, K,

@@ -303,3 +303,25 @@ def test_layout_dispatch_validation(lib):
     assert F(P, 8, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 0, 0) == lib.MOE_ERR_ARG       # no fields
     bad = (lib.moe_field * 1)(lib.moe_field(P + 2, 64, P, 64, 64))
     assert F(P, 8, 16, 8, 64, 1, P, P, P, P, 128, P, bad, 1, 0) == lib.MOE_ERR_ALIGN
+
+
+def test_record_offsets_and_pack_validation(lib):
+    """moe_record_offsets is host-only: the packed-record workload's layout
+    (ids 32 B @0, weights 32 B @32, hidden 3584 B @64, scales 448 B @3648, a
+    4096-B record) and the 16-byte rounding of odd sizes."""
+    offs, size = lib.record_offsets([32, 32, 3584, 448])
+    assert offs == [0, 32, 64, 3648] and size == 4096
+    offs, size = lib.record_offsets([4, 20, 8])
+    assert offs == [0, 16, 48] and size == 64
+    assert lib.record_offsets([0])[1] == 0
+    for bad in ([], [4] * 5, [3], [-4]):
+        with pytest.raises(lib.MoeError):
+            lib.record_offsets(bad)
+    L = lib._lib
+    P = 0x10000
+    fld = (lib.moe_field * 2)(lib.moe_field(P, 64, 0, 0, 64), lib.moe_field(P, 16, 0, 0, 16))
+    assert L.moe_pack_records(fld, 2, 8, P, 64, 0) == lib.MOE_ERR_ARG      # record is 80 B
+    assert L.moe_pack_records(fld, 2, 8, 0, 80, 0) == lib.MOE_ERR_ARG      # NULL records
+    assert L.moe_pack_records(fld, 0, 8, P, 80, 0) == lib.MOE_ERR_ARG
+    assert L.moe_unpack_records(P, 64, 8, fld, 2, 0) == lib.MOE_ERR_ARG
+    assert L.moe_pack_records(fld, 2, 0, P, 80, 0) == lib.MOE_OK           # N = 0
