@@ -151,21 +151,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
     if (threadIdx.x == 0) nbad_s = 0;
     __syncthreads();
 
-    const int32_t before = (int32_t)t * K;
-    int32_t nbad = 0;
-    for (int32_t i = threadIdx.x; i < nk; i += kThreads) {
-        const int32_t ti = i / K;
-        const int32_t e = f.ids[(int64_t)ti * f.ids_stride + (i - ti * K)];
-        if (e >= E) {
-            ++nbad;
-        } else if (e >= 0) {
-            atomicAdd(&tot[e], 1);
-            if (i < before)
-                for (int32_t k = 0; k < K; ++k)
-                    if (e == tok_e[k]) atomicAdd(&hits[k], 1);
-        }
-    }
-    if (nbad) atomicAdd(&nbad_s, nbad);
+    count_batch_ids(f.ids, f.ids_stride, nk, K, E, (int32_t)t * K, tok_e, tot, hits, &nbad_s);
     __syncthreads();
 
     // 2. offsets: thread i scans experts 4i .. 4i+3 (E <= 1024)
@@ -205,11 +191,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
         const int32_t k = threadIdx.x;
         const int32_t e = tok_e[k];
         int32_t p = -1;
-        if (e >= 0 && e < E) {
-            int32_t r = hits[k];
-            for (int32_t j = 0; j < k; ++j) r += tok_e[j] == e;
-            p = off[e] + r;
-        }
+        if (e >= 0 && e < E) p = off[e] + rank_in_expert(tok_e, hits, k);
         rows[k] = p;
         if (g == 0) {
             f.pos[(int64_t)t * K + k] = p;

@@ -221,21 +221,7 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
     __syncthreads();
 
     // 1. totals, bad ids, and matches of the token's experts before token t
-    const int32_t before = (int32_t)t * K;
-    int32_t nbad = 0;
-    for (int32_t i = threadIdx.x; i < nk; i += kFusedThreads) {
-        const int32_t ti = i / K;
-        const int32_t v = f.ids[(int64_t)ti * f.ids_stride + (i - ti * K)];
-        if (v >= E) {
-            ++nbad;
-        } else if (v >= 0) {
-            atomicAdd(&tot[v], 1);
-            if (i < before)
-                for (int32_t k = 0; k < K; ++k)
-                    if (v == tok_e[k]) atomicAdd(&hits[k], 1);
-        }
-    }
-    if (nbad) atomicAdd(&nbad_s, nbad);
+    count_batch_ids(f.ids, f.ids_stride, nk, K, E, (int32_t)t * K, tok_e, tot, hits, &nbad_s);
     __syncthreads();
 
     // 2. the token's rows
@@ -244,8 +230,7 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
         const int32_t e = tok_e[k];
         int32_t p = -1;
         if (e >= 0 && e < E) {
-            int32_t r = hits[k];
-            for (int32_t j = 0; j < k; ++j) r += tok_e[j] == e;
+            const int32_t r = rank_in_expert(tok_e, hits, k);
             if (r < M) p = e * M + r;
         }
         rows[k] = p;
