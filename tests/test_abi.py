@@ -282,6 +282,9 @@ def test_c_program_builds_against_the_header(tmp_path):
     against the header, the library and the oracle."""
     import importlib.util
 
+    import oracle
+
+    oracle.lib()                      # builds liboracle.so when it is missing
     spec = importlib.util.spec_from_file_location("cb", os.path.join(ROOT, "tests", "c_abi", "build.py"))
     cb = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(cb)
