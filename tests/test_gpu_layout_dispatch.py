@@ -158,3 +158,44 @@ def test_graph_capture_of_the_one_launch_forms(mg):
             if a.dtype == torch.bfloat16:
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), (rep, name)
+
+
+@pytest.mark.parametrize("seed", range(2000, 2060))
+def test_stress(mg, seed):
+    """Random shapes over the whole parameter space of the one-launch forms:
+    N*K up to the 8192 limit, E up to 1024, K up to 32, masks, out-of-range
+    and repeated ids, align up to 16, M below the counts."""
+    rng = np.random.default_rng(seed)
+    K = int(rng.choice([1, 2, 3, 8, 16, 32]))
+    N = int(rng.integers(0, 8192 // K + 1))
+    E = int(rng.choice([1, 3, 64, 255, 256, 1024]))
+    ids = rng.integers(-2, E + 3, size=(N, K)).astype(np.int32)
+    if rng.random() < 0.5 and N:
+        ids[:, : max(1, K // 2)] = rng.integers(0, min(E, 4), size=(N, max(1, K // 2)))  # hot experts
+    align = int(rng.choice([1, 2, 16]))
+    srcs = [rng.integers(0, 256, size=(N, b), dtype=np.uint8) for b in (48, 16)]
+    say(f"stress seed={seed} N={N} K={K} E={E} align={align}")
+    check(mg, ids, E, align, srcs, cap=oracle.required_cap(N, K, E, align) + int(rng.integers(0, 9)))
+    # the padded FP8 form on the same ids
+    M = int(rng.choice([1, 5, max(1, N * K // max(E, 1)), max(1, N)]))
+    if E * M <= 1 << 20:
+        H = 512
+        x = mw.bf16_bits_from_f32((rng.standard_normal((N, H)) * 8).astype(np.float32))
+        fmt = int(rng.integers(0, 3))
+        rows = E * M
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        pos = torch.empty((N, K), dtype=torch.int32, device="cuda")
+        row_pair = torch.empty(rows, dtype=torch.int32, device="cuda")
+        status = torch.empty(2, dtype=torch.int32, device="cuda")
+        dst = torch.full((rows, H), 0x66, dtype=torch.uint8, device="cuda")
+        shape = {0: (rows, H // 128), 1: (E, H // 128, M), 2: (E, H // 512, M)}[fmt]
+        scales = torch.zeros(shape, dtype=torch.int32 if fmt == 2 else torch.float32, device="cuda")
+        mg.moe_dispatch_fp8_padded(dev(ids), E, M, dev(x.view(np.int16)).view(torch.bfloat16),
+                                   counts, pos, row_pair, status, dst, scales, fmt, fmt == 2)
+        torch.cuda.synchronize()
+        c, p, rp, st = oracle.layout_padded(ids, E, M)
+        assert np.array_equal(counts.cpu().numpy(), c) and np.array_equal(pos.cpu().numpy(), p)
+        assert np.array_equal(row_pair.cpu().numpy(), rp) and tuple(status.cpu().tolist()) == st
+        codes, ref_scales = oracle.dispatch_fp8(x, p, rows, fmt, M, fmt == 2, fill=0x66)
+        assert np.array_equal(dst.cpu().numpy(), codes)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
