@@ -72,6 +72,7 @@ KERNEL_SOURCES = {
     "combine_backward_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
     "dispatch_fp8_padded_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
     "layout_dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
+    "scatter_scales_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
@@ -291,12 +292,17 @@ class LowLatencySet:
     rows per expert), bf16 -> e4m3 cast on dispatch with per-128-channel
     scales, combine reading the expert outputs from the padded buffer."""
 
-    def __init__(self, torch, mg, wl, x_bits, y_bits, M, scale_format, round_scale, fused=False):
+    def __init__(self, torch, mg, wl, x_bits, y_bits, M, scale_format, round_scale, fused=False,
+                 staged=False):
         d = "cuda"
         self.fused = fused
         N, K, E, Hc = wl.N, wl.K, wl.E, wl.Hc
         H = x_bits.shape[1]
         self.M, self.H, self.fmt = M, H, SCALE_FORMATS[scale_format]
+        # staged: per-token scales (MOE_SCALE_TOKENS) placed by moe_scatter_scales
+        self.staged = staged
+        if staged:
+            self.tok = torch.empty((N, H // 128), dtype=torch.float32, device=d)
         self.round_scale = int(round_scale)
         self.ids = torch.from_numpy(np.ascontiguousarray(wl.ids)).to(d)
         self.w = torch.from_numpy(np.ascontiguousarray(wl.weights)).to(d)
@@ -339,6 +345,13 @@ class LowLatencySet:
                self.scales.data_ptr(), self.fmt, srs, M, self.round_scale, stream)
         com = (self.y.data_ptr(), Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K, Hc,
                self.out.data_ptr(), Hc, stream)
+        if self.staged:
+            dis = (self.x.data_ptr(), H, N, K, H, self.pos.data_ptr(), self.codes.data_ptr(), H,
+                   self.tok.data_ptr(), mg.MOE_SCALE_TOKENS, H // 128, M, self.round_scale, stream)
+            sca = (self.tok.data_ptr(), H // 128, N, K, H, self.row_pair.data_ptr(), E, M,
+                   self.scales.data_ptr(), self.fmt, stream)
+            return ((L.moe_get_layout_padded, lay), (L.moe_dispatch_fp8, dis),
+                    (L.moe_scatter_scales, sca), (L.moe_combine, com))
         if self.fused:
             fu = (self.ids.data_ptr(), K, N, K, E, M, self.x.data_ptr(), H, H,
                   self.counts.data_ptr(), self.pos.data_ptr(), self.row_pair.data_ptr(),
@@ -539,6 +552,9 @@ def main():
                     help="--lowlatency scales: rows, cols (column-major fp32) or ue8m0")
     ap.add_argument("--round-scale", action="store_true",
                     help="--lowlatency: round scales up to powers of two (implied by ue8m0)")
+    ap.add_argument("--scales-staged", action="store_true",
+                    help="low-latency cols/ue8m0: per-token scales (MOE_SCALE_TOKENS) placed by "
+                         "moe_scatter_scales, instead of the one-call dispatch writing them")
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch in one launch for small batches (N*K <= 8192): "
                          "moe_layout_dispatch, or with --lowlatency moe_dispatch_fp8_padded")
@@ -560,6 +576,9 @@ def main():
         return
     if args.lowlatency + args.epilogue + args.backward > 1:
         raise SystemExit("--lowlatency, --epilogue and --backward are separate measurements")
+    if args.scales_staged and (not args.lowlatency or args.fused or args.scale_format == "rows"):
+        raise SystemExit("--scales-staged applies to the unfused low-latency step with cols or "
+                         "ue8m0 scales")
     if args.fused and (args.epilogue or args.backward):
         raise SystemExit("--fused applies to the plain and the low-latency step")
 
@@ -583,13 +602,23 @@ def main():
     R = N * K
     M = args.rows_per_expert or N
     round_scale = args.round_scale or args.scale_format == "ue8m0"
+    staged = args.lowlatency and args.scale_format != "rows" and args.scales_staged
     if args.lowlatency:
         x = mw.make_x(N, 7168, wl.seed + 104729)
-        sets = [LowLatencySet(torch, mg, wl, x, y, M, args.scale_format, round_scale, args.fused)
+        sets = [LowLatencySet(torch, mg, wl, x, y, M, args.scale_format, round_scale, args.fused,
+                              staged)
                 for _ in range(max(1, args.sets))]
         names = ("layout", "dispatch", "combine")
         op_bytes = ll_algorithmic_bytes(N, K, E, M, 7168, Hc, R, args.scale_format)
         kernels = {"dispatch": "dispatch_fp8_kernel", "combine": "combine_kernel"}
+        if staged:
+            # the codes kernel and the scale placement, each with its share of
+            # the algorithmic bytes (the staging buffer's traffic is overhead)
+            sb = R * (7168 // 128 if args.scale_format == "ue8m0" else 4 * (7168 // 128))
+            names = ("layout", "dispatch", "scales", "combine")
+            op_bytes = (op_bytes[0], op_bytes[1] - sb, sb, op_bytes[2])
+            kernels = {"dispatch": "dispatch_fp8_kernel", "scales": "scatter_scales_kernel",
+                       "combine": "combine_kernel"}
         if args.fused:
             names = ("layout+dispatch", "combine")
             op_bytes = (op_bytes[0] + op_bytes[1], op_bytes[2])
@@ -705,6 +734,7 @@ def main():
                     f"{M} rows per expert, bf16 hidden 7168 cast to e4m3 on dispatch with "
                     f"{args.scale_format} scales per 128 channels"
                     + (" (power-of-two)" if round_scale else "")
+                    + (" staged per token and placed by expert row" if staged else "")
                     + f", combine bf16 hidden {Hc}, fp32 accumulation")
         metric = ("low-latency dispatch (fp8 cast) + combine effective HBM GB/s and tokens/s, "
                   f"{N}×7168 top-{K}, 1 GPU")

@@ -34,6 +34,7 @@ MOE_ERR_HIP = -6
 MOE_SCALE_ROWS = 0
 MOE_SCALE_COLS = 1
 MOE_SCALE_UE8M0 = 2
+MOE_SCALE_TOKENS = 3
 MAX_TOPK = 32
 MAX_EXPERTS = 1024
 MAX_FIELDS = 4
@@ -100,6 +101,8 @@ def _load():
     L.moe_combine_backward.argtypes = [P, i64, P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64,
                                        P]
     L.moe_combine_backward.restype = ctypes.c_int
+    L.moe_scatter_scales.argtypes = [P, i64, i32, i32, i32, P, i32, i32, P, i32, P]
+    L.moe_scatter_scales.restype = ctypes.c_int
     return L
 
 
@@ -221,9 +224,10 @@ def moe_dispatch_fp8(x: torch.Tensor, pos: Optional[torch.Tensor], K: int, dst: 
     N, H = x.shape
     xp, xs = _rows(x, "x") if N else (0, H)
     dp, ds = _rows(dst, "dst") if dst.shape[0] else (0, H)
-    if scale_format == MOE_SCALE_ROWS:
+    if scale_format in (MOE_SCALE_ROWS, MOE_SCALE_TOKENS):
         if scales.dtype != torch.float32 or scales.dim() != 2 or scales.stride(1) != 1:
-            raise TypeError("row scales must be float32 [rows, >= H/128] with contiguous rows")
+            raise TypeError("row or token scales must be float32 [rows, >= H/128] with "
+                            "contiguous rows")
         srs = scales.stride(0)
     else:
         if not scales.is_contiguous():
@@ -235,6 +239,31 @@ def moe_dispatch_fp8(x: torch.Tensor, pos: Optional[torch.Tensor], K: int, dst: 
     _check(_lib.moe_dispatch_fp8(xp, xs, N, K, H, _dev(pos, "pos"), dp, ds,
                                  _dev(scales, "scales"), scale_format, srs, rows_per_expert,
                                  int(bool(round_scale)), _stream(stream)))
+
+
+def moe_scatter_scales(token_scales: torch.Tensor, K: int, H: int, row_pair: torch.Tensor,
+                       num_experts: int, rows_per_expert: int, scales: torch.Tensor,
+                       scale_format: int = MOE_SCALE_COLS, stream=None) -> None:
+    """Column-major (fp32 [E, H/128, M]) or UE8M0 (int32 [E, H/512, M]) scales
+    of the padded layout from token-major ones (fp32 [N, >= H/128], as written
+    by moe_dispatch_fp8 with MOE_SCALE_TOKENS), placed by row_pair [E*M]."""
+    if token_scales.dtype != torch.float32 or token_scales.dim() != 2 or \
+            token_scales.stride(1) != 1:
+        raise TypeError("token_scales must be float32 [N, >= H/128] with contiguous rows")
+    if row_pair.dtype != torch.int32 or not row_pair.is_contiguous():
+        raise TypeError("row_pair must be a contiguous int32 tensor")
+    if not scales.is_contiguous():
+        raise TypeError("scales must be a contiguous tensor")
+    E, M = num_experts, rows_per_expert
+    if row_pair.numel() < E * M:
+        raise ValueError("row_pair has fewer than E*M entries")
+    per_word = 128 if scale_format == MOE_SCALE_COLS else 512
+    if scales.numel() < E * M * (H // per_word):
+        raise ValueError("scales too small for [E, H/%d, M]" % per_word)
+    N = token_scales.shape[0]
+    _check(_lib.moe_scatter_scales(_dev(token_scales, "token_scales"), token_scales.stride(0), N,
+                                   K, H, _dev(row_pair, "row_pair"), E, M,
+                                   _dev(scales, "scales"), scale_format, _stream(stream)))
 
 
 def _as_bytes2d(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
@@ -342,9 +371,10 @@ def moe_dispatch_fp8_padded(ids: torch.Tensor, num_experts: int, rows_per_expert
     ip, istr = _rows(ids, "ids") if N else (0, K)
     xp, xs = _rows(x, "x") if N else (0, H)
     dp, ds = _rows(dst, "dst") if dst.shape[0] else (0, H)
-    if scale_format == MOE_SCALE_ROWS:
+    if scale_format in (MOE_SCALE_ROWS, MOE_SCALE_TOKENS):
         if scales.dtype != torch.float32 or scales.dim() != 2 or scales.stride(1) != 1:
-            raise TypeError("row scales must be float32 [rows, >= H/128] with contiguous rows")
+            raise TypeError("row or token scales must be float32 [rows, >= H/128] with "
+                            "contiguous rows")
         srs = scales.stride(0)
     else:
         if not scales.is_contiguous():

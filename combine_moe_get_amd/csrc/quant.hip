@@ -33,7 +33,7 @@ struct Fp8Args {
     int64_t ds;          // bytes
     void* scales;
     int32_t mode;
-    int64_t srs;         // MOE_SCALE_ROWS: floats between rows
+    int64_t srs;         // MOE_SCALE_ROWS, MOE_SCALE_TOKENS: floats between rows
     int32_t M;           // rows per expert for the column-major forms
     int32_t round_scale;
 };
@@ -93,11 +93,13 @@ __device__ __forceinline__ bool load_segment(const Fp8Args& a, uint32_t t, int32
     return active;
 }
 
-// Quantises a loaded segment once and stores it, with its scales, to the
-// rows of the token's K pairs: lane k < K holds the row of pair k in pk (-1:
-// not dispatched). Every lane takes part in the lane swaps.
-__device__ __forceinline__ void cast_and_store(const Fp8Args& a, int32_t seg, int lane,
-                                               int32_t pk, const float (&f)[16], bool active) {
+// Quantises a loaded segment of token t once and stores it, with its scales,
+// to the rows of the token's K pairs: lane k < K holds the row of pair k in
+// pk (-1: not dispatched). Token-major scales are stored once, for the token.
+// Every lane takes part in the lane swaps.
+__device__ __forceinline__ void cast_and_store(const Fp8Args& a, uint32_t t, int32_t seg,
+                                               int lane, int32_t pk, const float (&f)[16],
+                                               bool active) {
     const int32_t c0 = seg * kChanPerWave + lane * kChanPerLane;
     float amax = 0.0f;
 #pragma unroll
@@ -121,11 +123,14 @@ __device__ __forceinline__ void cast_and_store(const Fp8Args& a, int32_t seg, in
                    up24 = __shfl_down(ex, 24, kWave);
     const uint32_t word = ex | (up8 << 8) | (up16 << 16) | (up24 << 24);
 
+    if (a.mode == MOE_SCALE_TOKENS && (lane & (kLanesPerBlock - 1)) == 0 && active)
+        static_cast<float*>(a.scales)[(int64_t)t * a.srs + b] = s;
     for (int32_t k = 0; k < a.K; ++k) {
         const int32_t p = __builtin_amdgcn_readlane(pk, k);
         if (p < 0) continue;
         if (active)
             __builtin_nontemporal_store(codes, reinterpret_cast<u32x4*>(a.dst + (int64_t)p * a.ds + c0));
+        if (a.mode == MOE_SCALE_TOKENS) continue;   // stored once above
         if (a.mode == MOE_SCALE_UE8M0) {
             if ((lane & 31) == 0 && active) {
                 const int64_t i = ((int64_t)(p / a.M) * (nb / 4) + b / 4) * a.M + p % a.M;
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
     if (a.pos != nullptr) pk = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
     float f[16];
     const bool active = load_segment(a, t, seg, lane, f);
-    cast_and_store(a, seg, lane, pk, f, active);
+    cast_and_store(a, t, seg, lane, pk, f, active);
 }
 
 // ---------------------------------------------------------------------------
@@ -262,7 +267,81 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
     // 4. cast and store this workgroup's segments
     if (!casts) return;
     const int32_t pk = lane < K ? rows[lane] : -1;
-    cast_and_store(a, seg, lane, pk, xv, active);
+    cast_and_store(a, t, seg, lane, pk, xv, active);
+}
+
+// ---------------------------------------------------------------------------
+// Column-major scales from token-major ones. Row p = e*M + m of the padded
+// layout holds pair r = row_pair[p] (-1: unused), i.e. token r / K, so its
+// scale of block b is token_scales[(r / K)*tss + b]. Written by destination
+// row, every store is a run along m: one wave takes 64 consecutive rows of
+// one expert, loads their row_pair entries once, gathers each lane's token
+// scales (kGather blocks in flight) and stores one 256-byte run per block
+// (fp32) or per 4-block word (UE8M0). Entries outside [0, N*K) count as
+// unused, so the gathers stay inside the token scales whatever row_pair
+// holds. With M a power of two (a column stride of 4*M bytes) the rows in
+// use of all columns share their low address bits, so these stores crowd
+// onto a few memory channels: the time then grows with M, not with the
+// bytes written.
+// ---------------------------------------------------------------------------
+
+constexpr int kScatterThreads = 256;
+constexpr int kGather = 32;   // blocks (fp32) or words (UE8M0) in flight per lane
+
+struct ScatterArgs {
+    const float* ts;
+    int64_t tss;          // floats between token rows
+    const int32_t* row_pair;
+    int32_t NK, K, E, M, chunks, nb;
+    void* out;
+    int32_t mode;
+};
+
+__global__ __launch_bounds__(kScatterThreads) void scatter_scales_kernel(const ScatterArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(
+        blockIdx.x * (kScatterThreads / kWave) + threadIdx.x / kWave);
+    const uint32_t e = wave / (uint32_t)a.chunks;
+    if (e >= (uint32_t)a.E) return;
+    const int32_t m = (int32_t)(wave - e * (uint32_t)a.chunks) * kWave + lane;
+    const int32_t r = m < a.M ? a.row_pair[(int64_t)e * a.M + m] : -1;
+    const bool valid = r >= 0 && r < a.NK;
+    if (__ballot(valid) == 0) return;
+    const float* src = a.ts + (valid ? (int64_t)(r / a.K) * a.tss : 0);
+
+    if (a.mode == MOE_SCALE_COLS) {
+        float* dst = static_cast<float*>(a.out) + (int64_t)e * a.nb * a.M + m;
+        for (int32_t b0 = 0; b0 < a.nb; b0 += kGather) {
+            float v[kGather];
+#pragma unroll
+            for (int j = 0; j < kGather; ++j)
+                if (valid && b0 + j < a.nb) v[j] = src[b0 + j];
+#pragma unroll
+            for (int j = 0; j < kGather; ++j)
+                if (valid && b0 + j < a.nb) dst[(int64_t)(b0 + j) * a.M] = v[j];
+        }
+    } else {
+        // UE8M0: byte j of word w is the exponent field of block 4w + j
+        // (the scales are powers of two, so the field is the whole value).
+        const int32_t nw = a.nb / 4;
+        uint32_t* dst = static_cast<uint32_t*>(a.out) + (int64_t)e * nw * a.M + m;
+        for (int32_t w0 = 0; w0 < nw; w0 += kGather) {
+            uint32_t v[kGather];
+#pragma unroll
+            for (int j = 0; j < kGather; ++j) {
+                if (valid && w0 + j < nw) {
+                    const float* q = src + 4 * (w0 + j);
+                    v[j] = ((__float_as_uint(q[0]) >> 23) & 0xFFu) |
+                           (((__float_as_uint(q[1]) >> 23) & 0xFFu) << 8) |
+                           (((__float_as_uint(q[2]) >> 23) & 0xFFu) << 16) |
+                           (((__float_as_uint(q[3]) >> 23) & 0xFFu) << 24);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kGather; ++j)
+                if (valid && w0 + j < nw) dst[(int64_t)(w0 + j) * a.M] = v[j];
+        }
+    }
 }
 
 }  // namespace
@@ -288,14 +367,15 @@ extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_strid
                     "moe_get_layout_padded + moe_dispatch_fp8)", (long long)N * K, kFusedMaxPairs);
     if ((int64_t)E * M >= ((int64_t)1 << 31))
         return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8_padded: E*M must be below 2^31");
-    if (scale_format < MOE_SCALE_ROWS || scale_format > MOE_SCALE_UE8M0)
+    if (scale_format < MOE_SCALE_ROWS || scale_format > MOE_SCALE_TOKENS)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: unknown scale_format %d", scale_format);
     if (H % kBlock != 0)
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: H=%d must be a multiple of 128", H);
     if (scale_format == MOE_SCALE_UE8M0 && (!round_scale || H % (4 * kBlock) != 0))
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: ue8m0 scales need round_scale and "
                     "H %% 512 == 0");
-    if (scale_format == MOE_SCALE_ROWS && scale_row_stride < H / kBlock)
+    if ((scale_format == MOE_SCALE_ROWS || scale_format == MOE_SCALE_TOKENS) &&
+        scale_row_stride < H / kBlock)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: scale_row_stride < H/128");
     if (counts == nullptr || row_pair == nullptr || status == nullptr)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8_padded: counts, row_pair and status must not "
@@ -354,15 +434,16 @@ extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, 
     if (N < 0 || K < 1 || H < 0)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: need N >= 0, K >= 1, H >= 0");
     if (K > MOE_MAX_TOPK) return fail(MOE_ERR_LIMIT, "moe_dispatch_fp8: K=%d > %d", K, MOE_MAX_TOPK);
-    if (scale_format < MOE_SCALE_ROWS || scale_format > MOE_SCALE_UE8M0)
+    if (scale_format < MOE_SCALE_ROWS || scale_format > MOE_SCALE_TOKENS)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: unknown scale_format %d", scale_format);
     if (H % kBlock != 0)
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8: H=%d must be a multiple of 128", H);
     if (scale_format == MOE_SCALE_UE8M0 && (!round_scale || H % (4 * kBlock) != 0))
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: ue8m0 scales need round_scale and H %% 512 == 0");
-    if (scale_format != MOE_SCALE_ROWS && rows_per_expert < 1)
+    if ((scale_format == MOE_SCALE_COLS || scale_format == MOE_SCALE_UE8M0) && rows_per_expert < 1)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: column-major scales need rows_per_expert >= 1");
-    if (scale_format == MOE_SCALE_ROWS && scale_row_stride < H / kBlock)
+    if ((scale_format == MOE_SCALE_ROWS || scale_format == MOE_SCALE_TOKENS) &&
+        scale_row_stride < H / kBlock)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: scale_row_stride < H/128");
     if (pos == nullptr && K != 1 && N > 0)
         return fail(MOE_ERR_ARG, "moe_dispatch_fp8: pos == NULL (identity) requires K == 1");
@@ -404,4 +485,46 @@ extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, 
     clear_launch_error();
     dispatch_fp8_kernel<<<(uint32_t)blocks, threads, 0, stream>>>(a);
     return check_launch("moe_dispatch_fp8");
+}
+
+extern "C" int moe_scatter_scales(const float* token_scales, int64_t token_scale_row_stride,
+                                  int32_t N, int32_t K, int32_t H, const int32_t* row_pair,
+                                  int32_t E, int32_t M, void* scales, int32_t scale_format,
+                                  hipStream_t stream) {
+    if (N < 0 || K < 1 || H < 0 || E < 0 || M < 1)
+        return fail(MOE_ERR_ARG, "moe_scatter_scales: need N >= 0, K >= 1, H >= 0, E >= 0, M >= 1");
+    if (scale_format != MOE_SCALE_COLS && scale_format != MOE_SCALE_UE8M0)
+        return fail(MOE_ERR_ARG, "moe_scatter_scales: scale_format must be MOE_SCALE_COLS or "
+                    "MOE_SCALE_UE8M0, not %d", scale_format);
+    if (H % kBlock != 0)
+        return fail(MOE_ERR_ALIGN, "moe_scatter_scales: H=%d must be a multiple of 128", H);
+    if (scale_format == MOE_SCALE_UE8M0 && H % (4 * kBlock) != 0)
+        return fail(MOE_ERR_ARG, "moe_scatter_scales: ue8m0 scales need H %% 512 == 0");
+    if (token_scale_row_stride < H / kBlock)
+        return fail(MOE_ERR_ARG, "moe_scatter_scales: token_scale_row_stride < H/128");
+    if ((int64_t)N * K >= ((int64_t)1 << 31) || (int64_t)E * M >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "moe_scatter_scales: N*K and E*M must be below 2^31");
+    if (N == 0 || E == 0 || H == 0) return ok();   // N = 0: no row_pair entry is valid
+    if (token_scales == nullptr || row_pair == nullptr || scales == nullptr)
+        return fail(MOE_ERR_ARG, "moe_scatter_scales: NULL pointer");
+    if (!aligned(token_scales, 4) || !aligned(row_pair, 4) || !aligned(scales, 4))
+        return fail(MOE_ERR_ALIGN, "moe_scatter_scales: pointers must be 4-byte aligned");
+
+    ScatterArgs a;
+    a.ts = token_scales;
+    a.tss = token_scale_row_stride;
+    a.row_pair = row_pair;
+    a.NK = N * K;
+    a.K = K;
+    a.E = E;
+    a.M = M;
+    a.chunks = ceil_div<int32_t>(M, kWave);
+    a.nb = H / kBlock;
+    a.out = scales;
+    a.mode = scale_format;
+    const int64_t waves = (int64_t)E * a.chunks;
+    const int64_t blocks = ceil_div<int64_t>(waves, kScatterThreads / kWave);
+    clear_launch_error();
+    scatter_scales_kernel<<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(a);
+    return check_launch("moe_scatter_scales");
 }

@@ -206,6 +206,7 @@ int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
 #define MOE_SCALE_ROWS 0   /* fp32 [rows, H/128]: scales[row*scale_row_stride + b] */
 #define MOE_SCALE_COLS 1   /* fp32 column-major per expert, [E, H/128, M] */
 #define MOE_SCALE_UE8M0 2  /* int32 [E, H/512, M], byte j of a word = exponent of block 4i+j */
+#define MOE_SCALE_TOKENS 3 /* fp32 [N, H/128] per token: scales[t*scale_row_stride + b] */
 
 /*
  * Dispatch with an FP8 cast, as DeepEP's low-latency dispatch does with
@@ -224,6 +225,9 @@ int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
  *   MOE_SCALE_COLS   fp32 scales[((p/M)*(H/128) + b)*M + p%M]   (M = rows_per_expert)
  *   MOE_SCALE_UE8M0  int32 word ((p/M)*(H/512) + b/4)*M + p%M, byte b%4 = biased
  *                    exponent of s (needs round_scale and H % 512 == 0)
+ *   MOE_SCALE_TOKENS fp32 scales[t*scale_row_stride + b], once per token and
+ *                    for every token (whether or not a pair of it is valid);
+ *                    moe_scatter_scales then places them by expert row
  * x: bf16 bits, 16-byte aligned, row stride a multiple of 8 elements;
  * dst: 16-byte aligned, row stride a multiple of 16 bytes; scales 4-byte aligned.
  * H % 128 == 0. Rows no pair maps to are left untouched. Errors:
@@ -233,6 +237,37 @@ int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K, 
                      const int32_t* pos, void* dst, int64_t dst_row_stride, void* scales,
                      int32_t scale_format, int64_t scale_row_stride, int32_t rows_per_expert,
                      int32_t round_scale, hipStream_t stream);
+
+/*
+ * Column-major or UE8M0 scales of the padded layout from token-major ones:
+ * moe_dispatch_fp8(..., MOE_SCALE_TOKENS into token_scales, ...) followed by
+ * this call leaves in `scales` exactly what moe_dispatch_fp8 with
+ * MOE_SCALE_COLS / MOE_SCALE_UE8M0 and rows_per_expert = M writes there, when
+ * row_pair is the padded layout's (moe_get_layout_padded) for the same pos.
+ * The layouts are those of DeepEP's low-latency receive scales (repository
+ * dump, deep_ep.cpp, Buffer::low_latency_dispatch: per expert, column-major
+ * over the expert's rows; with use_ue8m0, four exponents per int32).
+ * It also places per-token scales a caller already holds (its own
+ * quantiser's) into the receive layout. It is not faster than the one-call
+ * form: with M a power of two the rows in use of every column share the same
+ * low address bits, and the stores crowd onto a few memory channels.
+ *
+ * For every row p = e*M + m (e < E, m < M) with 0 <= row_pair[p] < N*K, i.e.
+ * pair r = row_pair[p] of token t = r / K:
+ *   MOE_SCALE_COLS   scales[(e*(H/128) + b)*M + m] = token_scales[t*tss + b]
+ *   MOE_SCALE_UE8M0  int32 word (e*(H/512) + b/4)*M + m, byte b%4 = bits 23..30
+ *                    (the exponent field) of token_scales[t*tss + b]; the
+ *                    scales must be powers of two (dispatch with round_scale)
+ * Other rows (row_pair[p] < 0 or >= N*K) are left untouched.
+ * token_scales: fp32 [N, tss], tss = token_scale_row_stride >= H/128;
+ * row_pair: int32 [E*M]; scales as above. All device pointers, 4-byte aligned.
+ * H % 128 == 0 (UE8M0: H % 512 == 0); N*K and E*M below 2^31. N = 0, E = 0
+ * or H = 0 enqueue nothing. Errors: MOE_ERR_ARG, MOE_ERR_ALIGN,
+ * MOE_ERR_LIMIT, MOE_ERR_HIP.
+ */
+int moe_scatter_scales(const float* token_scales, int64_t token_scale_row_stride, int32_t N,
+                       int32_t K, int32_t H, const int32_t* row_pair, int32_t E, int32_t M,
+                       void* scales, int32_t scale_format, hipStream_t stream);
 
 /*
  * Optional terms applied after the top-k sum by moe_combine_epilogue. All

@@ -74,6 +74,8 @@ def lib():
         L.oracle_fp8_block_scale.restype = ctypes.c_float
         L.oracle_dispatch_fp8.argtypes = [P, i64, i32, i32, i32, P, P, i64, P, i32, i64, i32, i32]
         L.oracle_dispatch_fp8.restype = ctypes.c_int
+        L.oracle_scatter_scales.argtypes = [P, i64, i32, i32, i32, P, i32, i32, P, i32]
+        L.oracle_scatter_scales.restype = ctypes.c_int
         L.oracle_dispatch_backward.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64]
         L.oracle_dispatch_backward.restype = ctypes.c_int
         L.oracle_combine_backward.argtypes = [P, i64, P, i64, P, i64, P, i32, i32, i32, P, i64, P,
@@ -298,7 +300,7 @@ def layout_padded(ids: np.ndarray, E: int, M: int):
     return counts, pos, row_pair, (int(status[0]), int(status[1]))
 
 
-SCALE_ROWS, SCALE_COLS, SCALE_UE8M0 = 0, 1, 2
+SCALE_ROWS, SCALE_COLS, SCALE_UE8M0, SCALE_TOKENS = 0, 1, 2, 3
 
 
 def dispatch_fp8(x: np.ndarray, pos: np.ndarray, rows: int, scale_mode: int = SCALE_ROWS,
@@ -306,7 +308,8 @@ def dispatch_fp8(x: np.ndarray, pos: np.ndarray, rows: int, scale_mode: int = SC
                  codes: np.ndarray = None, scales: np.ndarray = None):
     """Quantising dispatch of bf16 x [N, H] (bits). Returns (codes [rows, H]
     uint8, scales): fp32 [rows, H/128] (SCALE_ROWS), fp32 [rows/M, H/128, M]
-    (SCALE_COLS) or int32 [rows/M, H/512, M] (SCALE_UE8M0). Given `codes`
+    (SCALE_COLS), int32 [rows/M, H/512, M] (SCALE_UE8M0) or fp32 [N, H/128]
+    per token (SCALE_TOKENS). Given `codes`
     and `scales` (contiguous, of those shapes), writes into them instead;
     rows no pair lands on are left as they are."""
     assert x.dtype == np.uint16
@@ -314,6 +317,8 @@ def dispatch_fp8(x: np.ndarray, pos: np.ndarray, rows: int, scale_mode: int = SC
     K = pos.shape[1]
     if scale_mode == SCALE_ROWS:
         sshape, sdtype = (rows, H // 128), np.float32
+    elif scale_mode == SCALE_TOKENS:
+        sshape, sdtype = (N, H // 128), np.float32
     elif scale_mode == SCALE_COLS:
         sshape, sdtype = (rows // M, H // 128, M), np.float32
     else:
@@ -331,6 +336,30 @@ def dispatch_fp8(x: np.ndarray, pos: np.ndarray, rows: int, scale_mode: int = SC
     if rc != OK:
         raise OracleError(rc, "dispatch_fp8")
     return codes, scales
+
+
+def scatter_scales(token_scales: np.ndarray, K: int, row_pair: np.ndarray, E: int, M: int,
+                   scale_mode: int = SCALE_COLS, scales: np.ndarray = None) -> np.ndarray:
+    """Scales of the padded layout's rows from per-token ones (fp32 [N, H/128]):
+    fp32 [E, H/128, M] (SCALE_COLS) or int32 [E, H/512, M] (SCALE_UE8M0).
+    Given `scales`, writes into it; rows without a pair are left as they are."""
+    ts = np.ascontiguousarray(token_scales, dtype=np.float32)
+    N, nb = ts.shape
+    H = nb * 128
+    if scale_mode == SCALE_COLS:
+        sshape, sdtype = (E, nb, M), np.float32
+    else:
+        sshape, sdtype = (E, H // 512, M), np.int32
+    if scales is None:
+        scales = np.zeros(sshape, sdtype)
+    assert scales.shape == sshape and scales.dtype == sdtype and scales.flags.c_contiguous
+    rp = np.ascontiguousarray(row_pair, dtype=np.int32).reshape(-1)
+    assert rp.size >= E * M
+    rc = lib().oracle_scatter_scales(_ptr(ts), nb, N, K, H, _ptr(rp), E, M, _ptr(scales),
+                                     scale_mode)
+    if rc != OK:
+        raise OracleError(rc, "scatter_scales")
+    return scales
 
 
 def f32_to_e4m3(x: float) -> int:

@@ -389,18 +389,24 @@ float oracle_fp8_block_scale(const uint16_t* x, int round_scale) {
  * its scale. scale_mode 0: fp32 rows, scales[p*scale_row_stride + b];
  * 1: fp32 column-major per expert, scales[((p/M)*(H/128) + b)*M + p%M];
  * 2: ue8m0 column-major per expert, int32 words [((p/M)*(H/512) + b/4)*M + p%M],
- *    byte b%4 = biased exponent of the (power-of-two) scale. */
+ *    byte b%4 = biased exponent of the (power-of-two) scale;
+ * 3: fp32 per token, scales[t*scale_row_stride + b], for every token. */
 int oracle_dispatch_fp8(const uint16_t* x, int64_t x_row_stride, int32_t N, int32_t K, int32_t H,
                         const int32_t* pos, uint8_t* dst, int64_t dst_row_stride, void* scales,
                         int32_t scale_mode, int64_t scale_row_stride, int32_t M,
                         int32_t round_scale) {
     if (N < 0 || K < 1 || K > ORC_MAX_K || H < 0 || H % 128 != 0) return ORC_ERR_ARG;
+    if (scale_mode < 0 || scale_mode > 3) return ORC_ERR_ARG;
     if (scale_mode == 2 && (!round_scale || H % 512 != 0)) return ORC_ERR_ARG;
-    if (scale_mode != 0 && M < 1) return ORC_ERR_ARG;
+    if ((scale_mode == 1 || scale_mode == 2) && M < 1) return ORC_ERR_ARG;
     const int32_t nb = H / 128;
 #pragma omp parallel for schedule(static)
     for (int32_t t = 0; t < N; ++t) {
         const uint16_t* xr = x + (int64_t)t * x_row_stride;
+        if (scale_mode == 3)
+            for (int32_t b = 0; b < nb; ++b)
+                ((float*)scales)[(int64_t)t * scale_row_stride + b] =
+                    oracle_fp8_block_scale(xr + 128 * b, round_scale);
         for (int32_t k = 0; k < K; ++k) {
             int32_t p = pos[(int64_t)t * K + k];
             if (p < 0) continue;
@@ -409,7 +415,9 @@ int oracle_dispatch_fp8(const uint16_t* x, int64_t x_row_stride, int32_t N, int3
                 for (int i = 0; i < 128; ++i)
                     dst[(int64_t)p * dst_row_stride + 128 * b + i] =
                         oracle_f32_to_e4m3(oracle_bf16_to_f32(xr[128 * b + i]) / s);
-                if (scale_mode == 0) {
+                if (scale_mode == 3) {
+                    /* written once per token above */
+                } else if (scale_mode == 0) {
                     ((float*)scales)[(int64_t)p * scale_row_stride + b] = s;
                 } else if (scale_mode == 1) {
                     ((float*)scales)[((int64_t)(p / M) * nb + b) * M + p % M] = s;
@@ -419,6 +427,41 @@ int oracle_dispatch_fp8(const uint16_t* x, int64_t x_row_stride, int32_t N, int3
                     uint8_t* word = (uint8_t*)((uint32_t*)scales +
                                                ((int64_t)(p / M) * (nb / 4) + b / 4) * M + p % M);
                     word[b % 4] = (uint8_t)(bits >> 23);
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Scales placed by expert row (the receive-side scale layouts of the
+ * low-latency dispatch, deep_ep.cpp, Buffer::low_latency_dispatch): row
+ * p = e*M + m of the padded layout holds pair r = row_pair[p], a pair of
+ * token r / K, so it takes that token's scales. scale_mode 1: fp32
+ * scales[(e*(H/128) + b)*M + m]; 2: int32 word (e*(H/512) + b/4)*M + m whose
+ * byte b%4 is the biased exponent of the token's scale of block b. Rows with
+ * row_pair < 0 (or >= N*K) are left untouched. */
+int oracle_scatter_scales(const float* token_scales, int64_t token_scale_row_stride, int32_t N,
+                          int32_t K, int32_t H, const int32_t* row_pair, int32_t E, int32_t M,
+                          void* scales, int32_t scale_mode) {
+    if (N < 0 || K < 1 || H < 0 || H % 128 != 0 || E < 0 || M < 1) return ORC_ERR_ARG;
+    if (scale_mode != 1 && scale_mode != 2) return ORC_ERR_ARG;
+    if (scale_mode == 2 && H % 512 != 0) return ORC_ERR_ARG;
+    const int32_t nb = H / 128;
+    for (int32_t e = 0; e < E; ++e) {
+        for (int32_t m = 0; m < M; ++m) {
+            int32_t r = row_pair[(int64_t)e * M + m];
+            if (r < 0 || (int64_t)r >= (int64_t)N * K) continue;
+            const float* ts = token_scales + (int64_t)(r / K) * token_scale_row_stride;
+            for (int32_t b = 0; b < nb; ++b) {
+                if (scale_mode == 1) {
+                    ((float*)scales)[((int64_t)e * nb + b) * M + m] = ts[b];
+                } else {
+                    uint32_t bits;
+                    memcpy(&bits, &ts[b], 4);
+                    uint8_t* word =
+                        (uint8_t*)((uint32_t*)scales + ((int64_t)e * (nb / 4) + b / 4) * M + m);
+                    word[b % 4] = (uint8_t)((bits >> 23) & 0xFF);
                 }
             }
         }

@@ -203,7 +203,7 @@ def _fused_case(mg, ids, E, M, x_bits, fmt, round_scale, fill=0x3C):
     row_pair = torch.full((rows,), -9, dtype=torch.int32, device="cuda")
     status = torch.full((2,), -9, dtype=torch.int32, device="cuda")
     dst = torch.full((rows, H), fill, dtype=torch.uint8, device="cuda")
-    shape = {0: (rows, H // 128), 1: (E, H // 128, M), 2: (E, H // 512, M)}[fmt]
+    shape = {0: (rows, H // 128), 1: (E, H // 128, M), 2: (E, H // 512, M), 3: (N, H // 128)}[fmt]
     scales = torch.zeros(shape, dtype=torch.int32 if fmt == 2 else torch.float32, device="cuda")
     mg.moe_dispatch_fp8_padded(dev(ids), E, M, dev(x_bits.view(np.int16)).view(torch.bfloat16),
                                counts, pos, row_pair, status, dst, scales, fmt, round_scale)
@@ -218,7 +218,7 @@ def _fused_case(mg, ids, E, M, x_bits, fmt, round_scale, fill=0x3C):
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt,round_scale", [(0, False), (1, False), (1, True), (2, True)])
+@pytest.mark.parametrize("fmt,round_scale", [(0, False), (1, False), (1, True), (2, True), (3, False)])
 def test_fused_padded_fp8_decode(mg, fmt, round_scale):
     rng = np.random.default_rng(60 + fmt)
     N, K, E, H, M = 128, 8, 256, 7168, 128
@@ -253,3 +253,95 @@ def test_fused_padded_fp8_largest_and_empty(mg):
     _fused_case(mg, np.zeros((0, 8), np.int32), 16, 4, np.zeros((0, 256), np.uint16), 0, False)
     with pytest.raises(mg.MoeError):
         _fused_case(mg, np.zeros((1025, 8), np.int32), 16, 4, np.zeros((1025, 256), np.uint16), 0, False)
+
+
+# ------------------------------------------- token-major scales + scatter ---
+
+STAGED_CASES = [
+    # name, N, K, E, H, M, ids recipe
+    ("decode", 128, 8, 256, 7168, 128, "uniform"),
+    ("prefill", 4096, 8, 256, 7168, 256, "uniform"),
+    ("prefill, N % 8 != 0", 4093, 8, 256, 7168, 256, "uniform"),
+    ("drops, M % 64 != 0", 300, 3, 5, 1536, 50, "random"),
+    ("E = 1000, tiny M", 500, 8, 1000, 512, 3, "random"),
+    ("one token", 1, 4, 16, 1024, 1, "random"),
+]
+
+
+@pytest.mark.parametrize("case", STAGED_CASES, ids=[c[0] for c in STAGED_CASES])
+@pytest.mark.parametrize("fmt", [1, 2], ids=["cols", "ue8m0"])
+def test_fp8_cols_direct_and_staged(mg, case, fmt):
+    """Column-major and UE8M0 scales of the padded layout, both ways: the
+    one-call dispatch, and per-token scales (MOE_SCALE_TOKENS) placed by
+    moe_scatter_scales. Both bit-exact against the oracle's one-call form;
+    rows without a pair keep their sentinel."""
+    name, N, K, E, H, M, recipe = case
+    rng = np.random.default_rng(900 + N + fmt)
+    if recipe == "uniform":
+        ids = mw.uniform_distinct_ids(rng, N, K, E)
+    else:
+        ids = rng.integers(-1, E + 2, size=(N, K)).astype(np.int32)
+    x = _x(rng, N, H)
+    round_scale = fmt == 2
+    rows = E * M
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    pos_d = torch.empty((N, K), dtype=torch.int32, device="cuda")
+    row_pair = torch.empty(rows, dtype=torch.int32, device="cuda")
+    status = torch.empty(2, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(mg.moe_layout_workspace_bytes(N, K, E), 256), dtype=torch.uint8,
+                     device="cuda")
+    mg.moe_get_layout_padded(dev(ids), E, M, counts, pos_d, row_pair, ws, status)
+    _, pos, rp, _ = oracle.layout_padded(ids, E, M)
+    shape = (E, H // 128, M) if fmt == 1 else (E, H // 512, M)
+    sdt = torch.float32 if fmt == 1 else torch.int32
+    sentinel = 3 if fmt == 1 else 0x0B0B0B0B
+    x_d = dev(x.view(np.int16)).view(torch.bfloat16)
+    ref_codes, ref_scales = oracle.dispatch_fp8(
+        x, pos, rows, fmt, M, round_scale, fill=0xA5,
+        scales=np.full(shape, sentinel, np.float32 if fmt == 1 else np.int32))
+    _, ref_tok = oracle.dispatch_fp8(x, pos, rows, oracle.SCALE_TOKENS, M, round_scale,
+                                     codes=np.zeros((rows, H), np.uint8))
+    used = rp >= 0
+
+    say(f"fp8 {name} format={fmt} direct")
+    dst = torch.full((rows, H), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full(shape, sentinel, dtype=sdt, device="cuda")
+    mg.moe_dispatch_fp8(x_d, pos_d, K, dst, scales, fmt, M, round_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy()[used], ref_codes[used])
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+
+    say(f"fp8 {name} format={fmt} staged")
+    dst.fill_(0xA5)
+    scales.fill_(sentinel)
+    tok = torch.full((N, H // 128 + 3), -1.0, dtype=torch.float32, device="cuda")[:, : H // 128]
+    mg.moe_dispatch_fp8(x_d, pos_d, K, dst, tok, mg.MOE_SCALE_TOKENS, 0, round_scale)
+    mg.moe_scatter_scales(tok, K, H, row_pair, E, M, scales, fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), ref_codes)
+    assert np.array_equal(tok.cpu().numpy().view(np.uint32), ref_tok.view(np.uint32))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+
+
+def test_scatter_scales_ignores_out_of_range_pairs(mg):
+    """row_pair entries outside [0, N*K) leave their rows untouched, so a
+    stale or foreign row_pair cannot make the gathers leave token_scales."""
+    N, K, E, M, H = 3, 2, 2, 70, 512
+    ts = np.arange(N * 4, dtype=np.float32).reshape(N, 4) + 1
+    rp = np.full(E * M, -1, np.int32)
+    rp[[0, 1, 5, 69, 70, 71, 139]] = [0, 5, 6, 1 << 30, 2, -5, 3]
+    ref = oracle.scatter_scales(ts, K, rp, E, M, oracle.SCALE_COLS,
+                                scales=np.full((E, 4, M), 9, np.float32))
+    got = torch.full((E, 4, M), 9.0, dtype=torch.float32, device="cuda")
+    mg.moe_scatter_scales(dev(ts), K, H, dev(rp), E, M, got, mg.MOE_SCALE_COLS)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+    # rows 0, 1 of expert 0 <- tokens 0, 2; rows 0, 69 of expert 1 <- token 1;
+    # entries 6 (= N*K), 2^30 and -5 leave rows 5, 69 of expert 0 and row 1 of expert 1
+    assert ref[0, :, 0].tolist() == ts[0].tolist() and ref[0, :, 1].tolist() == ts[2].tolist()
+    assert ref[1, :, 0].tolist() == ts[1].tolist() and ref[1, :, 69].tolist() == ts[1].tolist()
+    assert (ref[0, :, [5, 69]] == 9).all() and (ref[1, :, 1] == 9).all()
+    with pytest.raises(mg.MoeError):
+        mg.moe_scatter_scales(dev(ts), K, H, dev(rp), E, M, got, mg.MOE_SCALE_ROWS)
+    with pytest.raises(mg.MoeError):
+        mg.moe_scatter_scales(dev(ts), K, 500, dev(rp), E, M, got, mg.MOE_SCALE_COLS)

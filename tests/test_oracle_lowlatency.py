@@ -157,6 +157,60 @@ def test_scale_layouts_agree(orc):
     assert np.array_equal(c_rows[used], solo[t]) and np.array_equal(s_rows[used], solo_s[t])
 
 
+@pytest.mark.parametrize("fmt", ["cols", "ue8m0"])
+def test_token_scales_then_scatter_is_the_one_call_form(orc, fmt):
+    """Per-token scales (SCALE_TOKENS) are the K = 1 row scales of every
+    token, dropped or not, with the same codes; placing them by row_pair
+    gives the column-major / UE8M0 arrays of the one-call form, leaving
+    unused rows as they were."""
+    rng = np.random.default_rng(11)
+    N, K, E, H, M = 96, 4, 8, 1024, 20            # M < N*K/E: some pairs dropped
+    ids = rng.integers(-1, E, size=(N, K)).astype(np.int32)
+    ids[5] = -1                                     # a token with no pair at all
+    ids[ids == E - 1] = -1
+    ids[0, 0] = E - 1                               # expert E-1: one row, M-1 unused
+    x = _bits(rng.standard_normal((N, H)) * np.exp(rng.standard_normal((N, 1))))
+    counts, pos, row_pair, (_, dropped) = orc.layout_padded(ids, E, M)
+    assert dropped > 0
+    mode = orc.SCALE_COLS if fmt == "cols" else orc.SCALE_UE8M0
+    rows = E * M
+    c_tok, s_tok = orc.dispatch_fp8(x, pos, rows, orc.SCALE_TOKENS, M, True, fill=0x5A)
+    solo_c, solo_s = orc.dispatch_fp8(x, np.arange(N, dtype=np.int32).reshape(N, 1), N,
+                                      round_scale=True)
+    assert s_tok.shape == (N, H // 128) and np.array_equal(s_tok, solo_s)
+    c_one, s_one = orc.dispatch_fp8(x, pos, rows, mode, M, True, fill=0x5A)
+    assert np.array_equal(c_tok, c_one)
+    sentinel = np.full_like(s_one, 7)
+    s_one2 = orc.dispatch_fp8(x, pos, rows, mode, M, True, codes=np.zeros_like(c_one),
+                              scales=sentinel.copy())[1]
+    s_sc = orc.scatter_scales(s_tok, K, row_pair, E, M, mode, scales=sentinel.copy())
+    assert np.array_equal(s_sc, s_one2)
+    unused = (row_pair.reshape(E, M) < 0)
+    assert unused.any() and (s_sc.transpose(0, 2, 1)[unused] == 7).all()
+
+
+def test_scatter_scales_hand_worked(orc):
+    # N=2 tokens, K=2, E=2 experts, M=3 rows each, H=512 (4 blocks, one ue8m0 word).
+    # row_pair: e0 rows <- pairs 1 (token 0), 2 (token 1), 4 (>= N*K: untouched);
+    #           e1 rows <- pairs 3 (token 1), 0 (token 0), -1 (untouched).
+    ts = np.array([[1.0, 2.0, 0.5, 0.25], [4.0, 8.0, 0.125, 2.0 ** -126]], np.float32)
+    row_pair = np.array([1, 2, 4, 3, 0, -1], np.int32)
+    S = -3.0
+    cols = orc.scatter_scales(ts, 2, row_pair, 2, 3, orc.SCALE_COLS,
+                              scales=np.full((2, 4, 3), S, np.float32))
+    assert cols.tolist() == [
+        [[1.0, 4.0, S], [2.0, 8.0, S], [0.5, 0.125, S], [0.25, 2.0 ** -126, S]],
+        [[4.0, 1.0, S], [8.0, 2.0, S], [0.125, 0.5, S], [2.0 ** -126, 0.25, S]]]
+    # ue8m0: byte j of a row's word = biased exponent of its token's block j
+    # (1 -> 127, 2 -> 128, 0.5 -> 126, 0.25 -> 125, 4 -> 129, 8 -> 130,
+    #  0.125 -> 124, 2^-126 -> 1)
+    ue = orc.scatter_scales(ts, 2, row_pair, 2, 3, orc.SCALE_UE8M0,
+                            scales=np.full((2, 1, 3), -1, np.int32))
+    b = ue.view(np.uint8).reshape(2, 3, 4)
+    assert b[0].tolist() == [[127, 128, 126, 125], [129, 130, 124, 1], [255, 255, 255, 255]]
+    assert b[1].tolist() == [[129, 130, 124, 1], [127, 128, 126, 125], [255, 255, 255, 255]]
+
+
 def test_errors(orc):
     x = np.zeros((2, 100), np.uint16)
     with pytest.raises(orc.OracleError):

@@ -52,6 +52,17 @@ MUTANTS = [
     ("padded layout keeps pairs past M",
      "if (counts[e] < M) {", "if (counts[e] <= M && e * M + counts[e] < E * M) {",
      "test_oracle_lowlatency.py"),
+    ("scale scatter takes the pair's index as the token",
+     "const float* ts = token_scales + (int64_t)(r / K) * token_scale_row_stride;",
+     "const float* ts = token_scales + (int64_t)(r % N) * token_scale_row_stride;",
+     "test_oracle_lowlatency.py"),
+    ("scale scatter transposes blocks and rows",
+     "((float*)scales)[((int64_t)e * nb + b) * M + m] = ts[b];",
+     "((float*)scales)[((int64_t)e * M + m) * nb + b] = ts[b];", "test_oracle_lowlatency.py"),
+    ("token scales skip tokens without a pair",
+     "        if (scale_mode == 3)\n            for (int32_t b = 0; b < nb; ++b)",
+     "        if (scale_mode == 3 && pos[(int64_t)t * K] >= 0)\n            for (int32_t b = 0; b < nb; ++b)",
+     "test_oracle_lowlatency.py"),
     ("combine backward scales by the first weight",
      "float wk = w[(int64_t)t * w_row_stride + k];", "float wk = w[(int64_t)t * w_row_stride];",
      "test_oracle_backward.py"),
