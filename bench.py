@@ -571,6 +571,8 @@ def main():
                                   "-backward" if args.backward else "")
     if args.fused:
         workload_key += "-fused"
+    if args.scales_staged:
+        workload_key += "-staged"
     if args.traffic_from:
         summarize_traffic(*args.traffic_from, workload_key, args.traffic_command)
         return
