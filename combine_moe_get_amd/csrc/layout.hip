@@ -40,6 +40,9 @@ constexpr int kMaxChunks = 64;
 // load round instead of four per pass).
 constexpr int kBatchSmall = 4;
 constexpr int kBatchLarge = 16;
+// Third word of a gfx9 buffer descriptor for raw 32-bit loads (range-checked
+// against num_records: out-of-range loads return 0).
+constexpr int kBufferWord3 = 0x00020000;
 
 struct Plan {
     int32_t chunk;    // pairs per workgroup (multiple of kThreads)
@@ -98,16 +101,24 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane
 
 // Loads the expert ids of 64-pair steps s0 .. s0+B-1 of a wave's
 // quarter (-1 past the quarter or past the last pair). All loads are issued
-// before any is used.
+// before any is used. Contiguous ids (stride == K) need no division by K.
 template <int B>
 __device__ __forceinline__ void load_ids(int32_t (&e_reg)[B],
                                          const int32_t* __restrict__ ids, int64_t stride,
                                          uint32_t nk, uint32_t K, uint32_t first, int s0,
                                          int steps, int lane) {
+    if (stride == (int64_t)K) {
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-        const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
-        e_reg[j] = (s0 + j < steps && i < nk) ? load_id(ids, stride, i, K) : -1;
+        for (int j = 0; j < B; ++j) {
+            const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
+            e_reg[j] = (s0 + j < steps && i < nk) ? ids[i] : -1;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
+            e_reg[j] = (s0 + j < steps && i < nk) ? load_id(ids, stride, i, K) : -1;
+        }
     }
 }
 
@@ -224,17 +235,25 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
 
 // Per expert e (columns tid, tid+256, ... of H): pairs in chunks before b
 // (before_s) and in all chunks (total_s). C columns per thread and at most
-// R chunks, so every load is issued before the first sum.
+// R chunks, so every load is issued before the first sum. The loads go
+// through a buffer descriptor over H[blocks][E]: past its end they return 0,
+// so rows g >= blocks need no guard, and without guards each load is one
+// instruction rather than a branch around it (this straight-line code is
+// fetched cold by every workgroup, so its length is time). Columns e >= E
+// load whatever lies there and are not stored.
 template <int C, int R>
 __device__ __forceinline__ void reduce_chunks(const int32_t* __restrict__ H, int32_t blocks,
                                               int32_t E, int b, int32_t* total_s,
                                               int32_t* before_s) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(H), 0, blocks * E * (int32_t)sizeof(int32_t), kBufferWord3);
     int32_t v[C][R];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int e = threadIdx.x + c * kThreads;
 #pragma unroll
-        for (int g = 0; g < R; ++g) v[c][g] = (e < E && g < blocks) ? H[(int64_t)g * E + e] : 0;
+        for (int g = 0; g < R; ++g)
+            v[c][g] = __builtin_amdgcn_raw_buffer_load_b32(rs, (g * E + e) * 4, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -302,10 +321,18 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = threadIdx.x * 4 + j;
-        const int32_t c = e < E ? total_s[e] : 0;
-        mine4[j] = (int32_t)(((int64_t)c + align - 1) / align * align);
-        sum4 += mine4[j];
+        mine4[j] = e < E ? total_s[e] : 0;
     }
+    if (align > 1) {
+        // The host checks cap >= N*K + E*(align - 1) and cap < 2^31, so
+        // c + align - 1 fits in 32 bits (a 64-bit division is ~100
+        // instructions per use).
+        const uint32_t a = (uint32_t)align;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mine4[j] = (int32_t)(((uint32_t)mine4[j] + a - 1u) / a * a);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum4 += mine4[j];
     int32_t used = 0;
     int32_t run = block_exclusive_scan<kWaves>(sum4, wave_sums, &used);
     int32_t dropped4 = 0;   // padded form: pairs beyond their expert's M rows
