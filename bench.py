@@ -753,7 +753,8 @@ def main():
                     f"{P} B/token ({', '.join(f'{n} {a.shape[1]} B' for n, a in wl.fields) or 'one record: ids, weights, 3584 B hidden, 448 B scales; ids and weights read in place'}), "
                     f"combine bf16 hidden {Hc}, fp32 accumulation"
                     + (", fused residual add + RMSNorm epilogue" if args.epilogue else ""))
-        metric = METRIC
+        metric = METRIC if args.config == "prefill" else (
+            f"dispatch+combine effective HBM GB/s and tokens/s, {N}×{Hc} top-{K}, 1 GPU")
 
     result = {
         "metric": metric,
