@@ -87,8 +87,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a
 // concatenated fields (one per wave):
 //   1. its segment loads are issued first; then one pass over all ids gives
 //      the per-expert totals (LDS integer atomics: order-independent), the
-//      out-of-range count and the matches of the token's K experts among
-//      earlier tokens;
+//      out-of-range count and, per expert, the pairs of earlier tokens;
 //   2. the offsets: an exclusive scan of the aligned totals over E <= 1024;
 //   3. the token's rows; workgroup (t, 0) writes pos and row_pair, workgroup
 //      0 counts, offsets and status, and the unused rows (alignment padding
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
                                                                    const FusedLayout f) {
     __shared__ int32_t tot[MOE_MAX_EXPERTS];
     __shared__ int32_t off[MOE_MAX_EXPERTS + 1];
-    __shared__ int32_t hits[MOE_MAX_TOPK];
+    __shared__ int32_t bef[MOE_MAX_EXPERTS];
     __shared__ int32_t rows[MOE_MAX_TOPK];
     __shared__ int32_t tok_e[MOE_MAX_TOPK];
     __shared__ int32_t wave_sums[kWavesPerBlock];
@@ -144,14 +143,16 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
     VecT val{};
     if (moves) val = *reinterpret_cast<const VecT*>(src + (int64_t)t * ss + inner);
 
-    for (int e = threadIdx.x; e < E; e += kThreads) tot[e] = 0;
-    if (threadIdx.x < MOE_MAX_TOPK) hits[threadIdx.x] = 0;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        tot[e] = 0;
+        bef[e] = 0;
+    }
     if ((int32_t)threadIdx.x < K)
         tok_e[threadIdx.x] = has_token ? f.ids[(int64_t)t * f.ids_stride + threadIdx.x] : -1;
     if (threadIdx.x == 0) nbad_s = 0;
     __syncthreads();
 
-    count_batch_ids(f.ids, f.ids_stride, nk, K, E, (int32_t)t * K, tok_e, tot, hits, &nbad_s);
+    count_batch_ids(f.ids, f.ids_stride, nk, K, E, (int32_t)t * K, tot, bef, &nbad_s);
     __syncthreads();
 
     // 2. offsets: thread i scans experts 4i .. 4i+3 (E <= 1024)
@@ -159,10 +160,16 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = threadIdx.x * 4 + j;
-        const int32_t c = e < E ? tot[e] : 0;
-        mine[j] = (int32_t)(((int64_t)c + f.align - 1) / f.align * f.align);
-        sum4 += mine[j];
+        mine[j] = e < E ? tot[e] : 0;
     }
+    if (f.align > 1) {
+        // cap >= N*K + E*(align - 1) and cap < 2^31 (host checks): 32 bits
+        const uint32_t al = (uint32_t)f.align;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mine[j] = (int32_t)(((uint32_t)mine[j] + al - 1u) / al * al);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum4 += mine[j];
     int32_t x = sum4;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
         const int32_t k = threadIdx.x;
         const int32_t e = tok_e[k];
         int32_t p = -1;
-        if (e >= 0 && e < E) p = off[e] + rank_in_expert(tok_e, hits, k);
+        if (e >= 0 && e < E) p = off[e] + rank_in_expert(tok_e, bef, k);
         rows[k] = p;
         if (g == 0) {
             f.pos[(int64_t)t * K + k] = p;

@@ -34,39 +34,43 @@ __host__ __device__ constexpr T ceil_div(T a, T b) { return (a + b - 1) / b; }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // The one-pass layout of the one-launch forms (small batches): every
-// workgroup counts the whole batch itself. tot[E], hits[K] and *nbad live in
-// LDS and start at 0; tok_e[K] holds the token's expert ids. Adds, over all
-// pairs i < nk (ids read with a row stride): valid ids to tot[id] and, for
-// pairs of earlier tokens (i < before), to hits[k] of every k whose expert
-// matches; ids >= E to *nbad. LDS integer atomics: the sums do not depend on
-// their order. The caller synchronizes before and after.
+// workgroup counts the whole batch itself. tot[E], bef[E] and *nbad live in
+// LDS and start at 0. Adds, over all pairs i < nk (ids read with a row
+// stride; contiguous ids, stride == K, without a division by K): each valid
+// id to tot[id] and, for pairs of earlier tokens (i < before), to bef[id];
+// ids >= E to *nbad. LDS integer atomics: the sums do not depend on their
+// order. The caller synchronizes before and after.
 __device__ __forceinline__ void count_batch_ids(const int32_t* __restrict__ ids, int64_t stride,
                                                 int32_t nk, int32_t K, int32_t E, int32_t before,
-                                                const int32_t* tok_e, int32_t* tot, int32_t* hits,
-                                                int32_t* nbad) {
+                                                int32_t* tot, int32_t* bef, int32_t* nbad) {
+    const bool contiguous = stride == (int64_t)K;
     int32_t bad = 0;
     for (int32_t i = threadIdx.x; i < nk; i += blockDim.x) {
-        const int32_t ti = i / K;
-        const int32_t e = ids[(int64_t)ti * stride + (i - ti * K)];
+        int32_t e;
+        if (contiguous) {
+            e = ids[i];
+        } else {
+            const int32_t ti = i / K;
+            e = ids[(int64_t)ti * stride + (i - ti * K)];
+        }
         if (e >= E) {
             ++bad;
         } else if (e >= 0) {
             atomicAdd(&tot[e], 1);
-            if (i < before)
-                for (int32_t k = 0; k < K; ++k)
-                    if (e == tok_e[k]) atomicAdd(&hits[k], 1);
+            if (i < before) atomicAdd(&bef[e], 1);
         }
     }
     if (bad) atomicAdd(nbad, bad);
 }
 
-// Rank of the token's pair k among the pairs with its expert, in (t, k)
-// order: the matches among earlier tokens plus the earlier k' of the token
-// itself with the same expert.
-__device__ __forceinline__ int32_t rank_in_expert(const int32_t* tok_e, const int32_t* hits,
+// Rank of the token's pair k among the pairs with its (valid) expert, in
+// (t, k) order: the pairs of earlier tokens with that expert (bef) plus the
+// earlier k' of the token itself with the same expert.
+__device__ __forceinline__ int32_t rank_in_expert(const int32_t* tok_e, const int32_t* bef,
                                                   int32_t k) {
-    int32_t r = hits[k];
-    for (int32_t j = 0; j < k; ++j) r += tok_e[j] == tok_e[k];
+    const int32_t e = tok_e[k];
+    int32_t r = bef[e];
+    for (int32_t j = 0; j < k; ++j) r += tok_e[j] == e;
     return r;
 }
 

@@ -168,9 +168,9 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
 // token's rows from one pass over the batch's ids. Workgroup (t, g) takes
 // token t and the 1024-channel segments 4g .. 4g+3 (one per wave):
 //   1. one pass over all N*K ids: per-expert totals in LDS (integer atomics,
-//      so the totals do not depend on their order) and, for the token's K
-//      experts, the matches among earlier tokens;
-//   2. r(t, k) = matches(e_k) + (earlier k' < k of the token with e_k' = e_k);
+//      so the totals do not depend on their order) and, per expert, the
+//      pairs of earlier tokens, bef(e);
+//   2. r(t, k) = bef(e_k) + (earlier k' < k of the token with e_k' = e_k);
 //      workgroup (t, 0) writes pos and row_pair of the token's pairs;
 //   3. workgroup 0 writes counts and status from the totals; every expert's
 //      unused rows are marked -1 by workgroup e mod (number of workgroups);
@@ -197,7 +197,7 @@ struct FusedArgs {
 __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(const Fp8Args a,
                                                                             const FusedArgs f) {
     __shared__ int32_t tot[MOE_MAX_EXPERTS];
-    __shared__ int32_t hits[MOE_MAX_TOPK];
+    __shared__ int32_t bef[MOE_MAX_EXPERTS];
     __shared__ int32_t rows[MOE_MAX_TOPK];
     __shared__ int32_t tok_e[MOE_MAX_TOPK];
     __shared__ int32_t nbad_s, drop_s;
@@ -219,14 +219,16 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
     bool active = false;
     if (casts) active = load_segment(a, t, seg, lane, xv);
 
-    for (int e = threadIdx.x; e < E; e += kFusedThreads) tot[e] = 0;
-    if (threadIdx.x < MOE_MAX_TOPK) hits[threadIdx.x] = 0;
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) {
+        tot[e] = 0;
+        bef[e] = 0;
+    }
     if ((int32_t)threadIdx.x < K) tok_e[threadIdx.x] = has_token ? idrow[threadIdx.x] : -1;
     if (threadIdx.x == 0) nbad_s = drop_s = 0;
     __syncthreads();
 
-    // 1. totals, bad ids, and matches of the token's experts before token t
-    count_batch_ids(f.ids, f.ids_stride, nk, K, E, (int32_t)t * K, tok_e, tot, hits, &nbad_s);
+    // 1. totals, bad ids, and per expert the pairs of tokens before t
+    count_batch_ids(f.ids, f.ids_stride, nk, K, E, (int32_t)t * K, tot, bef, &nbad_s);
     __syncthreads();
 
     // 2. the token's rows
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
         const int32_t e = tok_e[k];
         int32_t p = -1;
         if (e >= 0 && e < E) {
-            const int32_t r = rank_in_expert(tok_e, hits, k);
+            const int32_t r = rank_in_expert(tok_e, bef, k);
             if (r < M) p = e * M + r;
         }
         rows[k] = p;
