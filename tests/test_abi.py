@@ -212,6 +212,32 @@ def test_layout_padded_and_fp8_validation(lib):
     assert F(P, 256, 4, 2, 256, 0, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ARG           # identity, K=2
     assert F(P, 256, 4, 33, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_LIMIT
     assert F(P, 256, 0, 2, 256, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_OK                # N = 0
+    # per-token scales: a row stride of at least H/128, no rows per expert needed
+    assert F(P, 256, 4, 2, 256, P, P, 256, P, 3, 1, 0, 0, 0) == lib.MOE_ERR_ARG           # row stride
+    assert F(P, 256, 0, 2, 256, P, P, 256, P, 3, 2, 0, 0, 0) == lib.MOE_OK                # N = 0, M = 0
+
+
+def test_scatter_scales_validation(lib):
+    S = lib._lib.moe_scatter_scales
+    P = 0x10000
+    # (token_scales, tss, N, K, H, row_pair, E, M, scales, fmt, stream)
+    ok = lambda **kw: [kw.get(n, d) for n, d in (
+        ("ts", P), ("tss", 4), ("N", 16), ("K", 8), ("H", 512), ("rp", P), ("E", 32), ("M", 64),
+        ("sc", P), ("fmt", 1), ("stream", 0))]
+    assert S(*ok(fmt=0)) == lib.MOE_ERR_ARG                # row-major is not a placed form
+    assert S(*ok(fmt=3)) == lib.MOE_ERR_ARG
+    assert S(*ok(K=0)) == lib.MOE_ERR_ARG
+    assert S(*ok(M=0)) == lib.MOE_ERR_ARG
+    assert S(*ok(N=-1)) == lib.MOE_ERR_ARG
+    assert S(*ok(H=200)) == lib.MOE_ERR_ALIGN              # H % 128
+    assert S(*ok(H=384, tss=3, fmt=2)) == lib.MOE_ERR_ARG  # ue8m0: H % 512
+    assert S(*ok(tss=3)) == lib.MOE_ERR_ARG                # stride < H/128
+    assert S(*ok(E=1 << 16, M=1 << 15)) == lib.MOE_ERR_LIMIT   # E*M >= 2^31
+    assert S(*ok(rp=0)) == lib.MOE_ERR_ARG
+    assert S(*ok(ts=0)) == lib.MOE_ERR_ARG
+    assert S(*ok(sc=P + 2)) == lib.MOE_ERR_ALIGN
+    assert S(*ok(N=0, ts=0)) == lib.MOE_OK                 # no pair can be valid: nothing to do
+    assert S(*ok(E=0)) == lib.MOE_OK
 
 
 def test_backward_validation(lib):
@@ -257,6 +283,7 @@ def test_fused_padded_fp8_validation(lib):
     assert F(*ok(H=200)) == lib.MOE_ERR_ALIGN              # H % 128
     assert F(*ok(fmt=2, rnd=0)) == lib.MOE_ERR_ARG         # ue8m0 needs round_scale
     assert F(*ok(fmt=0, srs=1)) == lib.MOE_ERR_ARG         # row scale stride
+    assert F(*ok(fmt=3, srs=1)) == lib.MOE_ERR_ARG         # token scale stride
     assert F(*ok(st=0)) == lib.MOE_ERR_ARG
     assert F(*ok(istr=4)) == lib.MOE_ERR_ARG               # ids stride < K
     assert F(*ok(x=P + 8)) == lib.MOE_ERR_ALIGN
