@@ -229,6 +229,43 @@ def test_edge_cases(mg):
         check_layout(mg, lay, ids, E)
 
 
+@pytest.mark.parametrize("Hc,N", [(131072, 24), (65538, 16), (16392, 64)])
+def test_wide_rows(mg, Hc, N):
+    """Rows far wider than the workloads': combine over 256 and 129 segments
+    (16-byte and 4-byte paths: Hc % 8 != 0 takes the 4-byte one), dispatch of
+    256 KiB payload rows, and the FP8 cast over 64 1024-channel segments."""
+    rng = np.random.default_rng(Hc)
+    K, E = 8, 16
+    ids = rng.integers(-1, E, size=(N, K)).astype(np.int32)
+    lay = mg.layout(dev(ids), E)
+    pos = check_layout(mg, lay, ids, E)
+    say(f"wide combine Hc={Hc} N={N}")
+    y = mw.bf16_bits_from_f32(rng.standard_normal((lay.cap, Hc)).astype(np.float32))
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    out = mg.combine(dev_bf16(y), dev(w), lay)
+    assert check_combine(out, y, w, pos) == 0
+    if Hc % 16 == 0:
+        say(f"wide dispatch {2 * Hc} B rows")
+        src = rng.integers(0, 256, size=(N, 2 * Hc), dtype=np.uint8)
+        (recv,) = mg.dispatch([dev(src)], lay)
+        torch.cuda.synchronize()
+        valid = pos.reshape(-1) >= 0
+        tok = np.repeat(np.arange(N), K)[valid]
+        assert np.array_equal(host(recv)[pos.reshape(-1)[valid]], src[tok])
+        say("wide fp8 cast, ue8m0")
+        H = Hc // 2
+        x = mw.bf16_bits_from_f32((rng.standard_normal((N, H)) * 4).astype(np.float32))
+        dst = torch.full((lay.cap, H), 0x11, dtype=torch.uint8, device="cuda")
+        M = lay.cap
+        scales = torch.zeros((1, H // 512, M), dtype=torch.int32, device="cuda")
+        # one "expert" of M rows: the column-major forms index rows p directly
+        mg.moe_dispatch_fp8(dev_bf16(x), lay.pos, K, dst, scales, mg.MOE_SCALE_UE8M0, M, True)
+        torch.cuda.synchronize()
+        codes, ref = oracle.dispatch_fp8(x, pos, lay.cap, oracle.SCALE_UE8M0, M, True, fill=0x11)
+        assert np.array_equal(host(dst), codes)
+        assert np.array_equal(host(scales).view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("N,K,E", [(4096, 8, 256), (4097, 8, 256), (4096, 8, 600)])
 def test_layout_paths_agree_on_uniform_and_skewed_ids(mg, N, K, E):
     """Both layout forms (one workgroup, and histogram + assign) against the
