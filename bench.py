@@ -44,8 +44,16 @@ def algorithmic_bytes(N, K, E, P, Hc, R, cap, epilogue=False):
 
 
 def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source with comments and whitespace removed, so that
+    counters stay attached to a kernel until its code changes."""
+    import re
+
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def traffic_entry(kernel, workload):

@@ -97,3 +97,13 @@ def test_copy_launches_must_agree(tmp_path, monkeypatch):
     _counter_csv(str(tmp_path / "w"), ok)
     with pytest.raises(SystemExit):
         bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "wl", "cmd")
+
+
+def test_source_hash_ignores_comments_not_code(tmp_path):
+    a = tmp_path / "a.hip"
+    a.write_text("// header\n__global__ void k(int* p) {\n    p[0] = 1;  /* one */\n}\n")
+    h = bench.source_hash(str(a))
+    a.write_text("// another header\n\n__global__ void k(int* p) {\n  p[0] = 1;  // one\n}\n")
+    assert bench.source_hash(str(a)) == h
+    a.write_text("// header\n__global__ void k(int* p) {\n    p[0] = 2;  /* one */\n}\n")
+    assert bench.source_hash(str(a)) != h
