@@ -376,7 +376,9 @@ float oracle_fp8_block_scale(const uint16_t* x, int round_scale) {
     }
     float s = amax / 448.0f;
     if (s < 0x1.0p-126f) s = 0x1.0p-126f;
-    if (round_scale) {
+    /* An infinite s (the block holds an infinity) has no power of two above
+     * it and stays infinite; frexpf leaves an infinity's exponent unset. */
+    if (round_scale && isfinite(s)) {
         int e;
         float g = frexpf(s, &e);       /* s = g * 2^e, 0.5 <= g < 1 */
         s = (g == 0.5f) ? s : ldexpf(1.0f, e);

@@ -106,6 +106,28 @@ def test_block_scale_rules(orc):
     assert orc.fp8_block_scale(np.zeros(128, np.uint16), False) == 2.0 ** -126
 
 
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_block_with_an_infinity(orc, round_scale):
+    """amax = inf makes s = inf, and with round_scale it stays inf: there is
+    no power of two above it. x / inf is then +-0 for finite x and NaN for
+    +-inf, so the codes are 0x00 / 0x80 and 0x7F (NaN), and the UE8M0 byte is
+    inf's exponent field, 0xFF."""
+    blk = _bits(np.linspace(-3.0, 3.0, 128))
+    blk[5], blk[9], blk[17] = 0x7F80, 0xFF80, 0x7FC0        # +inf, -inf, NaN
+    s = orc.fp8_block_scale(blk, round_scale)
+    assert math.isinf(s) and s > 0
+    x = blk.reshape(1, 128)
+    codes, scales = orc.dispatch_fp8(x, np.zeros((1, 1), np.int32), 1, orc.SCALE_ROWS, 0, round_scale)
+    f = bf16_bits_to_float(blk)
+    want = np.where(np.isfinite(f), np.where(np.signbit(f), 0x80, 0x00), 0x7F).astype(np.uint8)
+    assert np.array_equal(codes[0], want)
+    assert math.isinf(scales[0, 0])
+    if round_scale:
+        x4 = np.tile(blk, 4).reshape(1, 512)
+        _, ue = orc.dispatch_fp8(x4, np.zeros((1, 1), np.int32), 1, orc.SCALE_UE8M0, 1, True)
+        assert ue.view(np.uint8).reshape(-1).tolist() == [0xFF] * 4
+
+
 def test_constant_block_maps_to_max_code(orc):
     for c in (1.0, -3.5, 1e-3, 7.0e4):
         x = np.tile(_bits([c] * 128), (1, 1))
