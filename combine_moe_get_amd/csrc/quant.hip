@@ -14,6 +14,7 @@
 // exchange their partial amax with three DPP lane swaps, so every lane of
 // the block derives the same scale. Each destination row then takes one
 // 16-byte non-temporal store per lane: 1 KiB contiguous per wave and row.
+#include "fp8.hpp"
 #include "internal.hpp"
 
 namespace moe {
@@ -38,23 +39,6 @@ struct Fp8Args {
     int32_t round_scale;
 };
 
-// fp32 -> e4m3fn code on the bit pattern: round the 20 bits dropped below
-// the 3 kept mantissa bits to nearest even, rebias the exponent (127 -> 7),
-// saturate finite overflow at 448 (0x7E); below 2^-6 the codes are the
-// multiples of 2^-9, found by scaling by 2^9 (exact) and rounding to even.
-__device__ __forceinline__ uint32_t e4m3_code(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;               // NaN
-    if (a >= 0x43E00000u) return sign | 0x7Eu;       // >= 448, and infinity
-    if (a < 0x3C800000u)                             // below 2^-6
-        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    const uint32_t c = (r >> 20) - (120u << 3);
-    return sign | (c > 0x7Eu ? 0x7Eu : c);
-}
-
 // max of v over the 8 lanes of an aligned lane group (DPP within a row of
 // 16 lanes: swap neighbours, swap pairs, then mirror the two quads).
 __device__ __forceinline__ float group8_max(float v) {
@@ -62,11 +46,6 @@ __device__ __forceinline__ float group8_max(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
     return v;
-}
-
-__device__ __forceinline__ uint32_t pack4(const float* f, float s) {
-    return e4m3_code(f[0] / s) | (e4m3_code(f[1] / s) << 8) | (e4m3_code(f[2] / s) << 16) |
-           (e4m3_code(f[3] / s) << 24);
 }
 
 // Loads this lane's 16 channels of segment seg (1024 channels) of token t;

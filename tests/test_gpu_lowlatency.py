@@ -345,3 +345,47 @@ def test_scatter_scales_ignores_out_of_range_pairs(mg):
         mg.moe_scatter_scales(dev(ts), K, H, dev(rp), E, M, got, mg.MOE_SCALE_ROWS)
     with pytest.raises(mg.MoeError):
         mg.moe_scatter_scales(dev(ts), K, 500, dev(rp), E, M, got, mg.MOE_SCALE_COLS)
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_fp8_every_bf16_value(mg, fmt):
+    """Every finite bf16 value of magnitude <= 448 (and the infinities and a
+    NaN) through the FP8 dispatch with a scale of exactly 1: each 128-channel
+    block holds 448 (so amax / 448 = 1, a power of two) and 127 test values,
+    so every code is the e4m3 rounding of the bf16 value itself, ties
+    included. Bit-exact against the oracle, row-major and UE8M0 scales."""
+    vals = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (vals.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(f) & (np.abs(f) <= 448.0)
+    vals = vals[keep]
+    per = 127
+    nblk = -(-vals.size // per)
+    blocks = np.zeros((nblk, 128), np.uint16)
+    blocks[:, 0] = 0x43E0                                 # 448.0 in bf16
+    flat = np.concatenate([vals, np.zeros(nblk * per - vals.size, np.uint16)])
+    blocks[:, 1:] = flat.reshape(nblk, per)
+    H = 7168
+    bpt = H // 128
+    N = -(-nblk // bpt)
+    x = np.zeros((N * bpt, 128), np.uint16)
+    x[:nblk] = blocks
+    x[nblk:, 0] = 0x43E0
+    x = x.reshape(N, H)
+    x[N - 1, H - 3] = 0x7FC1                              # NaN
+    x[N - 1, H - 2], x[N - 1, H - 1] = 0x7F80, 0xFF80     # +-inf (their block's s becomes inf)
+    pos = np.arange(N, dtype=np.int32).reshape(N, 1)
+    say(f"fp8 every bf16 value: {vals.size} values in {N} tokens, format {fmt}")
+    dst = torch.full((N, H), 0x33, dtype=torch.uint8, device="cuda")
+    if fmt == 0:
+        scales = torch.zeros((N, bpt), dtype=torch.float32, device="cuda")
+    else:
+        scales = torch.zeros((1, H // 512, N), dtype=torch.int32, device="cuda")
+    mg.moe_dispatch_fp8(dev(x.view(np.int16)).view(torch.bfloat16), dev(pos), 1, dst, scales,
+                        fmt, N, True)
+    torch.cuda.synchronize()
+    codes, ref = oracle.dispatch_fp8(x, pos, N, fmt, N, True, fill=0x33)
+    assert np.array_equal(dst.cpu().numpy(), codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    # the blocks built from test values really had a scale of 1
+    if fmt == 0:
+        assert (scales.cpu().numpy().reshape(-1)[:nblk] == 1.0).all()
