@@ -43,17 +43,22 @@ def algorithmic_bytes(N, K, E, P, Hc, R, cap, epilogue=False):
     return layout, dispatch, combine
 
 
-def source_hash(path):
-    """Hash of a kernel source with comments and whitespace removed, so that
-    counters stay attached to a kernel until its code changes."""
+def source_hash(paths):
+    """Hash of a kernel's source files (one path or several) with comments and
+    whitespace removed, so that counters stay attached to a kernel until its
+    code changes."""
     import re
 
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = re.sub(r"\s+", " ", text).strip()
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    if isinstance(paths, str):
+        paths = [paths]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def traffic_entry(kernel, workload):
@@ -70,18 +75,21 @@ def traffic_entry(kernel, workload):
     return e
 
 
-KERNEL_SOURCES = {
-    "combine_epilogue_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
-    "combine_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
-    "dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
-    "layout_hist": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
-    "layout_assign": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "layout.hip"),
-    "dispatch_fp8_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
-    "combine_backward_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "combine.hip"),
-    "dispatch_fp8_padded_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
-    "layout_dispatch_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "dispatch.hip"),
-    "scatter_scales_kernel": os.path.join(ROOT, "combine_moe_get_amd", "csrc", "quant.hip"),
-}
+_CSRC = os.path.join(ROOT, "combine_moe_get_amd", "csrc")
+# Each kernel's source file and the library headers it is built with.
+_HDRS = (os.path.join(_CSRC, "internal.hpp"), os.path.join(_CSRC, "fp8.hpp"))
+KERNEL_SOURCES = {k: (os.path.join(_CSRC, f),) + _HDRS for k, f in (
+    ("combine_epilogue_kernel", "combine.hip"),
+    ("combine_kernel", "combine.hip"),
+    ("dispatch_kernel", "dispatch.hip"),
+    ("layout_hist", "layout.hip"),
+    ("layout_assign", "layout.hip"),
+    ("dispatch_fp8_kernel", "quant.hip"),
+    ("combine_backward_kernel", "combine.hip"),
+    ("dispatch_fp8_padded_kernel", "quant.hip"),
+    ("layout_dispatch_kernel", "dispatch.hip"),
+    ("scatter_scales_kernel", "quant.hip"),
+)}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
 
@@ -98,15 +106,23 @@ def _counter_rows(directory):
             yield from csv.DictReader(fh)
 
 
+def kernel_key(name):
+    """The function name of a profiled kernel ("void moe::(anonymous
+    namespace)::combine_kernel<4, false>(...)" -> "combine_kernel")."""
+    import re
+
+    m = re.match(r"(?:void\s+)?(?:[\w:]*\(anonymous namespace\)::|moe::)*([A-Za-z_]\w*)", name)
+    return m.group(1) if m else name
+
+
 def _per_kernel(directory, counter):
     """{short kernel name: [value per dispatch]} for one counter."""
     out = {}
     for r in _counter_rows(directory):
         if r.get("Counter_Name") != counter:
             continue
-        name = r["Kernel_Name"]
-        key = next((k for k in list(KERNEL_SOURCES) + [COPY_KERNEL] if k in name), None)
-        if key is not None:
+        key = kernel_key(r["Kernel_Name"])
+        if key in KERNEL_SOURCES or key == COPY_KERNEL:
             out.setdefault(key, []).append(float(r["Counter_Value"]))
     return out
 

@@ -72,6 +72,13 @@ def test_traffic_calibration_and_hash_check(tmp_path, monkeypatch):
     write = [{"Kernel_Name": bench.COPY_KERNEL, "Counter_Name": "WRITE_SIZE",
               "Counter_Value": copy} for _ in range(3)]
     write += [{"Kernel_Name": k, "Counter_Name": "WRITE_SIZE", "Counter_Value": 100.0}] * 2
+    # a kernel whose name contains another's is not counted as that one
+    ld = "void moe::(anonymous namespace)::layout_dispatch_kernel<unsigned int __vector(4)>(a)"
+    d = "void moe::(anonymous namespace)::dispatch_kernel<unsigned int __vector(4)>(a)"
+    fetch += [{"Kernel_Name": ld, "Counter_Name": "FETCH_SIZE", "Counter_Value": 7.0},
+              {"Kernel_Name": d, "Counter_Name": "FETCH_SIZE", "Counter_Value": 3.0}]
+    write += [{"Kernel_Name": ld, "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0},
+              {"Kernel_Name": d, "Counter_Name": "WRITE_SIZE", "Counter_Value": 1.0}]
     _counter_csv(str(tmp_path / "f"), fetch)
     _counter_csv(str(tmp_path / "w"), write)
     bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "wl", "cmd")
@@ -80,6 +87,8 @@ def test_traffic_calibration_and_hash_check(tmp_path, monkeypatch):
     assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
     assert e["bytes_per_launch"] == int((1001.0 * 2 + 100.0) * 1024)
     assert e["launches"] == 2 and e["command"] == "cmd"
+    assert data["dispatch_kernel/wl"]["bytes_per_launch"] == int((3.0 * 2 + 1.0) * 1024)
+    assert data["layout_dispatch_kernel/wl"]["bytes_per_launch"] == int((7.0 * 2 + 5.0) * 1024)
     assert bench.traffic_entry("combine_kernel", "wl") == e
     e["source_sha256_16"] = "0" * 16                    # counters of another source
     json.dump(data, open(tmp_path / "traffic.json", "w"))
