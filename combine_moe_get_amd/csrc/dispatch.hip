@@ -379,6 +379,32 @@ extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, i
     return check_launch("moe_layout_dispatch");
 }
 
+int moe::layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                           int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
+                           int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* status,
+                           hipStream_t stream) {
+    DispatchArgs a{};   // no payload: no vectors per token, no segments
+    a.pos = nullptr;
+    a.N = N;
+    a.K = K;
+    FusedLayout f;
+    f.ids = ids;
+    f.ids_stride = ids_row_stride;
+    f.E = E;
+    f.align = align;
+    f.groups = 1;
+    f.cap = cap;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.pos = pos;
+    f.row_pair = row_pair;
+    f.status = status;
+    const int64_t blocks = N > 0 ? N : 1;
+    clear_launch_error();
+    layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
+    return check_launch("moe_get_layout");
+}
+
 extern "C" int64_t moe_record_offsets(const int64_t* row_bytes, int32_t nfields,
                                       int64_t* offsets) {
     if (row_bytes == nullptr || nfields < 1 || nfields > MOE_MAX_FIELDS)

@@ -33,6 +33,19 @@ __host__ __device__ constexpr T ceil_div(T a, T b) { return (a + b - 1) / b; }
 // 16-byte and 4-byte lane payloads.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Layouts of small batches in one launch: the layout part of the one-launch
+// dispatch kernels, run without a payload. Every workgroup counts the whole
+// batch itself, which beats the two-kernel layout (histogram, then
+// assignment) up to about kOneLaunchPairs pairs. Same outputs as the
+// two-kernel layout; arguments are validated by the caller.
+constexpr int64_t kOneLaunchPairs = 2048;
+int layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                      int32_t E, int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
+                      int32_t* row_pair, int64_t cap, int32_t* status, hipStream_t stream);
+int layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                             int32_t E, int32_t M, int32_t* counts, int32_t* pos,
+                             int32_t* row_pair, int32_t* status, hipStream_t stream);
+
 // The one-pass layout of the one-launch forms (small batches): every
 // workgroup counts the whole batch itself. tot[E], bef[E] and *nbad live in
 // LDS and start at 0. Adds, over all pairs i < nk (ids read with a row

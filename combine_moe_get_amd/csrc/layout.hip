@@ -24,7 +24,10 @@
 //                same 64-pair step with that expert. Finally all workgroups
 //                mark unused rows with -1.
 // The kernel boundary is the only grid-wide ordering used, so the result
-// does not depend on scheduling. H has at most 16384 entries, so the
+// does not depend on scheduling. Batches of at most kOneLaunchPairs pairs
+// take one launch instead, the layout part of the one-launch dispatch
+// kernels (dispatch.hip, quant.hip), where every workgroup counts the whole
+// batch: below that size it is the faster of the two. H has at most 16384 entries, so the
 // redundant reduction costs each workgroup at most 64 loads per thread.
 #include "internal.hpp"
 
@@ -510,6 +513,9 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
                     ws, workspace_bytes, workspace ? "" : " (NULL)");
     if (!aligned(workspace, 4))
         return fail(MOE_ERR_ALIGN, "moe_get_layout: workspace must be 4-byte aligned");
+    if (N > 0 && nk <= kOneLaunchPairs)
+        return layout_one_launch(ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
+                                 row_pair, cap, status, stream);
 
     clear_launch_error();
     int32_t* H = static_cast<int32_t*>(workspace);
@@ -550,6 +556,11 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
                     "got %zu", ws, workspace_bytes);
     if (!aligned(workspace, 4))
         return fail(MOE_ERR_ALIGN, "moe_get_layout_padded: workspace must be 4-byte aligned");
+    // The one-launch form marks unused rows from N workgroups: used for small
+    // batches with at most 2^18 padded rows (and a status word to write).
+    if (N > 0 && nk <= kOneLaunchPairs && cap <= (1 << 18) && status != nullptr)
+        return layout_padded_one_launch(ids, ids_row_stride, N, K, E, M, counts, pos, row_pair,
+                                        status, stream);
     clear_launch_error();
     int32_t* H = static_cast<int32_t*>(workspace);
     int32_t* bad = H + (int64_t)p.blocks * E;

@@ -408,6 +408,28 @@ extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_strid
     return check_launch("moe_dispatch_fp8_padded");
 }
 
+int moe::layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N,
+                                  int32_t K, int32_t E, int32_t M, int32_t* counts, int32_t* pos,
+                                  int32_t* row_pair, int32_t* status, hipStream_t stream) {
+    Fp8Args a{};        // no channels: the kernel's layout part only
+    a.N = N;
+    a.K = K;
+    a.M = M;
+    FusedArgs f;
+    f.ids = ids;
+    f.ids_stride = ids_row_stride;
+    f.E = E;
+    f.groups = 1;
+    f.counts = counts;
+    f.pos = pos;
+    f.row_pair = row_pair;
+    f.status = status;
+    const int64_t blocks = N > 0 ? N : 1;
+    clear_launch_error();
+    dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
+    return check_launch("moe_get_layout_padded");
+}
+
 extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K,
                                 int32_t H, const int32_t* pos, void* dst, int64_t dst_row_stride,
                                 void* scales, int32_t scale_format, int64_t scale_row_stride,
