@@ -229,6 +229,43 @@ def test_edge_cases(mg):
         check_layout(mg, lay, ids, E)
 
 
+@pytest.mark.parametrize("N", [255, 256, 257])
+@pytest.mark.parametrize("align", [1, 16])
+def test_layout_around_the_one_launch_limit(mg, N, align):
+    """Batches of at most 2048 pairs take the one-launch layout, larger ones
+    the two kernels: both sides of the limit, with padding and spare rows."""
+    rng = np.random.default_rng(N * 31 + align)
+    K, E = 8, 64
+    ids = rng.integers(-1, E + 1, size=(N, K)).astype(np.int32)
+    cap = oracle.required_cap(N, K, E, align) + 7
+    say(f"layout at N*K={N * K} align={align}")
+    lay = mg.layout(dev(ids), E, align, cap=cap)
+    check_layout(mg, lay, ids, E, align, cap)
+
+
+@pytest.mark.parametrize("N,E,M,with_status", [(256, 64, 4096, True), (256, 64, 4097, True),
+                                               (257, 64, 64, True), (100, 16, 40, False)])
+def test_padded_layout_around_the_one_launch_limits(mg, N, E, M, with_status):
+    """The padded layout's one-launch form (N*K <= 2048, E*M <= 2^18, status
+    given) and its two-kernel form agree with the oracle on both sides."""
+    rng = np.random.default_rng(N + E + M)
+    K = 8
+    ids = rng.integers(-1, E + 1, size=(N, K)).astype(np.int32)
+    counts = torch.full((E,), -3, dtype=torch.int32, device="cuda")
+    pos = torch.full((N, K), -3, dtype=torch.int32, device="cuda")
+    row_pair = torch.full((E * M,), -3, dtype=torch.int32, device="cuda")
+    status = torch.full((2,), -3, dtype=torch.int32, device="cuda") if with_status else None
+    ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device="cuda")
+    say(f"padded layout N*K={N * K} E*M={E * M} status={with_status}")
+    mg.moe_get_layout_padded(dev(ids), E, M, counts, pos, row_pair, ws, status)
+    torch.cuda.synchronize()
+    c, p, rp, st = oracle.layout_padded(ids, E, M)
+    assert np.array_equal(host(counts), c) and np.array_equal(host(pos), p)
+    assert np.array_equal(host(row_pair), rp)
+    if with_status:
+        assert tuple(host(status).tolist()) == st
+
+
 @pytest.mark.parametrize("Hc,N", [(131072, 24), (65538, 16), (16392, 64)])
 def test_wide_rows(mg, Hc, N):
     """Rows far wider than the workloads': combine over 256 and 129 segments
