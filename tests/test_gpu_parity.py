@@ -355,10 +355,12 @@ def test_non_default_stream(mg):
     check_combine(out, y, wl.weights, pos)
 
 
-def test_graph_capture_replay(mg):
+@pytest.mark.parametrize("N", [256, 1024], ids=["one-launch layout", "two-kernel layout"])
+def test_graph_capture_replay(mg, N):
     """layout + dispatch + combine captured once and replayed on new inputs
-    (eager work and a sync between replays); every replay checked."""
-    N, K, E, Hc = 256, 8, 64, 512
+    (eager work and a sync between replays); every replay checked. 2048
+    pairs take the one-launch layout, 8192 the two kernels."""
+    K, E, Hc = 8, 64, 512
     ids_s = torch.zeros((N, K), dtype=torch.int32, device="cuda")
     x_s = torch.zeros((N, 1024), dtype=torch.uint8, device="cuda")
     w_s = torch.zeros((N, K), dtype=torch.float32, device="cuda")
@@ -387,8 +389,8 @@ def test_graph_capture_replay(mg):
     with torch.cuda.graph(g):
         step()
     for rep in range(4):
-        say(f"graph replay {rep}")
-        rng = np.random.default_rng(50 + rep)
+        say(f"graph replay {rep}, N={N}")
+        rng = np.random.default_rng(50 + rep + N)
         ids = mw.uniform_distinct_ids(rng, N, K, E)
         ids[rng.random((N, K)) < 0.1] = -1
         x = rng.integers(0, 256, size=(N, 1024), dtype=np.uint8)
