@@ -320,6 +320,36 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     return check_launch("moe_dispatch");
 }
 
+// Launches the one-launch layout+dispatch kernel for the payload in `a`
+// (a.V = 0: the layout part only): one workgroup per (token, group of
+// kWavesPerBlock segments); N = 0 still runs one workgroup, since counts,
+// offsets, status and row_pair are outputs.
+static int launch_layout_dispatch(const DispatchArgs& a, bool all16, const int32_t* ids,
+                                  int64_t ids_row_stride, int32_t E, int32_t align,
+                                  int32_t* counts, int32_t* offsets, int32_t* pos,
+                                  int32_t* row_pair, int64_t cap, int32_t* status,
+                                  hipStream_t stream, const char* who) {
+    FusedLayout f;
+    f.ids = ids;
+    f.ids_stride = ids_row_stride;
+    f.E = E;
+    f.align = align;
+    f.groups = a.segs > 0 ? ceil_div<int32_t>(a.segs, kWavesPerBlock) : 1;
+    f.cap = cap;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.pos = pos;
+    f.row_pair = row_pair;
+    f.status = status;
+    const int64_t blocks = a.N > 0 ? (int64_t)a.N * f.groups : 1;
+    clear_launch_error();
+    if (all16)
+        layout_dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
+    else
+        layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
+    return check_launch(who);
+}
+
 extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N,
                                    int32_t K, int32_t E, int32_t align, int32_t* counts,
                                    int32_t* offsets, int32_t* pos, int32_t* row_pair, int64_t cap,
@@ -356,27 +386,8 @@ extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, i
     a.pos = nullptr;
     a.N = N;
     a.K = K;
-    FusedLayout f;
-    f.ids = ids;
-    f.ids_stride = ids_row_stride;
-    f.E = E;
-    f.align = align;
-    f.groups = a.segs > 0 ? ceil_div<int32_t>(a.segs, kWavesPerBlock) : 1;
-    f.cap = cap;
-    f.counts = counts;
-    f.offsets = offsets;
-    f.pos = pos;
-    f.row_pair = row_pair;
-    f.status = status;
-    // N = 0 still runs one workgroup: counts, offsets, status and row_pair
-    // are outputs.
-    const int64_t blocks = N > 0 ? (int64_t)N * f.groups : 1;
-    clear_launch_error();
-    if (all16)
-        layout_dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
-    else
-        layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
-    return check_launch("moe_layout_dispatch");
+    return launch_layout_dispatch(a, all16, ids, ids_row_stride, E, align, counts, offsets, pos,
+                                  row_pair, cap, status, stream, "moe_layout_dispatch");
 }
 
 int moe::layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
@@ -387,22 +398,8 @@ int moe::layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N
     a.pos = nullptr;
     a.N = N;
     a.K = K;
-    FusedLayout f;
-    f.ids = ids;
-    f.ids_stride = ids_row_stride;
-    f.E = E;
-    f.align = align;
-    f.groups = 1;
-    f.cap = cap;
-    f.counts = counts;
-    f.offsets = offsets;
-    f.pos = pos;
-    f.row_pair = row_pair;
-    f.status = status;
-    const int64_t blocks = N > 0 ? N : 1;
-    clear_launch_error();
-    layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
-    return check_launch("moe_get_layout");
+    return launch_layout_dispatch(a, false, ids, ids_row_stride, E, align, counts, offsets, pos,
+                                  row_pair, cap, status, stream, "moe_get_layout");
 }
 
 extern "C" int64_t moe_record_offsets(const int64_t* row_bytes, int32_t nfields,

@@ -330,6 +330,28 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_scales_kernel(const S
 
 using namespace moe;
 
+// Launches the padded one-launch kernel on the cast arguments `a` (a.segs =
+// 0: the layout part only): one workgroup per (token, group of kFusedWaves
+// segments); N = 0 still runs one workgroup, since counts, status and every
+// row_pair entry are outputs.
+static int launch_padded_one_launch(const Fp8Args& a, const int32_t* ids, int64_t ids_row_stride,
+                                    int32_t E, int32_t* counts, int32_t* pos, int32_t* row_pair,
+                                    int32_t* status, hipStream_t stream, const char* who) {
+    FusedArgs f;
+    f.ids = ids;
+    f.ids_stride = ids_row_stride;
+    f.E = E;
+    f.groups = a.segs > 0 ? ceil_div<int32_t>(a.segs, kFusedWaves) : 1;
+    f.counts = counts;
+    f.pos = pos;
+    f.row_pair = row_pair;
+    f.status = status;
+    const int64_t blocks = a.N > 0 ? (int64_t)a.N * f.groups : 1;
+    clear_launch_error();
+    dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
+    return check_launch(who);
+}
+
 extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
                                        int32_t K, int32_t E, int32_t M, const void* x,
                                        int64_t x_row_stride, int32_t H, int32_t* counts,
@@ -391,21 +413,8 @@ extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_strid
     a.srs = scale_row_stride;
     a.M = M;
     a.round_scale = round_scale ? 1 : 0;
-    FusedArgs f;
-    f.ids = ids;
-    f.ids_stride = ids_row_stride;
-    f.E = E;
-    f.groups = a.segs > 0 ? ceil_div<int32_t>(a.segs, kFusedWaves) : 1;
-    f.counts = counts;
-    f.pos = pos;
-    f.row_pair = row_pair;
-    f.status = status;
-    // N = 0 still runs one workgroup: counts, status and every row_pair
-    // entry are outputs.
-    const int64_t blocks = N > 0 ? (int64_t)N * f.groups : 1;
-    clear_launch_error();
-    dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
-    return check_launch("moe_dispatch_fp8_padded");
+    return launch_padded_one_launch(a, ids, ids_row_stride, E, counts, pos, row_pair, status,
+                                    stream, "moe_dispatch_fp8_padded");
 }
 
 int moe::layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N,
@@ -415,19 +424,8 @@ int moe::layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, in
     a.N = N;
     a.K = K;
     a.M = M;
-    FusedArgs f;
-    f.ids = ids;
-    f.ids_stride = ids_row_stride;
-    f.E = E;
-    f.groups = 1;
-    f.counts = counts;
-    f.pos = pos;
-    f.row_pair = row_pair;
-    f.status = status;
-    const int64_t blocks = N > 0 ? N : 1;
-    clear_launch_error();
-    dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
-    return check_launch("moe_get_layout_padded");
+    return launch_padded_one_launch(a, ids, ids_row_stride, E, counts, pos, row_pair, status,
+                                    stream, "moe_get_layout_padded");
 }
 
 extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K,
