@@ -438,10 +438,11 @@ using namespace moe;
 // batch, follows the chunk size: 4 steps when a wave's quarter has at most
 // 4 (short code for small batches), else 16 (fewer dependent load rounds).
 template <int B>
-static void launch_layout_b(const Plan& p, uint32_t assign_grid, const int32_t* ids, int64_t stride,
-                     int64_t nk, int32_t K, int32_t E, int32_t align, int32_t* H, int32_t* bad,
-                     int32_t* counts, int32_t* offsets, int32_t* status, int32_t* pos,
-                     int32_t* row_pair, int64_t cap, int32_t M, hipStream_t stream) {
+static void launch_layout_b(const Plan& p, uint32_t assign_grid, const int32_t* ids,
+                            int64_t stride, int64_t nk, int32_t K, int32_t E, int32_t align,
+                            int32_t* H, int32_t* bad, int32_t* counts, int32_t* offsets,
+                            int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
+                            int32_t M, hipStream_t stream) {
     if (p.blocks > 0)
         layout_hist<B><<<p.blocks, kThreads, 0, stream>>>(ids, stride, (uint32_t)nk, (uint32_t)K,
                                                           E, p.chunk, p.nbits, H, bad);
@@ -450,10 +451,11 @@ static void launch_layout_b(const Plan& p, uint32_t assign_grid, const int32_t* 
         counts, offsets, status, pos, row_pair, cap, M);
 }
 
-static void launch_layout(const Plan& p, uint32_t assign_grid, const int32_t* ids, int64_t stride,
-                   int64_t nk, int32_t K, int32_t E, int32_t align, int32_t* H, int32_t* bad,
-                   int32_t* counts, int32_t* offsets, int32_t* status, int32_t* pos,
-                   int32_t* row_pair, int64_t cap, int32_t M, hipStream_t stream) {
+static void launch_layout(const Plan& p, uint32_t assign_grid, const int32_t* ids,
+                          int64_t stride, int64_t nk, int32_t K, int32_t E, int32_t align,
+                          int32_t* H, int32_t* bad, int32_t* counts, int32_t* offsets,
+                          int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
+                          int32_t M, hipStream_t stream) {
     if (p.chunk / kThreads > kBatchSmall)
         launch_layout_b<kBatchLarge>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
                                      offsets, status, pos, row_pair, cap, M, stream);
