@@ -49,6 +49,8 @@ MUTANTS = [
     ("round_scale rounds down",
      "s = (g == 0.5f) ? s : ldexpf(1.0f, e);", "s = (g == 0.5f) ? s : ldexpf(1.0f, e - 1);",
      "test_oracle_lowlatency.py"),
+    ("round_scale rounds an infinite scale",
+     "if (round_scale && isfinite(s)) {", "if (round_scale) {", "test_oracle_lowlatency.py"),
     ("padded layout keeps pairs past M",
      "if (counts[e] < M) {", "if (counts[e] <= M && e * M + counts[e] < E * M) {",
      "test_oracle_lowlatency.py"),
