@@ -89,10 +89,10 @@ template <int W, bool UNIT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint16_t* __restrict__ y, int64_t ys, const float* __restrict__ w, int64_t wst,
     const int32_t* __restrict__ pos, int32_t N, int32_t K, int32_t V, int32_t segs,
-    uint16_t* __restrict__ out, int64_t os, const RowSums rs) {
+    uint16_t* __restrict__ out, int64_t os, const RowSums rs, int64_t first_block) {
     constexpr int E = 2 * W;   // bf16 elements per lane
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    const int64_t gw = (first_block + blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
     const int32_t t = __builtin_amdgcn_readfirstlane((int32_t)(gw / segs));
     if (t >= N) return;
     const int32_t seg = (int32_t)(gw - (int64_t)t * segs);
@@ -205,11 +205,12 @@ constexpr int kEpiThreads = 1024;
 constexpr int kEpiWaves = kEpiThreads / kWave;
 
 template <int VPT>
-__global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const EpilogueArgs a) {
+__global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const EpilogueArgs a,
+                                                                        int32_t first_token) {
     __shared__ float wave_ss[kEpiWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int32_t t = blockIdx.x;
+    const int32_t t = first_token + (int32_t)blockIdx.x;
     const int32_t* prow = a.pos + (int64_t)t * a.K;
     const float* wrow = a.w + (int64_t)t * a.wst;
 
@@ -320,11 +321,12 @@ struct BackwardArgs {
 };
 
 template <int VPT>
-__global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const BackwardArgs a) {
+__global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const BackwardArgs a,
+                                                                        int32_t first_token) {
     __shared__ float part[kEpiWaves][kBatch];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int32_t t = blockIdx.x;
+    const int32_t t = first_token + (int32_t)blockIdx.x;
     const int32_t* prow = a.pos + (int64_t)t * a.K;
     const float* wrow = a.w + (int64_t)t * a.wst;
     const bool want_w = a.gw != nullptr;
@@ -441,12 +443,16 @@ extern "C" int moe_combine(const void* y, int64_t y_row_stride, const float* w,
     auto* oo = static_cast<uint16_t*>(out);
     const RowSums none = {nullptr, 0, nullptr, 0};
     clear_launch_error();
-    if (vec16)
-        combine_kernel<4, false><<<(uint32_t)blocks, kThreads, 0, stream>>>(
-            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none);
-    else
-        combine_kernel<1, false><<<(uint32_t)blocks, kThreads, 0, stream>>>(
-            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none);
+    in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
+        if (vec16)
+            combine_kernel<4, false><<<(uint32_t)count, kThreads, 0, stream>>>(
+                yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none,
+                first);
+        else
+            combine_kernel<1, false><<<(uint32_t)count, kThreads, 0, stream>>>(
+                yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none,
+                first);
+    });
     return check_launch("moe_combine");
 }
 
@@ -487,12 +493,16 @@ extern "C" int moe_dispatch_backward(const void* grad_recv, int64_t grad_recv_ro
     auto* gx = static_cast<uint16_t*>(grad_x);
     const RowSums rs = {grad_recv_w, grad_recv_w_row_stride, grad_w, grad_w_row_stride};
     clear_launch_error();
-    if (vec16)
-        combine_kernel<4, true><<<(uint32_t)blocks, kThreads, 0, stream>>>(
-            gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride, rs);
-    else
-        combine_kernel<1, true><<<(uint32_t)blocks, kThreads, 0, stream>>>(
-            gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride, rs);
+    in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
+        if (vec16)
+            combine_kernel<4, true><<<(uint32_t)count, kThreads, 0, stream>>>(
+                gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride,
+                rs, first);
+        else
+            combine_kernel<1, true><<<(uint32_t)count, kThreads, 0, stream>>>(
+                gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride,
+                rs, first);
+    });
     return check_launch("moe_dispatch_backward");
 }
 
@@ -564,14 +574,17 @@ extern "C" int moe_combine_epilogue(const void* y, int64_t y_row_stride, const f
     a.os = out_row_stride;
     const int vpt = ceil_div<int32_t>(a.V, kEpiThreads);
     clear_launch_error();
-    if (vpt <= 1)
-        combine_epilogue_kernel<1><<<N, kEpiThreads, 0, stream>>>(a);
-    else if (vpt <= 2)
-        combine_epilogue_kernel<2><<<N, kEpiThreads, 0, stream>>>(a);
-    else if (vpt <= 4)
-        combine_epilogue_kernel<4><<<N, kEpiThreads, 0, stream>>>(a);
-    else
-        combine_epilogue_kernel<8><<<N, kEpiThreads, 0, stream>>>(a);
+    in_pieces(N, kMaxLaunchItems / kEpiThreads, [&](int64_t first, int64_t count) {
+        const int32_t t0 = (int32_t)first;
+        if (vpt <= 1)
+            combine_epilogue_kernel<1><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+        else if (vpt <= 2)
+            combine_epilogue_kernel<2><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+        else if (vpt <= 4)
+            combine_epilogue_kernel<4><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+        else
+            combine_epilogue_kernel<8><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+    });
     return check_launch("moe_combine_epilogue");
 }
 
@@ -632,11 +645,14 @@ extern "C" int moe_combine_backward(const void* grad_out, int64_t grad_out_row_s
     a.gws = grad_w_row_stride;
     const int vpt = ceil_div<int32_t>(a.V, kEpiThreads);
     clear_launch_error();
-    if (vpt <= 1)
-        combine_backward_kernel<1><<<N, kEpiThreads, 0, stream>>>(a);
-    else if (vpt <= 2)
-        combine_backward_kernel<2><<<N, kEpiThreads, 0, stream>>>(a);
-    else
-        combine_backward_kernel<4><<<N, kEpiThreads, 0, stream>>>(a);
+    in_pieces(N, kMaxLaunchItems / kEpiThreads, [&](int64_t first, int64_t count) {
+        const int32_t t0 = (int32_t)first;
+        if (vpt <= 1)
+            combine_backward_kernel<1><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+        else if (vpt <= 2)
+            combine_backward_kernel<2><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+        else
+            combine_backward_kernel<4><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+    });
     return check_launch("moe_combine_backward");
 }

@@ -44,12 +44,14 @@ struct DispatchArgs {
 };
 
 template <typename VecT>
-__global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a) {
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a,
+                                                            uint32_t first_block) {
     const int lane = threadIdx.x & (kWave - 1);
-    // Logical workgroup: XCD (blockIdx % 8) takes a contiguous eighth. The
-    // grid is a multiple of 8, so this is a bijection on [0, gridDim.x).
+    // Logical workgroup: XCD (blockIdx % 8) takes a contiguous eighth of this
+    // launch's range. The grid is a multiple of 8, so this is a bijection
+    // onto [first_block, first_block + gridDim.x).
     const uint32_t per_xcd = gridDim.x / kXcds;
-    const uint32_t lb = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const uint32_t lb = first_block + (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     const uint32_t gw = lb * kWavesPerBlock + threadIdx.x / kWave;
     const uint32_t pair = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);   // t*K + k
     if (pair >= (uint32_t)a.N * (uint32_t)a.K) return;
@@ -312,11 +314,15 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
         return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K*segments=%lld waves must be below 2^31",
                     (long long)waves);
     const int64_t blocks = ceil_div<int64_t>(ceil_div<int64_t>(waves, kWavesPerBlock), kXcds) * kXcds;
+    constexpr int64_t kPiece = kMaxLaunchItems / kThreads;
+    static_assert(kPiece % kXcds == 0, "every piece must keep the XCD renumbering a bijection");
     clear_launch_error();
-    if (all16)
-        dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a);
-    else
-        dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a);
+    in_pieces(blocks, kPiece, [&](int64_t first, int64_t count) {
+        if (all16)
+            dispatch_kernel<u32x4><<<(uint32_t)count, kThreads, 0, stream>>>(a, (uint32_t)first);
+        else
+            dispatch_kernel<uint32_t><<<(uint32_t)count, kThreads, 0, stream>>>(a, (uint32_t)first);
+    });
     return check_launch("moe_dispatch");
 }
 
@@ -342,6 +348,9 @@ static int launch_layout_dispatch(const DispatchArgs& a, bool all16, const int32
     f.row_pair = row_pair;
     f.status = status;
     const int64_t blocks = a.N > 0 ? (int64_t)a.N * f.groups : 1;
+    if (blocks > kMaxLaunchItems / kThreads)
+        return fail(MOE_ERR_LIMIT, "%s: %lld workgroups (tokens x payload segments / %d) exceed "
+                    "one launch", who, (long long)blocks, kWavesPerBlock);
     clear_launch_error();
     if (all16)
         layout_dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);

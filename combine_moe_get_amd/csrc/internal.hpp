@@ -30,6 +30,21 @@ inline bool aligned(int64_t v, int64_t a) { return (v & (a - 1)) == 0; }
 template <typename T>
 __host__ __device__ constexpr T ceil_div(T a, T b) { return (a + b - 1) / b; }
 
+// A launch holds fewer than 2^32 work-items along x (HIP refuses a larger
+// grid as an invalid configuration). Kernels whose grid grows with the batch
+// are launched in pieces of at most this many work-items, one after another
+// on the same stream, each told the index of its first workgroup; the
+// one-launch kernels, which need their whole grid at once, refuse larger jobs.
+constexpr int64_t kMaxLaunchItems = (int64_t)1 << 31;
+
+// Calls launch(first, count) for consecutive pieces of [0, total), each of
+// at most `piece` workgroups.
+template <typename F>
+inline void in_pieces(int64_t total, int64_t piece, F&& launch) {
+    for (int64_t first = 0; first < total; first += piece)
+        launch(first, total - first < piece ? total - first : piece);
+}
+
 // 16-byte and 4-byte lane payloads.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -124,9 +124,9 @@ __device__ __forceinline__ void cast_and_store(const Fp8Args& a, uint32_t t, int
     }
 }
 
-__global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a) {
+__global__ __launch_bounds__(256) void dispatch_fp8_kernel(const Fp8Args a, uint32_t first_block) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t gw = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const uint32_t gw = (first_block + blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
     const uint32_t t = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
     if (t >= (uint32_t)a.N) return;
     const int32_t seg = (int32_t)(gw - t * (uint32_t)a.segs);
@@ -347,6 +347,9 @@ static int launch_padded_one_launch(const Fp8Args& a, const int32_t* ids, int64_
     f.row_pair = row_pair;
     f.status = status;
     const int64_t blocks = a.N > 0 ? (int64_t)a.N * f.groups : 1;
+    if (blocks > kMaxLaunchItems / kFusedThreads)
+        return fail(MOE_ERR_LIMIT, "%s: %lld workgroups (tokens x ceil(H/%d)) exceed one launch",
+                    who, (long long)blocks, kFusedWaves * kChanPerWave);
     clear_launch_error();
     dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
     return check_launch(who);
@@ -484,7 +487,9 @@ extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, 
     const int threads = waves < 4096 ? kWave : 4 * kWave;
     const int64_t blocks = ceil_div<int64_t>(waves, threads / kWave);
     clear_launch_error();
-    dispatch_fp8_kernel<<<(uint32_t)blocks, threads, 0, stream>>>(a);
+    in_pieces(blocks, kMaxLaunchItems / threads, [&](int64_t first, int64_t count) {
+        dispatch_fp8_kernel<<<(uint32_t)count, threads, 0, stream>>>(a, (uint32_t)first);
+    });
     return check_launch("moe_dispatch_fp8");
 }
 

@@ -143,8 +143,12 @@ typedef struct moe_field {
  * Rows no pair maps to are left untouched. Two pairs must not share a row
  * (moe_get_layout guarantees it). Alignment: row_bytes, both strides and
  * both pointers must be multiples of 4; when all of them are multiples of
- * 16 (every field), the copy runs in 16-byte vectors. Errors: MOE_ERR_ARG,
- * MOE_ERR_LIMIT, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ * 16 (every field), the copy runs in 16-byte vectors. Limits: 1 <= K <= 32,
+ * N*K < 2^31, and one wave per (pair, 64 vectors of the payload) gives
+ * N*K*ceil(V/64) < 2^31 with V the payload's vectors per token (its bytes
+ * over 16, or over 4 when the 4-byte form runs): a 7456-byte payload
+ * (466 vectors) allows N*K < 2^28. Errors: MOE_ERR_ARG, MOE_ERR_LIMIT,
+ * MOE_ERR_ALIGN, MOE_ERR_HIP.
  */
 int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N, int32_t K,
                  const int32_t* pos, hipStream_t stream);

@@ -127,6 +127,10 @@ def test_dispatch_validation(lib):
     assert L.moe_dispatch(None, 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
     assert L.moe_dispatch(f, 1, -1, 2, P, 0) == lib.MOE_ERR_ARG
     assert L.moe_dispatch(f, 1, 4, 33, P, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_dispatch(f, 1, 1 << 28, 8, P, 0) == lib.MOE_ERR_LIMIT  # N*K = 2^31
+    # one wave per (pair, 64-vector segment): 2^31 waves are refused
+    two = _fields(lib, [(P, 1040, P * 2, 1040, 1040)])                 # 65 vectors: 2 segments
+    assert L.moe_dispatch(two, 1, 1 << 27, 8, P, 0) == lib.MOE_ERR_LIMIT
     assert L.moe_dispatch(f, 1, 4, 2, 0, 0) == lib.MOE_ERR_ARG         # identity needs K == 1
     assert L.moe_dispatch(f, 1, 4, 2, P + 1, 0) == lib.MOE_ERR_ALIGN
     for bad in [(P + 2, 64, P * 2, 64, 64), (P, 66, P * 2, 64, 64), (P, 64, P * 2, 64, 62),
