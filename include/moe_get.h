@@ -17,7 +17,9 @@
  *   - Pointers named as device pointers must be device memory (or memory the
  *     device can access); the `fields` array itself is host memory.
  *   - Every call only enqueues work on `stream` (0 = the null stream) and
- *     returns; it never synchronizes and never waits on the host.
+ *     returns; it never synchronizes and never waits on the host. A call
+ *     may enqueue several kernels in order (the layout takes one or two;
+ *     a job past 2^31 work-items runs in pieces of at most that size).
  *   - The library never allocates, frees or keeps state between calls; all
  *     buffers belong to the caller. Inputs are read-only and must not
  *     overlap outputs.
