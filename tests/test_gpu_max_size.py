@@ -199,3 +199,86 @@ def test_padded_layout_at_the_pair_limit(mg, routed):
     torch.cuda.synchronize()
     say("padded layout: checking")
     check_padded(ids.view(-1), E, M, hist, nbad, counts, pos.view(-1), rp, status)
+
+
+def check_sparse_padded(ids, E, M, counts, pos, rp, status, nbad):
+    """A padded layout over E*M rows of which only a few are used (no
+    drops), checked row by row over all E*M rows in chunks with elementwise
+    operations and gathers from the small per-pair tensors only: every used
+    row r (r % M < counts[r / M]) names a valid pair i = rp[r] with
+    pos[i] = r and expert r / M, the rows of an expert keep (t, k) order,
+    and every other row holds -1."""
+    flat = ids.view(-1).long()
+    pos = pos.view(-1).long()
+    nk, dev = flat.numel(), flat.device
+    v = (flat >= 0) & (flat < E)
+    hist = torch.bincount(flat[v], minlength=E)
+    assert torch.equal(counts.long(), hist) and int(hist.max()) <= M
+    assert tuple(status.tolist()) == (nbad, 0)
+    assert (pos[~v] == -1).all()
+    c = counts.long()
+    used_total = 0
+    for s, e in chunks(E * M):
+        e1 = min(e + 1, E * M)              # one row more, for the order across chunks
+        r = torch.arange(s, e1, device=dev)
+        ex = r // M
+        used = (r % M) < c[ex]
+        i = rp[s:e1].long()
+        assert (i[~used] == -1).all()
+        iu, ru, eu = i[used], r[used], ex[used]
+        assert ((iu >= 0) & (iu < nk)).all()
+        assert torch.equal(pos[iu], ru) and torch.equal(flat[iu], eu)
+        nxt = used[:-1] & used[1:] & (ex[:-1] == ex[1:])
+        assert (i[:-1][nxt] < i[1:][nxt]).all()
+        used_total += int(used[:e - s].sum())
+    assert used_total == int(v.sum())
+
+
+@pytest.mark.timeout(600)
+def test_padded_layout_and_scale_scatter_at_the_row_limit(mg):
+    """E*M = 2^31 - 1024 padded rows (E = 1024, M = 2^21 - 1) for a 4096-token
+    batch: the layout marks every unused row, and moe_scatter_scales places
+    per-token scales into the column-major fp32 [E, 1, M] and UE8M0 int32
+    [E, 1, M] arrays (8 GB each) at the used rows only."""
+    Np, Ep, Mp = 4096, 1024, (1 << 21) - 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    ids = torch.randint(-1, Ep + 1, (Np, K), dtype=torch.int32, device="cuda", generator=g)
+    nbad = int((ids >= Ep).sum())
+    say(f"padded layout E={Ep} M={Mp}: {Ep * Mp} rows")
+    counts = torch.empty(Ep, dtype=torch.int32, device="cuda")
+    pos = torch.empty((Np, K), dtype=torch.int32, device="cuda")
+    rp = torch.empty(Ep * Mp, dtype=torch.int32, device="cuda")
+    status = torch.empty(2, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(mg.moe_layout_workspace_bytes(Np, K, Ep), 256), dtype=torch.uint8,
+                     device="cuda")
+    mg.moe_get_layout_padded(ids, Ep, Mp, counts, pos, rp, ws, status)
+    torch.cuda.synchronize()
+    say("padded layout: checking")
+    check_sparse_padded(ids, Ep, Mp, counts, pos, rp, status, nbad)
+
+    for fmt, H in ((mg.MOE_SCALE_COLS, 128), (mg.MOE_SCALE_UE8M0, 512)):
+        say(f"scale scatter, format {fmt}, H={H}")
+        ts = torch.exp2(torch.randint(-20, 20, (Np, H // 128), device="cuda",
+                                      generator=g).float())
+        canary = -7
+        out = torch.full((Ep, 1, Mp), canary, dtype=torch.int32, device="cuda")
+        if fmt == mg.MOE_SCALE_COLS:
+            out = out.view(torch.float32)
+        mg.moe_scatter_scales(ts, K, H, rp, Ep, Mp, out, fmt)
+        torch.cuda.synchronize()
+        words = out.view(torch.int32).view(-1)
+        tsb = ts.view(torch.int32)
+        if fmt == mg.MOE_SCALE_COLS:
+            want_of = lambda t: tsb[t, 0]
+        else:
+            ex = ((tsb >> 23) & 0xFF).long()
+            packed = ex[:, 0] | (ex[:, 1] << 8) | (ex[:, 2] << 16) | (ex[:, 3] << 24)
+            packed = (packed - (packed >= 1 << 31).long() * (1 << 32)).int()   # as int32 bits
+            want_of = lambda t: packed[t]
+        for s, e in chunks(Ep * Mp):
+            i = rp[s:e].long()
+            used = i >= 0                   # the layout marks every unused row -1 (checked)
+            got = words[s:e]
+            assert (got[~used] == canary).all()
+            assert torch.equal(got[used], want_of(i[used] // K))
