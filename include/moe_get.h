@@ -364,9 +364,10 @@ int moe_unpack_records(const void* records, int64_t record_row_stride, int32_t N
  * Arguments, layouts and alignment are those of the two calls (status may be
  * NULL). counts, offsets and row_pair are written even when N = 0. Limits:
  * N*K <= 8192 (larger batches: the two calls), 1 <= K <= 32,
- * 1 <= E <= 1024, cap >= moe_required_capacity(N, K, E, align), cap < 2^31.
- * Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT, MOE_ERR_CAPACITY,
- * MOE_ERR_HIP.
+ * 1 <= E <= 1024, cap >= moe_required_capacity(N, K, E, align), cap < 2^31,
+ * and at most 2^23 workgroups in the one launch: N * ceil(V / 256) with V
+ * the payload's vectors per token (16 or 4 bytes). Errors: MOE_ERR_ARG,
+ * MOE_ERR_ALIGN, MOE_ERR_LIMIT, MOE_ERR_CAPACITY, MOE_ERR_HIP.
  */
 int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                         int32_t E, int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
@@ -390,7 +391,8 @@ int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N, i
  * moe_dispatch_fp8 with rows_per_expert = M; status[2]). counts, row_pair and
  * status are written even when N = 0. Limits: N*K <= 8192 (larger batches:
  * the two calls), 1 <= K <= 32, 1 <= E <= 1024, M >= 1, E*M < 2^31,
- * H % 128 == 0. Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT,
+ * H % 128 == 0, and at most 2^23 workgroups in the one launch:
+ * N * ceil(H / 4096). Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT,
  * MOE_ERR_HIP.
  */
 int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,

@@ -293,6 +293,9 @@ def test_fused_padded_fp8_validation(lib):
     assert F(*ok(x=P + 8)) == lib.MOE_ERR_ALIGN
     assert F(*ok(ds=264)) == lib.MOE_ERR_ALIGN
     assert F(*ok(pos=P + 2)) == lib.MOE_ERR_ALIGN
+    # one launch: 8192 tokens x ceil(H/4096) workgroups must stay within 2^23
+    H = 4096 * 1024 + 128
+    assert F(*ok(N=8192, K=1, H=H, xs=H, ds=H)) == lib.MOE_ERR_LIMIT
 
 
 def test_builder_loads_without_the_package():
@@ -333,6 +336,10 @@ def test_layout_dispatch_validation(lib):
     assert F(P, 8, 16, 8, 1025, 1, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_LIMIT
     assert F(P, 8, 16, 8, 64, 0, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_ARG       # align 0
     assert F(P, 4, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_ARG       # ids stride
+    # one launch: 8192 tokens x ceil(segments / 4) workgroups must stay within 2^23
+    rb = 16 * 64 * 4 * 1024 + 16                                 # 1025 workgroups per token
+    big = (lib.moe_field * 1)(lib.moe_field(P, rb, P, rb, rb))
+    assert F(P, 1, 8192, 1, 64, 1, P, P, P, P, 8192, P, big, 1, 0) == lib.MOE_ERR_LIMIT
     assert F(P + 2, 8, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 1, 0) == lib.MOE_ERR_ALIGN
     assert F(P, 8, 16, 8, 64, 1, P, P, P, P, 128, P, fld, 0, 0) == lib.MOE_ERR_ARG       # no fields
     bad = (lib.moe_field * 1)(lib.moe_field(P + 2, 64, P, 64, 64))
