@@ -5,7 +5,6 @@ Bar: layout and dispatch bit-exact; combine within 1 bf16 ulp (ulp distance
 on the ordered bf16 encoding, +0 == -0), 0 expected because both sides run
 the same fp32 fma chain in k order and round once to nearest even.
 """
-import os
 import sys
 
 import numpy as np

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import moe_workloads as mw
-from _util import (bf16_bits_to_float, bf16_ulp_diff, f32_fraction, read_cases, round_bf16,
+from _util import (bf16_bits_to_float, f32_fraction, read_cases, round_bf16,
                    round_f32, float_to_bf16_bits_exact)
 
 
