@@ -32,6 +32,13 @@
  *               low_latency_combine takes topk_weights fp32 to weight the
  *               expert outputs. Here: acc = +0; for k ascending with a valid
  *               row, acc = fmaf(w[t,k], y[row,h], acc); out = bf16_rne(acc).
+ *
+ * Parity unpinned: two conventions of the layout rest on this oracle's own
+ * reading, because no page fixes them: the order of rows inside one
+ * expert's segment (ascending (token, k)) and what expert_alignment does
+ * (each segment padded to a multiple of align with unused rows). The tests
+ * pin that the oracle computes exactly these readings (a stable counting
+ * sort, brute force, hand-worked cases), not that the pages require them.
  */
 #include <math.h>
 #include <stdint.h>
