@@ -38,11 +38,14 @@ __host__ __device__ constexpr T ceil_div(T a, T b) { return (a + b - 1) / b; }
 constexpr int64_t kMaxLaunchItems = (int64_t)1 << 31;
 
 // Calls launch(first, count) for consecutive pieces of [0, total), each of
-// at most `piece` workgroups.
+// at most `piece` workgroups, and stops after a launch that failed, so that
+// check_launch reports that failure rather than a later launch's status.
 template <typename F>
 inline void in_pieces(int64_t total, int64_t piece, F&& launch) {
-    for (int64_t first = 0; first < total; first += piece)
+    for (int64_t first = 0; first < total; first += piece) {
         launch(first, total - first < piece ? total - first : piece);
+        if (hipPeekAtLastError() != hipSuccess) return;
+    }
 }
 
 // 16-byte and 4-byte lane payloads.
