@@ -28,6 +28,12 @@
  *     describes the last failure of the calling thread.
  *   - Data-dependent problems (an id >= E) never fail a call: they are
  *     counted into the optional device status word and the entry is skipped.
+ *   - Rows named by pos (as written by the layout calls) are trusted: the
+ *     copy and reduction kernels do not check them against the size of the
+ *     buffers they index, which the caller allocates with the layout's
+ *     capacity. A row outside its buffer is an out-of-bounds access, as an
+ *     invalid pointer would be. (moe_scatter_scales alone reads row_pair
+ *     defensively: entries outside [0, N*K) leave their row untouched.)
  *   - N = 0 is allowed and enqueues only the writes of empty results.
  */
 #ifndef MOE_GET_H
