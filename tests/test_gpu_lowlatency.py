@@ -123,6 +123,50 @@ def test_fp8_dispatch_prefill_rows(mg):
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("fmt", [1, 2], ids=["cols", "ue8m0"])
+def test_fp8_dispatch_prefill_padded_as_benchmarked(mg, fmt):
+    """The low-latency prefill step's dispatch as the benchmark runs it: the
+    prefill routing, x from the benchmark's recipe, the padded layout with
+    M = N = 4096 rows per expert (2^20 rows, 7.5 GB of codes, no drops) and
+    column-major fp32 or UE8M0 scales. Every used row's codes, every scale
+    word (unused ones keep their sentinel) and the layout against the
+    oracle; the codes are compared on the host, row by row."""
+    wl = mw.make("prefill")
+    N, K, E, H = wl.N, wl.K, wl.E, 7168
+    M = N
+    rows = E * M
+    round_scale = fmt == 2
+    x = mw.make_x(N, H, wl.seed + 104729)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    pos_d = torch.empty((N, K), dtype=torch.int32, device="cuda")
+    row_pair = torch.empty(rows, dtype=torch.int32, device="cuda")
+    status = torch.empty(2, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(mg.moe_layout_workspace_bytes(N, K, E), 256), dtype=torch.uint8,
+                     device="cuda")
+    mg.moe_get_layout_padded(dev(wl.ids), E, M, counts, pos_d, row_pair, ws, status)
+    c, pos, rp, st = oracle.layout_padded(wl.ids, E, M)
+    shape = (E, H // 128, M) if fmt == 1 else (E, H // 512, M)
+    sentinel = 3 if fmt == 1 else 0x0B0B0B0B
+    say(f"fp8 prefill padded M={M} format={fmt}")
+    dst = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+    scales = torch.full(shape, sentinel, dtype=torch.float32 if fmt == 1 else torch.int32,
+                        device="cuda")
+    mg.moe_dispatch_fp8(dev(x.view(np.int16)).view(torch.bfloat16), pos_d, K, dst, scales, fmt,
+                        M, round_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), c) and tuple(status.tolist()) == st
+    assert np.array_equal(pos_d.cpu().numpy(), pos)
+    assert np.array_equal(row_pair.cpu().numpy(), rp)
+    used = np.flatnonzero(rp >= 0)
+    # np.zeros leaves the pages of rows the oracle never writes unallocated
+    ref_codes, ref_scales = oracle.dispatch_fp8(
+        x, pos, rows, fmt, M, round_scale, codes=np.zeros((rows, H), np.uint8),
+        scales=np.full(shape, sentinel, np.float32 if fmt == 1 else np.int32))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+    assert np.array_equal(dst.cpu().numpy()[used], ref_codes[used])
+
+
 @pytest.mark.parametrize("H", [128, 384, 640])
 def test_fp8_identity_partial_segments(mg, H):
     """pos = None quantises N tokens in place order; H not a multiple of 512
