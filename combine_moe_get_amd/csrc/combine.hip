@@ -44,6 +44,35 @@ struct Words {
     uint32_t w[W];
 };
 
+// One pair's expert row as a buffer descriptor: the row's bytes from its
+// start, or an empty range for a masked pair (p < 0), whose loads then
+// return 0 without touching memory. Every lane can thus load every pair of
+// a batch unconditionally. That matters: with a load under a branch the
+// compiler cannot count the loads in flight and waits for all of them
+// before issuing the next, one memory round trip per pair.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint16_t* y, int64_t ys,
+                                                          int32_t p, uint32_t row_bytes) {
+    const uint16_t* row = y + (p < 0 ? 0 : (int64_t)p * ys);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row), 0,
+                                             __builtin_bit_cast(int32_t, p < 0 ? 0u : row_bytes),
+                                             kBufferWord3);
+}
+
+// W words of a row at byte offset `off` (non-temporal: each expert-output
+// element is read exactly once).
+template <int W>
+__device__ __forceinline__ Words<W> load_row_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Words<W> v;
+    if constexpr (W == 4) {
+        const u32x4 q = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int32_t)off, 0, kBufferNT));
+        v.w[0] = q.x; v.w[1] = q.y; v.w[2] = q.z; v.w[3] = q.w;
+    } else {
+        v.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int32_t)off, 0, kBufferNT);
+    }
+    return v;
+}
+
 template <int W>
 __device__ __forceinline__ Words<W> load_words(const uint16_t* p) {
     Words<W> r;
@@ -85,7 +114,15 @@ struct RowSums {
 
 // UNIT: every weight is 1 (the dispatch backward): acc + y, which is what
 // fmaf(1, y, acc) computes, without loading weights.
-template <int W, bool UNIT>
+// PIPE: how a lane's K row loads are issued. With PIPE every pair of a batch
+// is loaded unconditionally through row_rsrc, so all of them are in flight
+// together; without it each load sits under a branch on its pair's mask,
+// and the compiler issues the 16-byte ones one after another (each waits
+// for the ones before). Small batches are latency-bound and take the first form (the
+// decode combine: 7.4 -> 5.8 us); at large ones the second measured faster
+// (the prefill combine: 88.2-88.6 us, against 90.1-91.0 us with 2, 4 or 8
+// loads in flight per lane).
+template <int W, bool UNIT, bool PIPE>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint16_t* __restrict__ y, int64_t ys, const float* __restrict__ w, int64_t wst,
     const int32_t* __restrict__ pos, int32_t N, int32_t K, int32_t V, int32_t segs,
@@ -115,6 +152,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 
+    const uint32_t row_bytes = 4u * W * (uint32_t)V;
+    const uint32_t off = (uint32_t)col * 2;
     for (int k0 = 0; k0 < K; k0 += kBatch) {
         int32_t p[kBatch];
         float wk[kBatch];
@@ -124,7 +163,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
             const int k = k0 + j;
             p[j] = k < K ? prow[k] : -1;
             wk[j] = UNIT ? 1.0f : (k < K ? wrow[k] : 0.0f);
-            if (p[j] >= 0) val[j] = load_words<W>(y + (int64_t)p[j] * ys + col);
+            if constexpr (PIPE)
+                val[j] = load_row_words<W>(row_rsrc(y, ys, p[j], row_bytes), off);
+            else if (p[j] >= 0)
+                val[j] = load_words<W>(y + (int64_t)p[j] * ys + col);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
@@ -231,7 +273,8 @@ __global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const Epi
                 const int k = k0 + i;
                 p[i] = k < a.K ? prow[k] : -1;
                 wk[i] = k < a.K ? wrow[k] : 0.0f;
-                if (p[i] >= 0) val[i] = load_words<4>(a.y + (int64_t)p[i] * a.ys + col);
+                val[i] = load_row_words<4>(row_rsrc(a.y, a.ys, p[i], (uint32_t)a.V * 16),
+                                           (uint32_t)col * 2);
             }
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) {
@@ -364,7 +407,8 @@ __global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const Bac
             if (want_w) {
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i)
-                    if (p[i] >= 0) yv[i] = load_words<4>(a.y + (int64_t)p[i] * a.ys + col);
+                    yv[i] = load_row_words<4>(row_rsrc(a.y, a.ys, p[i], (uint32_t)a.V * 16),
+                                              (uint32_t)col * 2);
             }
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) {
@@ -407,6 +451,26 @@ __global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const Bac
     }
 }
 
+// Launches one piece of combine_kernel<W, UNIT, PIPE>.
+template <int W, bool UNIT>
+void launch_combine_piece(bool pipe, int64_t first, int64_t count, hipStream_t stream,
+                          const uint16_t* y, int64_t ys, const float* w, int64_t wst,
+                          const int32_t* pos, int32_t N, int32_t K, int32_t V, int32_t segs,
+                          uint16_t* out, int64_t os, const RowSums& rs) {
+    if (pipe)
+        combine_kernel<W, UNIT, true><<<(uint32_t)count, kThreads, 0, stream>>>(
+            y, ys, w, wst, pos, N, K, V, segs, out, os, rs, first);
+    else
+        combine_kernel<W, UNIT, false><<<(uint32_t)count, kThreads, 0, stream>>>(
+            y, ys, w, wst, pos, N, K, V, segs, out, os, rs, first);
+}
+
+// Jobs of at most this many waves (one per token and 64-vector segment)
+// issue all K row loads of a lane together (PIPE); larger ones one by one.
+// The two measured alike at 1024-2048 tokens of 7168 channels (14336-28672
+// waves).
+constexpr int64_t kPipeMaxWaves = 32768;
+
 }  // namespace
 }  // namespace moe
 
@@ -443,15 +507,16 @@ extern "C" int moe_combine(const void* y, int64_t y_row_stride, const float* w,
     auto* oo = static_cast<uint16_t*>(out);
     const RowSums none = {nullptr, 0, nullptr, 0};
     clear_launch_error();
+    const bool pipe = (int64_t)N * segs <= kPipeMaxWaves;
     in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
         if (vec16)
-            combine_kernel<4, false><<<(uint32_t)count, kThreads, 0, stream>>>(
-                yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none,
-                first);
+            launch_combine_piece<4, false>(pipe, first, count, stream, yy, y_row_stride, w,
+                                           w_row_stride, pos, N, K, V, segs, oo, out_row_stride,
+                                           none);
         else
-            combine_kernel<1, false><<<(uint32_t)count, kThreads, 0, stream>>>(
-                yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, oo, out_row_stride, none,
-                first);
+            launch_combine_piece<1, false>(pipe, first, count, stream, yy, y_row_stride, w,
+                                           w_row_stride, pos, N, K, V, segs, oo, out_row_stride,
+                                           none);
     });
     return check_launch("moe_combine");
 }
@@ -493,15 +558,16 @@ extern "C" int moe_dispatch_backward(const void* grad_recv, int64_t grad_recv_ro
     auto* gx = static_cast<uint16_t*>(grad_x);
     const RowSums rs = {grad_recv_w, grad_recv_w_row_stride, grad_w, grad_w_row_stride};
     clear_launch_error();
+    const bool pipe = (int64_t)N * segs <= kPipeMaxWaves;
     in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
         if (vec16)
-            combine_kernel<4, true><<<(uint32_t)count, kThreads, 0, stream>>>(
-                gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride,
-                rs, first);
+            launch_combine_piece<4, true>(pipe, first, count, stream, gr, grad_recv_row_stride,
+                                          nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride,
+                                          rs);
         else
-            combine_kernel<1, true><<<(uint32_t)count, kThreads, 0, stream>>>(
-                gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride,
-                rs, first);
+            launch_combine_piece<1, true>(pipe, first, count, stream, gr, grad_recv_row_stride,
+                                          nullptr, 0, pos, N, K, V, segs, gx, grad_x_row_stride,
+                                          rs);
     });
     return check_launch("moe_dispatch_backward");
 }

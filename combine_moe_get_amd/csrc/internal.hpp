@@ -51,6 +51,13 @@ inline void in_pieces(int64_t total, int64_t piece, F&& launch) {
 // 16-byte and 4-byte lane payloads.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Third word of a gfx9 buffer descriptor for raw (untyped) loads, which are
+// range-checked against num_records: loads past it return 0 and touch no
+// memory.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: non-temporal (the nt bit on gfx950).
+constexpr int kBufferNT = 2;
+
 // Layouts of small batches in one launch: the layout part of the one-launch
 // dispatch kernels, run without a payload. Every workgroup counts the whole
 // batch itself, which beats the two-kernel layout (histogram, then

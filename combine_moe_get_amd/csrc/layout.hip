@@ -43,9 +43,6 @@ constexpr int kMaxChunks = 64;
 // load round instead of four per pass).
 constexpr int kBatchSmall = 4;
 constexpr int kBatchLarge = 16;
-// Third word of a gfx9 buffer descriptor for raw 32-bit loads (range-checked
-// against num_records: out-of-range loads return 0).
-constexpr int kBufferWord3 = 0x00020000;
 
 struct Plan {
     int32_t chunk;    // pairs per workgroup (multiple of kThreads)
