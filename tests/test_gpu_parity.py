@@ -354,6 +354,36 @@ def test_non_default_stream(mg):
     check_combine(out, y, wl.weights, pos)
 
 
+@pytest.mark.parametrize("Hc,N,K", [(7168, 2340, 8), (7168, 2341, 8), (6, 32768, 12),
+                                     (6, 32769, 12), (7168, 2341, 12)])
+def test_combine_on_both_sides_of_the_load_form_switch(mg, Hc, N, K):
+    """Jobs of at most 32768 waves (one per token and 64-vector segment)
+    issue a lane's row loads together, larger ones one at a time: both forms,
+    16-byte (Hc = 7168: 14 segments per token) and 4-byte (Hc = 6) loads,
+    one and two batches of 8 pairs, masked pairs, for the combine and the
+    dispatch backward (unit weights, weight-gradient sums)."""
+    rng = np.random.default_rng(N * 31 + K)
+    E = 64
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.15] = -1
+    lay = mg.layout(dev(ids), E)
+    pos = check_layout(mg, lay, ids, E)
+    say(f"load forms: Hc={Hc} N={N} K={K}")
+    y = mw.bf16_bits_from_f32(rng.standard_normal((lay.cap, Hc)).astype(np.float32))
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y_d = dev_bf16(y)
+    out = mg.combine(y_d, dev(w), lay)
+    assert check_combine(out, y, w, pos) == 0
+    grw = rng.standard_normal((lay.cap, K)).astype(np.float32)
+    gx = torch.empty((N, Hc), dtype=torch.bfloat16, device="cuda")
+    gw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    mg.moe_dispatch_backward(y_d, lay.pos, gx, dev(grw), gw)
+    torch.cuda.synchronize()
+    ref_x, ref_w = oracle.dispatch_backward(y, pos, grw)
+    assert np.array_equal(host_bf16(gx), ref_x)
+    assert np.array_equal(gw.cpu().numpy().view(np.uint32), ref_w.view(np.uint32))
+
+
 def test_concurrent_streams(mg):
     """The library keeps no state between calls: four streams (default
     priority) each run layout -> dispatch -> combine on their own batch and
