@@ -12,9 +12,10 @@
 //
 // Launch shape: one wave per (token, 64-vector segment of the output row).
 // The token's K rows and weights are wave-uniform scalar loads. Each lane
-// issues the loads of up to 8 expert rows before the first FMA, so every
-// lane keeps 8 x 16 bytes in flight; each load instruction of a wave reads 1
-// KiB contiguous of one expert row. No MFMA: nothing here is a contraction.
+// loads up to 8 expert rows before the first FMA; each load instruction of a
+// wave reads 1 KiB contiguous of one expert row. Small batches issue the 8
+// loads together, large ones one at a time (combine_kernel's PIPE). No MFMA:
+// nothing here is a contraction.
 // The final rounding uses gfx950's v_cvt_pk_bf16_f32 (round to nearest
 // even).
 #include "internal.hpp"
