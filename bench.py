@@ -450,10 +450,12 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     return 2 * nbytes / t / 1e9
 
 
-def cpu_baseline(wl, y, total_bytes, budget_s):
+def cpu_baseline(wl, y, total_bytes, budget_s, epilogue=None):
     """The oracle as it stands, on the host cores: full steps of the same
     workload (layout serial, dispatch and combine OpenMP over tokens) until
-    `budget_s` seconds of work are done."""
+    `budget_s` seconds of work are done. With `epilogue` = (residual, gamma)
+    as bf16 bits, the step's combine is the oracle's combine epilogue with
+    that residual add and RMSNorm, as on the GPU."""
     import oracle
 
     srcs = [wl.records] if wl.records is not None else [a for _, a in wl.fields]
@@ -463,10 +465,14 @@ def cpu_baseline(wl, y, total_bytes, budget_s):
     def one():
         _, _, pos, _, _ = oracle.layout(wl.ids, wl.E)
         oracle.dispatch(srcs, pos, wl.K, dsts=dsts)
-        oracle.combine(y, w, pos)
+        if epilogue is None:
+            oracle.combine(y, w, pos)
+        else:
+            oracle.combine_epilogue(y, w, pos, residual=epilogue[0], gamma=epilogue[1], eps=1e-6)
 
-    return _time_oracle(one, wl, total_bytes, budget_s,
-                        f"full {wl.name} steps (layout+dispatch+combine)")
+    what = "layout+dispatch+combine" if epilogue is None else \
+        "layout+dispatch+combine with residual add and RMSNorm"
+    return _time_oracle(one, wl, total_bytes, budget_s, f"full {wl.name} steps ({what})")
 
 
 def _time_oracle(one, wl, total_bytes, budget_s, what):
@@ -832,7 +838,11 @@ def main():
         elif args.backward:
             result["cpu_baseline"] = cpu_baseline_bwd(wl, host, total, args.cpu_seconds)
         else:
-            result["cpu_baseline"] = cpu_baseline(wl, y, total, args.cpu_seconds)
+            ep = None
+            if args.epilogue:
+                bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)
+                ep = (bits(sets[0].residual), bits(sets[0].gamma))
+            result["cpu_baseline"] = cpu_baseline(wl, y, total, args.cpu_seconds, ep)
     print(json.dumps(result), flush=True)
 
 

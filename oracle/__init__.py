@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-OK, ERR_ARG, ERR_ALIGN, ERR_LIMIT, ERR_CAPACITY = 0, -1, -2, -3, -4
+OK, ERR_ARG, ERR_ALIGN, ERR_LIMIT, ERR_CAPACITY, ERR_NOMEM = 0, -1, -2, -3, -4, -5
 
 
 def build(force: bool = True) -> str:

@@ -33,15 +33,30 @@
  *               expert outputs. Here: acc = +0; for k ascending with a valid
  *               row, acc = fmaf(w[t,k], y[row,h], acc); out = bf16_rne(acc).
  *
- * Parity unpinned: two conventions of the layout rest on this oracle's own
- * reading, because no page fixes them: the order of rows inside one
- * expert's segment (ascending (token, k)) and what expert_alignment does
- * (each segment padded to a multiple of align with unused rows). The tests
- * pin that the oracle computes exactly these readings (a stable counting
- * sort, brute force, hand-worked cases), not that the pages require them.
+ * Parity unpinned: these readings rest on this oracle's own definition,
+ * because no page fixes them. The tests pin that the oracle computes exactly
+ * these readings (a stable counting sort, brute force, hand-worked cases,
+ * exact rationals), not that the pages require them.
+ *  - layout: the order of rows inside one expert's segment (ascending
+ *    (token, k)) and what expert_alignment does (each segment padded to a
+ *    multiple of align with unused rows);
+ *  - combine epilogue: where the two biases enter (after the top-k sum, in
+ *    fp32, bias_0 then bias_1, then the residual); DeepEP's combine kernel
+ *    body is not on the pages;
+ *  - FP8 cast: the floor 2^-126 under the block scale (it decides the scale
+ *    stored for an all-zero or nearly-zero block; the codes of an all-zero
+ *    block are 0 under any positive floor, and that is pinned) and the
+ *    element step as one fp32 division x / s rather than a product with a
+ *    reciprocal;
+ *  - backward: the sums over k as fp32 additions in ascending k (the
+ *    combine's order) and the weight-gradient dot products formed in double
+ *    and rounded once. The pages give the backward's dataflow only; the
+ *    double results are pinned against float64 autograd within their
+ *    rounding bound, the fp32 bit patterns are this reading's.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
@@ -49,6 +64,7 @@
 #define ORC_ERR_ALIGN (-2)
 #define ORC_ERR_LIMIT (-3)
 #define ORC_ERR_CAPACITY (-4)
+#define ORC_ERR_NOMEM (-5) /* a host buffer of the oracle itself could not be allocated */
 
 #define ORC_MAX_K 32
 #define ORC_MAX_E 1024
@@ -254,32 +270,43 @@ int oracle_combine_epilogue(const uint16_t* y, int64_t y_row_stride, const float
                             uint16_t* residual_out, uint16_t* out) {
     if (N < 0 || K < 1 || K > ORC_MAX_K || Hc < 0) return ORC_ERR_ARG;
     if (residual && (!gamma || !residual_out)) return ORC_ERR_ARG;
-#pragma omp parallel for schedule(static)
-    for (int32_t t = 0; t < N; ++t) {
-        float* acc = (float*)__builtin_alloca((size_t)Hc * sizeof(float));
-        for (int32_t h = 0; h < Hc; ++h) {
-            float a = combine_acc(y, y_row_stride, w, w_row_stride, pos, K, t, h);
-            int64_t i = (int64_t)t * Hc + h;
-            if (bias0) a = a + oracle_bf16_to_f32(bias0[i]);
-            if (bias1) a = a + oracle_bf16_to_f32(bias1[i]);
-            if (residual) a = a + oracle_bf16_to_f32(residual[i]);
-            acc[h] = a;
+    /* One Hc-float row per thread, taken from the heap once per parallel
+     * region: a row per token on the stack would grow every thread's stack
+     * by 4*Hc bytes per token until the loop ends. */
+    int oom = 0;
+#pragma omp parallel reduction(|| : oom)
+    {
+        float* acc = (float*)malloc((size_t)(Hc > 0 ? Hc : 1) * sizeof(float));
+        if (!acc) oom = 1;
+#pragma omp for schedule(static)
+        for (int32_t t = 0; t < N; ++t) {
+            if (!acc) continue;
+            for (int32_t h = 0; h < Hc; ++h) {
+                float a = combine_acc(y, y_row_stride, w, w_row_stride, pos, K, t, h);
+                int64_t i = (int64_t)t * Hc + h;
+                if (bias0) a = a + oracle_bf16_to_f32(bias0[i]);
+                if (bias1) a = a + oracle_bf16_to_f32(bias1[i]);
+                if (residual) a = a + oracle_bf16_to_f32(residual[i]);
+                acc[h] = a;
+            }
+            if (!residual) {
+                for (int32_t h = 0; h < Hc; ++h)
+                    out[(int64_t)t * Hc + h] = oracle_f32_to_bf16(acc[h]);
+                continue;
+            }
+            double ss = 0.0;
+            for (int32_t h = 0; h < Hc; ++h) ss += (double)acc[h] * (double)acc[h];
+            double scale = 1.0 / sqrt(ss / (double)Hc + (double)eps);
+            for (int32_t h = 0; h < Hc; ++h) {
+                int64_t i = (int64_t)t * Hc + h;
+                residual_out[i] = oracle_f32_to_bf16(acc[h]);
+                double v = (double)acc[h] * scale * (double)oracle_bf16_to_f32(gamma[h]);
+                out[i] = oracle_bf16_from_f64(v);
+            }
         }
-        if (!residual) {
-            for (int32_t h = 0; h < Hc; ++h) out[(int64_t)t * Hc + h] = oracle_f32_to_bf16(acc[h]);
-            continue;
-        }
-        double ss = 0.0;
-        for (int32_t h = 0; h < Hc; ++h) ss += (double)acc[h] * (double)acc[h];
-        double scale = 1.0 / sqrt(ss / (double)Hc + (double)eps);
-        for (int32_t h = 0; h < Hc; ++h) {
-            int64_t i = (int64_t)t * Hc + h;
-            residual_out[i] = oracle_f32_to_bf16(acc[h]);
-            double v = (double)acc[h] * scale * (double)oracle_bf16_to_f32(gamma[h]);
-            out[i] = oracle_bf16_from_f64(v);
-        }
+        free(acc);
     }
-    return ORC_OK;
+    return oom ? ORC_ERR_NOMEM : ORC_OK;
 }
 
 /* ---------------------------------------------------------------------------

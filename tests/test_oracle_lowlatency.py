@@ -94,6 +94,11 @@ def test_e4m3_saturates_and_decodes(orc):
 # ----------------------------------------------------------------- scale ---
 
 def test_block_scale_rules(orc):
+    """The scale rule of the reading the oracle takes, written out: amax/448
+    as one fp32 division, raised to 2^-126 when smaller, and with round_scale
+    the smallest power of two at or above it. The pages give the cast's
+    inputs and outputs only, so the floor and the division form are parity
+    unpinned; the property tests below pin what the scale must achieve."""
     rng = np.random.default_rng(1)
     for _ in range(200):
         blk = _bits(rng.standard_normal(128) * 10.0 ** rng.integers(-8, 4))
@@ -104,6 +109,45 @@ def test_block_scale_rules(orc):
         m, e = math.frexp(r)
         assert m == 0.5 and r >= s and r < 2 * s            # smallest power of two >= s
     assert orc.fp8_block_scale(np.zeros(128, np.uint16), False) == 2.0 ** -126
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_block_scale_puts_amax_at_the_top_of_e4m3(orc, round_scale):
+    """What a per-block scale is for, checked without its formula: the
+    block's largest magnitude lands at the top of the e4m3 range, so no code
+    saturates and none of the range is wasted. Without round_scale it encodes
+    to 448 itself; with a power-of-two scale (the next power of two at or
+    above the exact one) it lands in [224, 448]. Every other element stays
+    within +-448, and no code is NaN."""
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        f = rng.standard_normal(128) * 10.0 ** rng.integers(-30, 30)
+        blk = _bits(f)
+        codes, scales = orc.dispatch_fp8(blk.reshape(1, 128), np.zeros((1, 1), np.int32), 1,
+                                         orc.SCALE_ROWS, 0, round_scale)
+        dec = np.array([orc.e4m3_to_f32(int(c)) for c in codes[0]])
+        assert not np.isnan(dec).any()
+        assert (np.abs(dec) <= 448.0).all()
+        top = abs(dec[int(np.argmax(np.abs(bf16_bits_to_float(blk))))])
+        if round_scale:
+            assert 224.0 <= top <= 448.0
+            assert math.frexp(float(scales[0, 0]))[0] == 0.5
+        else:
+            assert top == 448.0
+
+
+def test_all_zero_block_encodes_to_zero(orc):
+    """An all-zero block has no magnitude to scale, so any positive finite
+    scale (whatever floor keeps it off zero) gives codes that are all +0 and
+    a dequantised block that is exactly zero. The value the oracle stores
+    for that scale (2^-126) is its own reading: parity unpinned."""
+    for round_scale in (False, True):
+        codes, scales = orc.dispatch_fp8(np.zeros((1, 512), np.uint16), np.zeros((1, 1), np.int32),
+                                         1, orc.SCALE_ROWS, 0, round_scale)
+        assert (codes == 0).all()
+        s = scales[0, :4]
+        assert np.isfinite(s).all() and (s > 0).all()
+    assert orc.e4m3_to_f32(0) == 0.0
 
 
 @pytest.mark.parametrize("round_scale", [False, True])

@@ -58,8 +58,10 @@ def _run(d, pin_files):
                ASAN_OPTIONS="detect_leaks=0:alloc_dealloc_mismatch=0:abort_on_error=0",
                UBSAN_OPTIONS="print_stacktrace=1")
     # -s: a sanitizer report is written to the child's stderr as the process
-    # ends, which pytest's own output capture would swallow
-    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-s", "-m", "not gpu",
+    # ends, which pytest's own output capture would swallow. The slow
+    # full-size thread test runs the unsanitized oracle in a child of its own.
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-s", "-m",
+                           "not gpu and not slow",
                            "-p", "no:cacheprovider"] + [os.path.join(TESTS, f) for f in pin_files],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
 
