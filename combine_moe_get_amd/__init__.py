@@ -10,10 +10,14 @@ if the library has not been built (``python combine_moe_get_amd/build.py``).
 
 Convenience wrappers (``layout``, ``dispatch``, ``combine``,
 ``pack_records``, ``unpack_records``) allocate outputs with torch and call the
-same entry points.
+same entry points. Given ``stream=``, they allocate on that stream, so that
+torch's caching allocator orders any reuse of those blocks (the layout's
+workspace is freed on return) after the kernels that stream runs; inputs
+must be ready on that stream, which is the caller's ordering.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -127,6 +131,13 @@ def _check(rc: int) -> None:
 def _stream(stream=None) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _on(stream):
+    """Context under which a wrapper allocates: the launch stream when one is
+    given (torch's caching allocator then reuses the blocks only in that
+    stream's order), else the current stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _dev(t: Optional[torch.Tensor], name: str) -> int:
@@ -523,34 +534,37 @@ def layout(ids: torch.Tensor, num_experts: int, align: int = 1, cap: Optional[in
         if cap < 0:
             raise MoeError(MOE_ERR_ARG, "invalid layout sizes")
     dev = ids.device
-    if workspace is None:
-        nbytes = moe_layout_workspace_bytes(N, K, num_experts)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    lay = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
-                 torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
-                 torch.empty((N, K), dtype=torch.int32, device=dev),
-                 torch.empty(max(cap, 0), dtype=torch.int32, device=dev),
-                 torch.empty(1, dtype=torch.int32, device=dev), num_experts, align)
-    moe_get_layout(ids, num_experts, align, lay.counts, lay.offsets, lay.pos, lay.row_pair,
-                   workspace, lay.status, stream)
+    with _on(stream):
+        if workspace is None:
+            nbytes = moe_layout_workspace_bytes(N, K, num_experts)
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        lay = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
+                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+                     torch.empty((N, K), dtype=torch.int32, device=dev),
+                     torch.empty(max(cap, 0), dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev), num_experts, align)
+        moe_get_layout(ids, num_experts, align, lay.counts, lay.offsets, lay.pos, lay.row_pair,
+                       workspace, lay.status, stream)
     return lay
 
 
 def dispatch(srcs: Sequence[torch.Tensor], lay: Layout, stream=None) -> List[torch.Tensor]:
     """Receive buffers [cap, ...] of every field, filled at the rows ``lay``
     assigned (other rows are left uninitialized)."""
-    dsts = [torch.empty((lay.cap,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device)
-            for s in srcs]
-    moe_dispatch(srcs, dsts, lay.pos, lay.K, stream)
+    with _on(stream):
+        dsts = [torch.empty((lay.cap,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device)
+                for s in srcs]
+        moe_dispatch(srcs, dsts, lay.pos, lay.K, stream)
     return dsts
 
 
 def combine(y: torch.Tensor, weights: torch.Tensor, lay: Layout,
             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     N = lay.pos.shape[0]
-    if out is None:
-        out = torch.empty((N, y.shape[1]), dtype=torch.bfloat16, device=y.device)
-    moe_combine(y, weights, lay.pos, out, stream)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((N, y.shape[1]), dtype=torch.bfloat16, device=y.device)
+        moe_combine(y, weights, lay.pos, out, stream)
     return out
 
 
@@ -590,9 +604,10 @@ def pack_records(tensors: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
     if any(x.shape[0] != N for x in b):
         raise ValueError("all tensors need the same number of tokens")
     _, rec_bytes = record_offsets([x.shape[1] for x in b])
-    rec = torch.zeros((N, rec_bytes), dtype=torch.uint8, device=tensors[0].device)
-    _check(_lib.moe_pack_records(_record_fields(b, True), len(b), N, _dev(rec, "records"),
-                                 rec_bytes, _stream(stream)))
+    with _on(stream):
+        rec = torch.zeros((N, rec_bytes), dtype=torch.uint8, device=tensors[0].device)
+        _check(_lib.moe_pack_records(_record_fields(b, True), len(b), N, _dev(rec, "records"),
+                                     rec_bytes, _stream(stream)))
     return rec
 
 
@@ -603,10 +618,11 @@ def unpack_records(records: torch.Tensor, like: Sequence[torch.Tensor],
     if not 1 <= len(like) <= MAX_FIELDS:
         raise ValueError("need 1..4 tensors")
     N = records.shape[0]
-    outs = [torch.empty((N,) + tuple(t.shape[1:]), dtype=t.dtype, device=records.device)
-            for t in like]
-    b = [_bytes2d(o) for o in outs]
-    rp, rs = _rows(records, "records") if N else (0, records.shape[1])
-    _check(_lib.moe_unpack_records(rp, rs, N, _record_fields(b, False), len(b),
-                                   _stream(stream)))
+    with _on(stream):
+        outs = [torch.empty((N,) + tuple(t.shape[1:]), dtype=t.dtype, device=records.device)
+                for t in like]
+        b = [_bytes2d(o) for o in outs]
+        rp, rs = _rows(records, "records") if N else (0, records.shape[1])
+        _check(_lib.moe_unpack_records(rp, rs, N, _record_fields(b, False), len(b),
+                                       _stream(stream)))
     return outs

@@ -474,54 +474,75 @@ extern "C" size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E) {
     return workspace_for(make_plan(N, K, E), E);
 }
 
+// Checks of moe_get_layout's arguments other than the workspace (shared with
+// moe_get_layout_noalloc; `fn` names the entry point in the message).
+static int check_layout_args(const char* fn, const int32_t* ids, int64_t ids_row_stride,
+                             int32_t N, int32_t K, int32_t E, int32_t align,
+                             const int32_t* counts, const int32_t* offsets, const int32_t* pos,
+                             const int32_t* row_pair, int64_t cap, const int32_t* status) {
+    if (N < 0 || K < 1 || E < 1 || align < 1)
+        return fail(MOE_ERR_ARG, "%s: need N >= 0, K >= 1, E >= 1, align >= 1 "
+                    "(got N=%d K=%d E=%d align=%d)", fn, N, K, E, align);
+    if (K > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_LIMIT, "%s: K=%d E=%d beyond K <= %d, E <= %d", fn, K, E,
+                    MOE_MAX_TOPK, MOE_MAX_EXPERTS);
+    const int64_t nk = (int64_t)N * K;
+    if (nk >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "%s: N*K=%lld must be below 2^31", fn, (long long)nk);
+    if (N > 0 && (ids == nullptr || pos == nullptr))
+        return fail(MOE_ERR_ARG, "%s: ids and pos must not be NULL", fn);
+    if (N > 0 && ids_row_stride < K)
+        return fail(MOE_ERR_ARG, "%s: ids_row_stride=%lld < K=%d", fn,
+                    (long long)ids_row_stride, K);
+    if (counts == nullptr || offsets == nullptr)
+        return fail(MOE_ERR_ARG, "%s: counts and offsets must not be NULL", fn);
+    const int64_t need = moe_required_capacity(N, K, E, align);
+    if (cap < need)
+        return fail(MOE_ERR_CAPACITY, "%s: cap=%lld below the worst case %lld", fn,
+                    (long long)cap, (long long)need);
+    if (cap >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_LIMIT, "%s: cap=%lld must be below 2^31", fn, (long long)cap);
+    if (cap > 0 && row_pair == nullptr)
+        return fail(MOE_ERR_ARG, "%s: row_pair must not be NULL", fn);
+    if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pos, 4) ||
+        !aligned(row_pair, 4) || !aligned(status, 4))
+        return fail(MOE_ERR_ALIGN, "%s: int32 pointers must be 4-byte aligned", fn);
+    return MOE_OK;
+}
+
+// The layout proper, on validated arguments, with its workspace at H (at
+// least workspace_for(make_plan(N, K, E), E) bytes).
+static int run_layout(const char* fn, const int32_t* ids, int64_t ids_row_stride, int32_t N,
+                      int32_t K, int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
+                      int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* H, int32_t* status,
+                      hipStream_t stream) {
+    const int64_t nk = (int64_t)N * K;
+    if (N > 0 && nk <= kOneLaunchPairs)
+        return layout_one_launch(ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
+                                 row_pair, cap, status, stream);
+    const Plan p = make_plan(N, K, E);
+    clear_launch_error();
+    int32_t* bad = H + (int64_t)p.blocks * E;
+    launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
+                  counts, offsets, status, pos, row_pair, cap, 0, stream);
+    return check_launch(fn);
+}
+
 extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                               int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
                               int32_t* pos, int32_t* row_pair, int64_t cap, void* workspace,
                               size_t workspace_bytes, int32_t* status, hipStream_t stream) {
-    if (N < 0 || K < 1 || E < 1 || align < 1)
-        return fail(MOE_ERR_ARG, "moe_get_layout: need N >= 0, K >= 1, E >= 1, align >= 1 "
-                    "(got N=%d K=%d E=%d align=%d)", N, K, E, align);
-    if (K > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS)
-        return fail(MOE_ERR_LIMIT, "moe_get_layout: K=%d E=%d beyond K <= %d, E <= %d", K, E,
-                    MOE_MAX_TOPK, MOE_MAX_EXPERTS);
-    const int64_t nk = (int64_t)N * K;
-    if (nk >= ((int64_t)1 << 31))
-        return fail(MOE_ERR_LIMIT, "moe_get_layout: N*K=%lld must be below 2^31", (long long)nk);
-    if (N > 0 && (ids == nullptr || pos == nullptr))
-        return fail(MOE_ERR_ARG, "moe_get_layout: ids and pos must not be NULL");
-    if (N > 0 && ids_row_stride < K)
-        return fail(MOE_ERR_ARG, "moe_get_layout: ids_row_stride=%lld < K=%d",
-                    (long long)ids_row_stride, K);
-    if (counts == nullptr || offsets == nullptr)
-        return fail(MOE_ERR_ARG, "moe_get_layout: counts and offsets must not be NULL");
-    const int64_t need = moe_required_capacity(N, K, E, align);
-    if (cap < need)
-        return fail(MOE_ERR_CAPACITY, "moe_get_layout: cap=%lld below the worst case %lld",
-                    (long long)cap, (long long)need);
-    if (cap >= ((int64_t)1 << 31))
-        return fail(MOE_ERR_LIMIT, "moe_get_layout: cap=%lld must be below 2^31", (long long)cap);
-    if (cap > 0 && row_pair == nullptr)
-        return fail(MOE_ERR_ARG, "moe_get_layout: row_pair must not be NULL");
-    if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pos, 4) ||
-        !aligned(row_pair, 4) || !aligned(status, 4))
-        return fail(MOE_ERR_ALIGN, "moe_get_layout: int32 pointers must be 4-byte aligned");
-    const Plan p = make_plan(N, K, E);
-    const size_t ws = workspace_for(p, E);
+    const int rc = check_layout_args("moe_get_layout", ids, ids_row_stride, N, K, E, align,
+                                     counts, offsets, pos, row_pair, cap, status);
+    if (rc != MOE_OK) return rc;
+    const size_t ws = workspace_for(make_plan(N, K, E), E);
     if (workspace == nullptr || workspace_bytes < ws)
         return fail(MOE_ERR_WORKSPACE, "moe_get_layout: workspace of %zu bytes needed, got %zu%s",
                     ws, workspace_bytes, workspace ? "" : " (NULL)");
     if (!aligned(workspace, 4))
         return fail(MOE_ERR_ALIGN, "moe_get_layout: workspace must be 4-byte aligned");
-    if (N > 0 && nk <= kOneLaunchPairs)
-        return layout_one_launch(ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
-                                 row_pair, cap, status, stream);
-
-    clear_launch_error();
-    int32_t* H = static_cast<int32_t*>(workspace);
-    int32_t* bad = H + (int64_t)p.blocks * E;
-    launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
-                  counts, offsets, status, pos, row_pair, cap, 0, stream);
-    return check_launch("moe_get_layout");
+    return run_layout("moe_get_layout", ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
+                      row_pair, cap, static_cast<int32_t*>(workspace), status, stream);
 }
 
 extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,

@@ -354,6 +354,38 @@ def test_non_default_stream(mg):
     check_combine(out, y, wl.weights, pos)
 
 
+def test_explicit_stream_argument(mg):
+    """The allocating wrappers given stream= (not a stream context) allocate
+    on that stream, so blocks they free (the layout's workspace) are not
+    handed to the current stream while the kernels on the given stream still
+    use them. The current stream meanwhile allocates and fills blocks of the
+    workspace's size; every result must still match the oracle."""
+    rng = np.random.default_rng(4242)
+    N, K, E, Hc = 1500, 8, 64, 512
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.1] = -1
+    src = rng.integers(0, 256, size=(N, 272), dtype=np.uint8)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y = mw.bf16_bits_from_f32(rng.standard_normal((N * K, Hc)).astype(np.float32))
+    ids_d, src_d, w_d, y_d = dev(ids), dev(src), dev(w), dev_bf16(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    nbytes = max(mg.moe_layout_workspace_bytes(N, K, E), 256)
+    for rep in range(3):
+        say(f"explicit stream argument, pass {rep}")
+        lay = mg.layout(ids_d, E, stream=s)
+        junk = [torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(8)]
+        (recv,) = mg.dispatch([src_d], lay, stream=s)
+        out = mg.combine(y_d, w_d, lay, stream=s)
+        s.synchronize()
+        pos = check_layout(mg, lay, ids, E)
+        (ref,) = oracle.dispatch([src], pos, K)
+        valid = pos.reshape(-1)[pos.reshape(-1) >= 0]
+        assert np.array_equal(host(recv)[valid], ref[valid])
+        assert check_combine(out, y, w, pos) == 0
+        del junk
+
+
 @pytest.mark.parametrize("Hc,N,K", [(7168, 2340, 8), (7168, 2341, 8), (6, 32768, 12),
                                      (6, 32769, 12), (7168, 2341, 12)])
 def test_combine_on_both_sides_of_the_load_form_switch(mg, Hc, N, K):
