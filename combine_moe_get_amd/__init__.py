@@ -77,6 +77,8 @@ def _load():
     L.moe_layout_workspace_bytes.restype = sz
     L.moe_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, sz, P, P]
     L.moe_get_layout.restype = ctypes.c_int
+    L.moe_get_layout_noalloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, P]
+    L.moe_get_layout_noalloc.restype = ctypes.c_int
     L.moe_dispatch.argtypes = [ctypes.POINTER(moe_field), i32, i32, i32, P, P]
     L.moe_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P]
@@ -197,6 +199,31 @@ def moe_get_layout(ids: torch.Tensor, num_experts: int, align: int, counts: torc
                                _dev(workspace, "workspace"),
                                workspace.numel() * workspace.element_size(),
                                _dev(status, "status"), _stream(stream)))
+
+
+def moe_get_layout_noalloc(ids: torch.Tensor, num_experts: int, align: int,
+                           counts: torch.Tensor, offsets: torch.Tensor, pos: torch.Tensor,
+                           row_pair: torch.Tensor, status: Optional[torch.Tensor] = None,
+                           stream=None) -> None:
+    """moe_get_layout without a workspace argument: the library's own static
+    scratch on the stream's GPU is used instead, so nothing is allocated.
+    Calls that overlap on one GPU race on that scratch."""
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    for n, t in (("counts", counts), ("offsets", offsets), ("pos", pos), ("row_pair", row_pair)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
+        raise TypeError("status must be an int32 tensor with at least one element")
+    N, K = ids.shape
+    if counts.numel() < num_experts or offsets.numel() < num_experts + 1 or pos.numel() < N * K:
+        raise ValueError("counts, offsets or pos too small")
+    ip, istride = _rows(ids, "ids") if N > 0 else (0, K)
+    _check(_lib.moe_get_layout_noalloc(ip, istride, N, K, num_experts, align,
+                                       _dev(counts, "counts"), _dev(offsets, "offsets"),
+                                       _dev(pos, "pos"), _dev(row_pair, "row_pair"),
+                                       row_pair.numel(), _dev(status, "status"),
+                                       _stream(stream)))
 
 
 def moe_get_layout_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: int,

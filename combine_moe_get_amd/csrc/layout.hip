@@ -29,6 +29,8 @@
 // kernels (dispatch.hip, quant.hip), where every workgroup counts the whole
 // batch: below that size it is the faster of the two. H has at most 16384 entries, so the
 // redundant reduction costs each workgroup at most 64 loads per thread.
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace moe {
@@ -543,6 +545,75 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
         return fail(MOE_ERR_ALIGN, "moe_get_layout: workspace must be 4-byte aligned");
     return run_layout("moe_get_layout", ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
                       row_pair, cap, static_cast<int32_t*>(workspace), status, stream);
+}
+
+// ---------------------------------------------------------------------------
+// moe_get_layout_noalloc: moe_get_layout for callers that cannot allocate
+// device memory. Its workspace is `scratch`, a file-scope device array that
+// holds the largest workspace any accepted size needs (kHEntries histogram
+// entries plus kMaxChunks out-of-range counts: 65 792 bytes), one copy per
+// GPU, kept until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: the kernels get the array's device address,
+// looked up once per device with hipGetSymbolAddress. Every call on a GPU
+// shares that GPU's copy, so calls that overlap on one GPU (on different
+// streams) race; calls in one stream's order do not. Nothing in the array
+// has to start at zero: the histogram kernel writes every entry the assign
+// kernel reads.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchWords = (size_t)kHEntries + kMaxChunks;
+static __device__ __align__(256) int32_t scratch[kScratchWords];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device
+}  // namespace
+
+// The device address of `scratch` on the device that runs `stream`, looked
+// up on the first call for that device (with that device current).
+static int scratch_on(hipStream_t stream, int32_t** out) {
+    int dev = -1;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "moe_get_layout_noalloc: no device for the stream: %s",
+                    hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_LIMIT, "moe_get_layout_noalloc: device %d beyond %d devices", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void* ptr = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(MOE_ERR_HIP, "moe_get_layout_noalloc: scratch address on device %d: %s",
+                        dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+extern "C" int moe_get_layout_noalloc(const int32_t* ids, int64_t ids_row_stride, int32_t N,
+                                      int32_t K, int32_t E, int32_t align, int32_t* counts,
+                                      int32_t* offsets, int32_t* pos, int32_t* row_pair,
+                                      int64_t cap, int32_t* status, hipStream_t stream) {
+    const char* fn = "moe_get_layout_noalloc";
+    int rc = check_layout_args(fn, ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
+                               row_pair, cap, status);
+    if (rc != MOE_OK) return rc;
+    const size_t ws = workspace_for(make_plan(N, K, E), E);
+    if (ws > sizeof(scratch))
+        return fail(MOE_ERR_LIMIT, "%s: these sizes need %zu bytes of workspace, beyond the "
+                    "%zu-byte static scratch", fn, ws, sizeof(scratch));
+    int32_t* H = nullptr;
+    rc = scratch_on(stream, &H);
+    if (rc != MOE_OK) return rc;
+    return run_layout(fn, ids, ids_row_stride, N, K, E, align, counts, offsets, pos, row_pair,
+                      cap, H, status, stream);
 }
 
 extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,

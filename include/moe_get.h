@@ -22,7 +22,8 @@
  *     a job past 2^31 work-items runs in pieces of at most that size).
  *   - The library never allocates, frees or keeps state between calls; all
  *     buffers belong to the caller. Inputs are read-only and must not
- *     overlap outputs.
+ *     overlap outputs. (One exception: moe_get_layout_noalloc keeps its
+ *     workspace in a static device array of the library, described there.)
  *   - Return value: MOE_OK (0) or a negative MOE_ERR_* code; argument
  *     problems are found before anything is enqueued. moe_last_error()
  *     describes the last failure of the calling thread.
@@ -116,6 +117,24 @@ int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_
                    int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
                    int32_t* row_pair, int64_t cap, void* workspace, size_t workspace_bytes,
                    int32_t* status, hipStream_t stream);
+
+/*
+ * moe_get_layout without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, outputs, limits and
+ * errors as moe_get_layout, minus the workspace. Its workspace is a static
+ * device array inside the library (65 792 bytes, the most any accepted size
+ * needs, one copy per GPU, held until the process ends); the call allocates
+ * nothing. Every call on one GPU shares that GPU's copy: calls ordered on
+ * one stream are fine, calls that overlap on one GPU (different streams)
+ * race. The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) with that device current; a failure there returns
+ * MOE_ERR_HIP. Errors: those of moe_get_layout except MOE_ERR_WORKSPACE.
+ */
+int moe_get_layout_noalloc(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
+                           int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
+                           int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* status,
+                           hipStream_t stream);
 
 /*
  * One payload field of a dispatch: `row_bytes` bytes per token, read from

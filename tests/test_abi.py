@@ -110,6 +110,26 @@ def test_layout_validation(lib):
         assert _err(lib)
 
 
+def test_layout_noalloc_validation(lib):
+    """The layout that allocates nothing rejects what moe_get_layout rejects
+    (it has no workspace to check), before any GPU call."""
+    L = lib._lib
+    P = 0x1000
+    cases = [
+        ((P, 8, -1, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 33, 64, 1, P, P, P, P, 264, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 1025, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 4, 8, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ARG),
+        ((0, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 63, 0, 0), lib.MOE_ERR_CAPACITY),
+        ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, 0, 0), lib.MOE_ERR_LIMIT),
+    ]
+    for args, code in cases:
+        assert L.moe_get_layout_noalloc(*args) == code, (args, _err(lib))
+        assert "moe_get_layout_noalloc" in _err(lib)
+
+
 def _fields(lib, specs):
     arr = (lib.moe_field * len(specs))()
     for i, s in enumerate(specs):
