@@ -127,6 +127,102 @@ def _per_kernel(directory, counter):
     return out
 
 
+def kernel_name_with_args(name):
+    """A profiled kernel's name with its template arguments but without
+    namespaces and parameters ("void (anonymous namespace)::read_kernel<true,
+    1>(...)" -> "read_kernel<true, 1>")."""
+    import re
+
+    base = re.sub(r"^void\s+", "", name)
+    base = re.sub(r"(?:[\w]*\(anonymous namespace\)::|moe::)", "", base)
+    depth, out = 0, []
+    for ch in base:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def summarize_ceiling_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of every kernel `bench.py --ceilings` runs, from
+    two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), calibrated by the
+    2 GiB device copy that run also makes. Printed as a table."""
+    def rows(counter):
+        out = {}
+        for r in _counter_rows(fetch_dir if counter == "FETCH_SIZE" else write_dir):
+            if r.get("Counter_Name") == counter:
+                out.setdefault(kernel_name_with_args(r["Kernel_Name"]), []).append(
+                    float(r["Counter_Value"]))
+        return out
+
+    fetch, write = rows("FETCH_SIZE"), rows("WRITE_SIZE")
+    known_kib = COPY_BYTES / 1024
+
+    def calib(vals):
+        big = sorted(v for v in vals if v > 0.5 * max(vals, default=0.0))
+        if len(big) < 3:
+            raise SystemExit(f"need the {COPY_KERNEL} launches of copy_bandwidth(), got {vals}")
+        return known_kib / big[len(big) // 2]
+
+    fscale, wscale = calib(fetch.get(COPY_KERNEL, [])), calib(write.get(COPY_KERNEL, []))
+    print(f"copy calibration: FETCH x{fscale:.4f}, WRITE x{wscale:.4f}")
+    print("| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |")
+    print("|---|---|---|---|---|---|")
+    for k in sorted(set(fetch) & set(write)):
+        if k == COPY_KERNEL:
+            continue
+        f, w = float(np.median(fetch[k])), float(np.median(write[k]))
+        print(f"| {k} | {len(fetch[k])} | {f:.0f} | {w:.0f} | {f * fscale * 1024 / 1e6:.2f} | "
+              f"{w * wscale * 1024 / 1e6:.2f} |")
+
+
+def summarize_write_requests(directory):
+    """Write requests that leave the L2 (TCC) for memory, per kernel, from a
+    rocprofv3 --pmc run of TCC_EA0_WRREQ, TCC_EA0_WRREQ_64B and
+    TCC_EA0_WRREQ_DRAM_CREDIT_STALL in its default (SQLite) output: requests
+    per launch, the share that are whole 64-byte requests (the rest are 32
+    bytes), the bytes they carry, and how evenly the requests and the stalls
+    for want of memory credits spread over the 16 x 8 L2 channels (per-channel
+    values, median over launches)."""
+    import glob
+    import sqlite3
+
+    dbs = glob.glob(os.path.join(directory, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {directory}")
+    per = {}   # kernel -> counter -> dispatch -> [per-channel values]
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for disp, name, counter, value in con.execute(
+                "select dispatch_id, name, counter_name, counter_value from pmc_events order by id"):
+            k = kernel_name_with_args(name)
+            per.setdefault(k, {}).setdefault(counter, {}).setdefault(disp, []).append(value)
+        con.close()
+    print("| kernel | launches | write requests / launch | 64-B share | bytes / launch (MB) | "
+          "requests per channel min / median / max | credit-stall cycles per channel "
+          "min / median / max |")
+    print("|---|---|---|---|---|---|---|")
+    for k in sorted(per):
+        c = per[k]
+        if "TCC_EA0_WRREQ" not in c or "TCC_EA0_WRREQ_64B" not in c:
+            continue
+        tot = [sum(v) for v in c["TCC_EA0_WRREQ"].values()]
+        b64 = [sum(v) for v in c["TCC_EA0_WRREQ_64B"].values()]
+        if np.median(tot) < 1000:
+            continue
+        req, r64 = float(np.median(tot)), float(np.median(b64))
+        nbytes = 64 * r64 + 32 * (req - r64)
+        ch = np.median(np.array(list(c["TCC_EA0_WRREQ"].values()), dtype=float), axis=0)
+        st = c.get("TCC_EA0_WRREQ_DRAM_CREDIT_STALL")
+        stall = (np.median(np.array(list(st.values()), dtype=float), axis=0) if st
+                 else np.zeros(1))
+        print(f"| {k} | {len(tot)} | {req:.0f} | {r64 / req:.3f} | {nbytes / 1e6:.2f} | "
+              f"{ch.min():.0f} / {np.median(ch):.0f} / {ch.max():.0f} | "
+              f"{stall.min():.0f} / {np.median(stall):.0f} / {stall.max():.0f} |")
+
+
 def summarize_traffic(fetch_dir, write_dir, workload, command):
     """HBM traffic per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then
     WRITE_SIZE, both in KiB per dispatch), each scaled by what the same
@@ -251,6 +347,7 @@ class BufferSet:
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
         self.pos = torch.empty((N, K), dtype=torch.int32, device=d)
         self.row_pair = torch.empty(cap, dtype=torch.int32, device=d)
+        self.order = torch.empty(N * K, dtype=torch.int32, device=d)   # the dispatch plan
         self.status = torch.empty(1, dtype=torch.int32, device=d)
         self.ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device=d)
         self.dsts = [torch.empty((cap, a.shape[1]), dtype=torch.uint8, device=d) for a in self.srcs]
@@ -269,9 +366,9 @@ class BufferSet:
             fields[i] = mg.moe_field(s.data_ptr(), s.stride(0), t.data_ptr(), t.stride(0), s.shape[1])
         self._fields = fields
         lay = (self.ids.data_ptr(), self.ids_stride, N, K, E, 1, self.counts.data_ptr(), self.offsets.data_ptr(),
-               self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap, self.ws.data_ptr(),
-               self.ws.numel(), self.status.data_ptr(), stream)
-        dis = (fields, len(self.srcs), N, K, self.pos.data_ptr(), stream)
+               self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap, self.order.data_ptr(),
+               self.ws.data_ptr(), self.ws.numel(), self.status.data_ptr(), stream)
+        dis = (fields, len(self.srcs), N, K, self.pos.data_ptr(), self.order.data_ptr(), stream)
         if self.fused:
             ld = (self.ids.data_ptr(), self.ids_stride, N, K, E, 1, self.counts.data_ptr(),
                   self.offsets.data_ptr(), self.pos.data_ptr(), self.row_pair.data_ptr(), self.cap,
@@ -557,6 +654,152 @@ def cpu_baseline_bwd(wl, host, total_bytes, budget_s):
                         f"full {wl.name} backward steps (combine backward + dispatch backward)")
 
 
+def ceilings(torch, mg, mw, reps):
+    """Bandwidth ceilings of the memory patterns the kernels use, timed on
+    this GPU next to the dispatch and combine themselves (prefill shapes):
+    streaming reads, writes and copies of 1 GiB (plain and non-temporal, 1 or
+    8 KiB per wave), the combine's 8:1 read/write mix as a stream, the
+    dispatch's exact stores with no loads, and the combine's exact loads with
+    no stores. The pattern kernels live in libmoe_ceilings.so. Each pattern is
+    launched `reps` times on alternating buffers (well beyond the 256 MB
+    last-level cache), each launch timed with events; the median is kept."""
+    import ctypes
+
+    L = ctypes.CDLL(os.path.join(ROOT, "combine_moe_get_amd", "libmoe_ceilings.so"))
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.ceil_read.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, P, P]
+    L.ceil_write.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, P]
+    L.ceil_copy.argtypes = [P, P, i64, ctypes.c_int, ctypes.c_int, P]
+    L.ceil_mix.argtypes = [P, P, i64, ctypes.c_int, P]
+    L.ceil_dispatch_stores.argtypes = [P, P, P, i32, P, i32, i32, P]
+    L.ceil_combine_reads.argtypes = [P, i64, P, i32, i32, i32, P, P]
+    L.ceil_empty.argtypes = [i32, P]
+    stream = torch.cuda.current_stream().cuda_stream
+    gib = 1 << 30
+    src = [torch.empty(gib, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    dst = [torch.empty(gib, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for t in src:
+        t.fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    wl = mw.make("prefill")
+    y_bits = wl.y()
+    sets = [BufferSet(torch, mg, wl, y_bits) for _ in range(2)]
+    N, K, Hc = wl.N, wl.K, wl.Hc
+    for st in sets:
+        mg.moe_get_layout(st.ids, wl.E, 1, st.counts, st.offsets, st.pos, st.row_pair, st.ws,
+                          st.status, order=st.order)
+    torch.cuda.synchronize()
+    nf = len(sets[0].dsts)
+    fields = []
+    for st in sets:
+        d = (P * nf)(*[t.data_ptr() for t in st.dsts])
+        ds = (i64 * nf)(*[t.stride(0) for t in st.dsts])
+        rb = (i64 * nf)(*[a.shape[1] for a in st.srcs])
+        fields.append((d, ds, rb))
+    R = N * K
+    disp_bytes = R * sum(a.shape[1] for a in sets[0].srcs)
+    y_bytes = R * Hc * 2
+    out_bytes = N * Hc * 2
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("a ceiling kernel failed to launch")
+
+    patterns = [
+        ("read, non-temporal, 1 KiB per wave", "read_kernel<true, 1>", gib,
+         lambda i: ok(L.ceil_read(src[i].data_ptr(), gib, 1, 1, sink.data_ptr(), stream))),
+        ("read, non-temporal, 8 KiB per wave", "read_kernel<true, 8>", gib,
+         lambda i: ok(L.ceil_read(src[i].data_ptr(), gib, 1, 8, sink.data_ptr(), stream))),
+        ("read, plain, 1 KiB per wave", "read_kernel<false, 1>", gib,
+         lambda i: ok(L.ceil_read(src[i].data_ptr(), gib, 0, 1, sink.data_ptr(), stream))),
+        ("write, non-temporal, 1 KiB per wave", "write_kernel<true, 1>", gib,
+         lambda i: ok(L.ceil_write(dst[i].data_ptr(), gib, 1, 1, stream))),
+        ("write, non-temporal, 8 KiB per wave", "write_kernel<true, 8>", gib,
+         lambda i: ok(L.ceil_write(dst[i].data_ptr(), gib, 1, 8, stream))),
+        ("write, plain, 1 KiB per wave", "write_kernel<false, 1>", gib,
+         lambda i: ok(L.ceil_write(dst[i].data_ptr(), gib, 0, 1, stream))),
+        ("copy, non-temporal, 1 KiB per wave (bytes read + written)", "copy_kernel<true, 1>",
+         2 * gib, lambda i: ok(L.ceil_copy(src[i].data_ptr(), dst[i].data_ptr(), gib, 1, 1,
+                                            stream))),
+        ("copy, plain, 1 KiB per wave (bytes read + written)", "copy_kernel<false, 1>", 2 * gib,
+         lambda i: ok(L.ceil_copy(src[i].data_ptr(), dst[i].data_ptr(), gib, 0, 1, stream))),
+        ("8:1 read/write mix, streamed (the combine's bytes)", "mix_kernel", y_bytes + out_bytes,
+         lambda i: ok(L.ceil_mix(sets[i].y.data_ptr(), sets[i].out.data_ptr(), out_bytes // 1024,
+                                 8, stream))),
+        ("dispatch stores, prefill rows from pos, no loads", "dispatch_stores_kernel<true>",
+         disp_bytes, lambda i: ok(L.ceil_dispatch_stores(*fields[i], nf, sets[i].pos.data_ptr(),
+                                                         N, K, stream))),
+        ("dispatch stores, rows in pair order, no loads", "dispatch_stores_kernel<false>", disp_bytes,
+         lambda i: ok(L.ceil_dispatch_stores(*fields[i], nf, None, N, K, stream))),
+        ("combine loads, prefill rows from pos, no stores", "combine_reads_kernel<true>", y_bytes,
+         lambda i: ok(L.ceil_combine_reads(sets[i].y.data_ptr(), Hc, sets[i].pos.data_ptr(), N,
+                                           K, Hc, sink.data_ptr(), stream))),
+        ("combine loads, rows in pair order, no stores", "combine_reads_kernel<false>", y_bytes,
+         lambda i: ok(L.ceil_combine_reads(sets[i].y.data_ptr(), Hc, None, N, K, Hc,
+                                           sink.data_ptr(), stream))),
+        ("moe_dispatch (the product kernel), prefill, pairs in the layout's plan",
+         "dispatch_kernel", algorithmic_bytes(N, K, wl.E, wl.payload_bytes(), Hc, R, sets[0].cap)[1],
+         lambda i: mg.moe_dispatch(sets[i].srcs, sets[i].dsts, sets[i].pos, K,
+                                   order=sets[i].order)),
+        ("moe_dispatch (the product kernel), prefill, pairs in index order", "dispatch_kernel",
+         algorithmic_bytes(N, K, wl.E, wl.payload_bytes(), Hc, R, sets[0].cap)[1],
+         lambda i: mg.moe_dispatch(sets[i].srcs, sets[i].dsts, sets[i].pos, K)),
+        ("moe_combine (the product kernel), prefill", "combine_kernel",
+         algorithmic_bytes(N, K, wl.E, wl.payload_bytes(), Hc, R, sets[0].cap)[2],
+         lambda i: mg.moe_combine(sets[i].y, sets[i].w, sets[i].pos, sets[i].out)),
+    ]
+    res = {}
+    # Launch-bound work, timed as calls per unit of time: `reps` rounds of 50
+    # calls back to back between two events, the median round kept.
+    for st in sets:
+        mg.moe_get_layout(st.ids, wl.E, 1, st.counts, st.offsets, st.pos, st.row_pair, st.ws,
+                          st.status, order=st.order)
+    calls = [
+        ("launch floor: empty kernel, 64 workgroups, per launch", "empty_kernel",
+         lambda: ok(L.ceil_empty(64, stream))),
+        ("moe_get_layout (two launches), prefill, per call", "layout_hist + layout_assign",
+         lambda: mg.moe_get_layout(sets[0].ids, wl.E, 1, sets[0].counts, sets[0].offsets,
+                                   sets[0].pos, sets[0].row_pair, sets[0].ws, sets[0].status,
+                                   order=sets[0].order)),
+    ]
+    for name, kernel, fn in calls:
+        fn()
+        torch.cuda.synchronize()
+        rounds = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(50):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            rounds.append(a.elapsed_time(b) * 1e3 / 50)
+        rounds.sort()
+        res[name] = {"kernel": kernel, "us_median": round(rounds[len(rounds) // 2], 2),
+                     "us_min": round(rounds[0], 2), "us_max": round(rounds[-1], 2)}
+        print(f"ceilings: {name}: {rounds[len(rounds) // 2]:.2f} us", flush=True)
+    for name, kernel, nbytes, fn in patterns:
+        for i in range(4):
+            fn(i % 2)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for r, (a, b) in enumerate(evs):
+            a.record()
+            fn(r % 2)
+            b.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[len(us) // 2]
+        res[name] = {"kernel": kernel, "bytes": int(nbytes), "us_median": round(med, 2),
+                     "us_min": round(us[0], 2), "us_max": round(us[-1], 2),
+                     "gbs": round(nbytes / med / 1e3, 1)}
+        print(f"ceilings: {name}: {med:.2f} us, {nbytes / med / 1e3:.1f} GB/s", flush=True)
+    return {"mode": "ceilings", "unit": "GB/s", "peak_gbs": HBM_PEAK_GBS, "reps": reps,
+            "ceilings": res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -596,6 +839,12 @@ def main():
                          "bench into profiles/traffic.json and exit (no GPU needed)")
     ap.add_argument("--traffic-command", default="",
                     help="the profiled command, recorded next to the figures")
+    ap.add_argument("--write-requests-from", metavar="DIR",
+                    help="summarize a rocprofv3 --pmc run of TCC_EA0_WRREQ, TCC_EA0_WRREQ_64B and "
+                         "TCC_EA0_WRREQ_DRAM_CREDIT_STALL (SQLite output) and exit (no GPU needed)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time the bandwidth ceilings of the kernels' memory patterns "
+                         "(libmoe_ceilings.so) next to moe_dispatch and moe_combine, and exit")
     args = ap.parse_args()
     workload_key = args.config + (f"-lowlatency-{args.scale_format}" if args.lowlatency else
                                   "-backward" if args.backward else "")
@@ -603,6 +852,12 @@ def main():
         workload_key += "-fused"
     if args.scales_staged:
         workload_key += "-staged"
+    if args.write_requests_from:
+        summarize_write_requests(args.write_requests_from)
+        return
+    if args.traffic_from and args.ceilings:
+        summarize_ceiling_traffic(*args.traffic_from)
+        return
     if args.traffic_from:
         summarize_traffic(*args.traffic_from, workload_key, args.traffic_command)
         return
@@ -627,6 +882,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.ceilings:
+        result = ceilings(torch, mg, mw, max(args.steps, 5))
+        # the 2 GiB copy that calibrates the FETCH_SIZE / WRITE_SIZE counters
+        result["copy_ref_gbs"] = round(copy_bandwidth(torch), 1)
+        print(json.dumps(result), flush=True)
+        return
     wl = mw.make(args.config)
     y = wl.y()
     N, K, E, Hc = wl.N, wl.K, wl.E, wl.Hc

@@ -75,11 +75,11 @@ def _load():
     L.moe_required_capacity.restype = i64
     L.moe_layout_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_layout_workspace_bytes.restype = sz
-    L.moe_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, sz, P, P]
+    L.moe_get_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, P, sz, P, P]
     L.moe_get_layout.restype = ctypes.c_int
-    L.moe_get_layout_noalloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, P]
+    L.moe_get_layout_noalloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P, P, P]
     L.moe_get_layout_noalloc.restype = ctypes.c_int
-    L.moe_dispatch.argtypes = [ctypes.POINTER(moe_field), i32, i32, i32, P, P]
+    L.moe_dispatch.argtypes = [ctypes.POINTER(moe_field), i32, i32, i32, P, P, P]
     L.moe_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P]
     L.moe_combine.restype = ctypes.c_int
@@ -177,26 +177,35 @@ def moe_layout_workspace_bytes(N: int, K: int, E: int) -> int:
     return int(_lib.moe_layout_workspace_bytes(N, K, E))
 
 
-def moe_get_layout(ids: torch.Tensor, num_experts: int, align: int, counts: torch.Tensor,
-                   offsets: torch.Tensor, pos: torch.Tensor, row_pair: torch.Tensor,
-                   workspace: torch.Tensor, status: Optional[torch.Tensor] = None,
-                   stream=None) -> None:
-    """ids: int32 [N, K] (rows may be strided, e.g. a view into records)."""
+def _layout_outputs(ids, num_experts, counts, offsets, pos, row_pair, order, status):
     if ids.dtype != torch.int32:
         raise TypeError("ids must be int32")
-    for n, t in (("counts", counts), ("offsets", offsets), ("pos", pos), ("row_pair", row_pair)):
-        if t.dtype != torch.int32 or not t.is_contiguous():
+    for n, t in (("counts", counts), ("offsets", offsets), ("pos", pos), ("row_pair", row_pair),
+                 ("order", order)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
             raise TypeError(f"{n} must be a contiguous int32 tensor")
     if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
         raise TypeError("status must be an int32 tensor with at least one element")
     N, K = ids.shape
     if counts.numel() < num_experts or offsets.numel() < num_experts + 1 or pos.numel() < N * K:
         raise ValueError("counts, offsets or pos too small")
+    if order is not None and order.numel() < N * K:
+        raise ValueError("order needs N*K entries")
+
+
+def moe_get_layout(ids: torch.Tensor, num_experts: int, align: int, counts: torch.Tensor,
+                   offsets: torch.Tensor, pos: torch.Tensor, row_pair: torch.Tensor,
+                   workspace: torch.Tensor, status: Optional[torch.Tensor] = None,
+                   stream=None, order: Optional[torch.Tensor] = None) -> None:
+    """ids: int32 [N, K] (rows may be strided, e.g. a view into records).
+    order (optional, int32 [N*K]) receives the dispatch plan."""
+    _layout_outputs(ids, num_experts, counts, offsets, pos, row_pair, order, status)
+    N, K = ids.shape
     ip, istride = _rows(ids, "ids") if N > 0 else (0, K)
     _check(_lib.moe_get_layout(ip, istride, N, K, num_experts, align, _dev(counts, "counts"),
                                _dev(offsets, "offsets"), _dev(pos, "pos"),
                                _dev(row_pair, "row_pair"), row_pair.numel(),
-                               _dev(workspace, "workspace"),
+                               _dev(order, "order"), _dev(workspace, "workspace"),
                                workspace.numel() * workspace.element_size(),
                                _dev(status, "status"), _stream(stream)))
 
@@ -204,26 +213,18 @@ def moe_get_layout(ids: torch.Tensor, num_experts: int, align: int, counts: torc
 def moe_get_layout_noalloc(ids: torch.Tensor, num_experts: int, align: int,
                            counts: torch.Tensor, offsets: torch.Tensor, pos: torch.Tensor,
                            row_pair: torch.Tensor, status: Optional[torch.Tensor] = None,
-                           stream=None) -> None:
+                           stream=None, order: Optional[torch.Tensor] = None) -> None:
     """moe_get_layout without a workspace argument: the library's own static
     scratch on the stream's GPU is used instead, so nothing is allocated.
     Calls that overlap on one GPU race on that scratch."""
-    if ids.dtype != torch.int32:
-        raise TypeError("ids must be int32")
-    for n, t in (("counts", counts), ("offsets", offsets), ("pos", pos), ("row_pair", row_pair)):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise TypeError(f"{n} must be a contiguous int32 tensor")
-    if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
-        raise TypeError("status must be an int32 tensor with at least one element")
+    _layout_outputs(ids, num_experts, counts, offsets, pos, row_pair, order, status)
     N, K = ids.shape
-    if counts.numel() < num_experts or offsets.numel() < num_experts + 1 or pos.numel() < N * K:
-        raise ValueError("counts, offsets or pos too small")
     ip, istride = _rows(ids, "ids") if N > 0 else (0, K)
     _check(_lib.moe_get_layout_noalloc(ip, istride, N, K, num_experts, align,
                                        _dev(counts, "counts"), _dev(offsets, "offsets"),
                                        _dev(pos, "pos"), _dev(row_pair, "row_pair"),
-                                       row_pair.numel(), _dev(status, "status"),
-                                       _stream(stream)))
+                                       row_pair.numel(), _dev(order, "order"),
+                                       _dev(status, "status"), _stream(stream)))
 
 
 def moe_get_layout_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: int,
@@ -313,17 +314,23 @@ def _as_bytes2d(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
 
 
 def moe_dispatch(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor],
-                 pos: Optional[torch.Tensor], K: int, stream=None) -> None:
+                 pos: Optional[torch.Tensor], K: int, stream=None,
+                 order: Optional[torch.Tensor] = None) -> None:
     """Copy row t of every srcs[f] into rows pos[t, k] of dsts[f].
 
     ``pos=None`` is the identity (K must be 1). Tensors are 2-D with
-    contiguous rows; each field's row size in bytes must match."""
+    contiguous rows; each field's row size in bytes must match. ``order``
+    (the layout's dispatch plan) sets the order the pairs are visited in."""
     N = srcs[0].shape[0] if len(srcs) else 0
     arr = _fields(srcs, dsts, N)
     if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()
                             or pos.numel() != N * K):
         raise ValueError("pos must be a contiguous int32 [N, K] tensor")
-    _check(_lib.moe_dispatch(arr, len(srcs), N, K, _dev(pos, "pos"), _stream(stream)))
+    if order is not None and (order.dtype != torch.int32 or not order.is_contiguous()
+                              or order.numel() != N * K):
+        raise ValueError("order must be a contiguous int32 tensor of N*K entries")
+    _check(_lib.moe_dispatch(arr, len(srcs), N, K, _dev(pos, "pos"), _dev(order, "order"),
+                             _stream(stream)))
 
 
 def _fields(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor], N: int):
@@ -543,6 +550,7 @@ class Layout:
     status: torch.Tensor      # int32 [1]: ids >= E seen
     num_experts: int
     align: int
+    order: Optional[torch.Tensor] = None   # int32 [N*K]: the dispatch plan
 
     @property
     def cap(self) -> int:
@@ -569,9 +577,10 @@ def layout(ids: torch.Tensor, num_experts: int, align: int = 1, cap: Optional[in
                      torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
                      torch.empty((N, K), dtype=torch.int32, device=dev),
                      torch.empty(max(cap, 0), dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev), num_experts, align)
+                     torch.empty(1, dtype=torch.int32, device=dev), num_experts, align,
+                     torch.empty(N * K, dtype=torch.int32, device=dev))
         moe_get_layout(ids, num_experts, align, lay.counts, lay.offsets, lay.pos, lay.row_pair,
-                       workspace, lay.status, stream)
+                       workspace, lay.status, stream, order=lay.order)
     return lay
 
 
@@ -581,7 +590,7 @@ def dispatch(srcs: Sequence[torch.Tensor], lay: Layout, stream=None) -> List[tor
     with _on(stream):
         dsts = [torch.empty((lay.cap,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device)
                 for s in srcs]
-        moe_dispatch(srcs, dsts, lay.pos, lay.K, stream)
+        moe_dispatch(srcs, dsts, lay.pos, lay.K, stream, order=lay.order)
     return dsts
 
 

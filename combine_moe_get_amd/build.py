@@ -1,4 +1,6 @@
-"""Build libmoe_get.so (the C-ABI HIP library) in-tree for gfx950.
+"""Build libmoe_get.so (the C-ABI HIP library) in-tree for gfx950, and
+libmoe_ceilings.so, the bandwidth-ceiling kernels `bench.py --ceilings` times
+(a separate library: the product library holds none of them).
 
     python combine_moe_get_amd/build.py
 
@@ -22,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_get.so")
 SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "quant.hip"]
+CEIL_LIB = os.path.join(PKG, "libmoe_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -54,11 +58,14 @@ def build(verbose: bool = False) -> str:
             print(out, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    srcs = SOURCES + CEIL_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
+    for lib, names in ((LIB, SOURCES), (CEIL_LIB, CEIL_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[n] for n in names],
+              "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -32,6 +32,6 @@ int check_launch(const char* what) {
 
 }  // namespace moe
 
-extern "C" int moe_version(void) { return 100; }
+extern "C" int moe_version(void) { return 200; }
 
 extern "C" const char* moe_last_error(void) { return g_last_error.c_str(); }

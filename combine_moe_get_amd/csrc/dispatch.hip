@@ -29,6 +29,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kXcds = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
+// The layout's plan visits a tile of ~4096 pairs (512 tokens of top-8) in
+// receive-row order, which re-reads each source row from L2 only while the
+// tile's source rows fit in an XCD's 4 MB L2: payloads of at most this many
+// bytes per token. Larger payloads take the pairs in index order, where the
+// K pairs of a token are copied together.
+constexpr int64_t kPlanMaxPayloadBytes = 8192;
 
 struct DispatchArgs {
     const char* src[MOE_MAX_FIELDS];
@@ -37,6 +43,7 @@ struct DispatchArgs {
     int64_t dstride[MOE_MAX_FIELDS];
     int32_t vend[MOE_MAX_FIELDS];  // running end of each field, in vectors
     const int32_t* pos;            // NULL: identity, K == 1
+    const int32_t* order;          // NULL: pairs in index order; else the plan's order (-1: skip)
     int32_t N;
     int32_t K;
     int32_t V;                     // vectors per token over all fields
@@ -53,14 +60,22 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const DispatchArgs a
     const uint32_t per_xcd = gridDim.x / kXcds;
     const uint32_t lb = first_block + (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     const uint32_t gw = lb * kWavesPerBlock + threadIdx.x / kWave;
-    const uint32_t pair = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);   // t*K + k
-    if (pair >= (uint32_t)a.N * (uint32_t)a.K) return;
-    const int32_t seg = (int32_t)(gw - pair * (uint32_t)a.segs);
+    const uint32_t item = __builtin_amdgcn_readfirstlane(gw / (uint32_t)a.segs);
+    if (item >= (uint32_t)a.N * (uint32_t)a.K) return;
+    const int32_t seg = (int32_t)(gw - item * (uint32_t)a.segs);
     const int32_t v = seg * kWave + lane;
     if (v >= a.V) return;
-    const int32_t t = __builtin_amdgcn_readfirstlane(pair / (uint32_t)a.K);
-    const int32_t p = a.pos ? a.pos[pair] : t;
+    // The pair this wave copies (t*K + k): the item-th of the layout's plan,
+    // or the item-th pair itself.
+    const int32_t planned = a.order ? a.order[item] : (int32_t)item;
+    if (planned < 0) return;
+    const uint32_t pair = (uint32_t)planned;
+    // The row is fetched before the token is derived, so that the two
+    // dependent fetches (plan entry, then row) are not held apart by the
+    // division. pos == NULL is the identity, with K == 1.
+    const int32_t p = a.pos ? a.pos[pair] : (int32_t)pair;
     if (p < 0) return;
+    const int32_t t = __builtin_amdgcn_readfirstlane(pair / (uint32_t)a.K);
 
     // Which field this lane's vector belongs to, and its offset inside it.
     const int f1 = v >= a.vend[0], f2 = v >= a.vend[1], f3 = v >= a.vend[2];
@@ -110,6 +125,7 @@ struct FusedLayout {
     int32_t* offsets;
     int32_t* pos;
     int32_t* row_pair;
+    int32_t* order;    // the dispatch plan of a layout-only call (may be NULL)
     int32_t* status;
 };
 
@@ -205,6 +221,9 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
         if (g == 0) {
             f.pos[(int64_t)t * K + k] = p;
             if (p >= 0) f.row_pair[p] = (int32_t)t * K + k;
+            // small batches: the plan is the pairs in index order, -1 for
+            // the masked and out-of-range ones
+            if (f.order != nullptr) f.order[(int64_t)t * K + k] = p >= 0 ? (int32_t)t * K + k : -1;
         }
     }
     if (blockIdx.x == 0) {
@@ -292,14 +311,15 @@ static int prepare_fields(const moe_field* fields, int32_t nfields, int32_t N, D
 }
 
 extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N, int32_t K,
-                            const int32_t* pos, hipStream_t stream) {
+                            const int32_t* pos, const int32_t* order, hipStream_t stream) {
     if (N < 0 || K < 1) return fail(MOE_ERR_ARG, "moe_dispatch: need N >= 0, K >= 1");
     if (K > MOE_MAX_TOPK) return fail(MOE_ERR_LIMIT, "moe_dispatch: K=%d > %d", K, MOE_MAX_TOPK);
     if ((int64_t)N * K >= ((int64_t)1 << 31))
         return fail(MOE_ERR_LIMIT, "moe_dispatch: N*K must be below 2^31");
     if (pos == nullptr && K != 1 && N > 0)
         return fail(MOE_ERR_ARG, "moe_dispatch: pos == NULL (identity) requires K == 1");
-    if (!aligned(pos, 4)) return fail(MOE_ERR_ALIGN, "moe_dispatch: pos must be 4-byte aligned");
+    if (!aligned(pos, 4) || !aligned(order, 4))
+        return fail(MOE_ERR_ALIGN, "moe_dispatch: pos and order must be 4-byte aligned");
     DispatchArgs a{};
     bool all16 = true;
     int64_t total_bytes = 0;
@@ -307,6 +327,7 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     if (rc != MOE_OK) return rc;
     if (N == 0 || total_bytes == 0) return ok();
     a.pos = pos;
+    a.order = total_bytes <= kPlanMaxPayloadBytes ? order : nullptr;
     a.N = N;
     a.K = K;
     const int64_t waves = (int64_t)N * K * a.segs;
@@ -333,8 +354,8 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
 static int launch_layout_dispatch(const DispatchArgs& a, bool all16, const int32_t* ids,
                                   int64_t ids_row_stride, int32_t E, int32_t align,
                                   int32_t* counts, int32_t* offsets, int32_t* pos,
-                                  int32_t* row_pair, int64_t cap, int32_t* status,
-                                  hipStream_t stream, const char* who) {
+                                  int32_t* row_pair, int64_t cap, int32_t* order,
+                                  int32_t* status, hipStream_t stream, const char* who) {
     FusedLayout f;
     f.ids = ids;
     f.ids_stride = ids_row_stride;
@@ -346,6 +367,7 @@ static int launch_layout_dispatch(const DispatchArgs& a, bool all16, const int32
     f.offsets = offsets;
     f.pos = pos;
     f.row_pair = row_pair;
+    f.order = order;
     f.status = status;
     const int64_t blocks = a.N > 0 ? (int64_t)a.N * f.groups : 1;
     if (blocks > kMaxLaunchItems / kThreads)
@@ -396,19 +418,19 @@ extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, i
     a.N = N;
     a.K = K;
     return launch_layout_dispatch(a, all16, ids, ids_row_stride, E, align, counts, offsets, pos,
-                                  row_pair, cap, status, stream, "moe_layout_dispatch");
+                                  row_pair, cap, nullptr, status, stream, "moe_layout_dispatch");
 }
 
 int moe::layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                            int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
-                           int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* status,
-                           hipStream_t stream) {
+                           int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* order,
+                           int32_t* status, hipStream_t stream) {
     DispatchArgs a{};   // no payload: no vectors per token, no segments
     a.pos = nullptr;
     a.N = N;
     a.K = K;
     return launch_layout_dispatch(a, false, ids, ids_row_stride, E, align, counts, offsets, pos,
-                                  row_pair, cap, status, stream, "moe_get_layout");
+                                  row_pair, cap, order, status, stream, "moe_get_layout");
 }
 
 extern "C" int64_t moe_record_offsets(const int64_t* row_bytes, int32_t nfields,
@@ -462,7 +484,7 @@ extern "C" int moe_pack_records(const moe_field* fields, int32_t nfields, int32_
     const int rc = record_fields(fields, nfields, records, record_row_stride, true, f,
                                  "moe_pack_records");
     if (rc != MOE_OK) return rc;
-    return moe_dispatch(f, nfields, N, 1, nullptr, stream);
+    return moe_dispatch(f, nfields, N, 1, nullptr, nullptr, stream);
 }
 
 extern "C" int moe_unpack_records(const void* records, int64_t record_row_stride, int32_t N,
@@ -472,5 +494,5 @@ extern "C" int moe_unpack_records(const void* records, int64_t record_row_stride
     const int rc = record_fields(fields, nfields, records, record_row_stride, false, f,
                                  "moe_unpack_records");
     if (rc != MOE_OK) return rc;
-    return moe_dispatch(f, nfields, N, 1, nullptr, stream);
+    return moe_dispatch(f, nfields, N, 1, nullptr, nullptr, stream);
 }

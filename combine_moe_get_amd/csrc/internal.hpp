@@ -66,7 +66,8 @@ constexpr int kBufferNT = 2;
 constexpr int64_t kOneLaunchPairs = 2048;
 int layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                       int32_t E, int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
-                      int32_t* row_pair, int64_t cap, int32_t* status, hipStream_t stream);
+                      int32_t* row_pair, int64_t cap, int32_t* order, int32_t* status,
+                      hipStream_t stream);
 int layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                              int32_t E, int32_t M, int32_t* counts, int32_t* pos,
                              int32_t* row_pair, int32_t* status, hipStream_t stream);

@@ -149,13 +149,22 @@ __device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[B], int s0
 // expert plus the number of lower lanes in the same step with that expert.
 // In the padded form (M > 0) expert e's segment is rows e*M .. e*M+M-1 and
 // a pair ranked past it is dropped (pos = -1).
+// With a plan (order != nullptr), a valid pair also takes its slot in the
+// plan: the tile's start, plus the tile's pairs of lower experts
+// (tile_scan[e]), plus its rank among the tile's pairs of expert e (its row
+// minus tile_row[e], the row of the first of them). With tile_row ==
+// nullptr the plan is the index order: every pair in its own slot, -1 for
+// the masked ones.
 template <int B>
 __device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[B], int s0, int steps,
                                            int32_t E, int nbits, int32_t* base_row,
                                            uint32_t first, uint32_t nk, int lane,
                                            int32_t* __restrict__ pos,
                                            int32_t* __restrict__ row_pair, int64_t cap,
-                                           int32_t M) {
+                                           int32_t M, int32_t* __restrict__ order = nullptr,
+                                           const int32_t* tile_scan = nullptr,
+                                           const int32_t* tile_row = nullptr,
+                                           int32_t tile_start = 0) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
         if (s0 + j < steps) {   // wave-uniform
@@ -171,6 +180,13 @@ __device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[B], int s0, in
             if (M > 0 && p >= (e + 1) * M) p = -1;   // past the expert's padded segment
             if (i < nk) pos[i] = p;
             if (p >= 0 && p < cap) row_pair[p] = (int32_t)i;
+            if (order != nullptr) {
+                if (tile_row == nullptr) {   // a plan in index order
+                    if (i < nk) order[i] = p >= 0 ? (int32_t)i : -1;
+                } else if (p >= 0) {
+                    order[tile_start + tile_scan[e] + (p - tile_row[e])] = (int32_t)i;
+                }
+            }
         }
     }
 }
@@ -273,19 +289,28 @@ __device__ __forceinline__ void reduce_chunks(const int32_t* __restrict__ H, int
     }
 }
 
-template <int B>
+// PLAN: also write the dispatch plan `order` (see moe_get_layout). Its tiles
+// are the chunks: chunk b's slots list its valid pairs by ascending row
+// (the pairs of lower experts first, then each expert's in (t, k) order),
+// then -1 for its masked and out-of-range pairs. Chunks of more than
+// kPlanMaxTile pairs write the index order instead.
+constexpr int32_t kPlanMaxTile = 4096;
+
+template <int B, bool PLAN>
 __global__ __launch_bounds__(kThreads) void layout_assign(
     const int32_t* __restrict__ ids, int64_t stride, uint32_t nk, uint32_t K, int32_t E,
     int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
     const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ status, int32_t* __restrict__ pos, int32_t* __restrict__ row_pair,
-    int64_t cap, int32_t M) {
+    int64_t cap, int32_t M, int32_t* __restrict__ order) {
     __shared__ int32_t cnt[kWaves * MOE_MAX_EXPERTS];   // per-wave counts, then bases
     __shared__ int32_t total_s[MOE_MAX_EXPERTS];       // valid pairs per expert
     __shared__ int32_t start_s[MOE_MAX_EXPERTS];       // segment start (offsets[e])
     __shared__ int32_t base[MOE_MAX_EXPERTS];          // pairs in earlier chunks, then chunk base
+    __shared__ int32_t tile_scan[PLAN ? MOE_MAX_EXPERTS : 1];   // chunk's pairs of lower experts
     __shared__ int32_t wave_sums[kWaves];
     __shared__ int32_t used_s;
+    __shared__ int32_t tile_valid_s;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int b = blockIdx.x;
@@ -375,7 +400,6 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
         if (b == 0 && status != nullptr && threadIdx.x == 0)
             status[1] = wave_sums[0] + wave_sums[1] + wave_sums[2] + wave_sums[3];
     }
-
     // Per-wave counts of this chunk.
     int32_t* mine = cnt + wave * E;
     count_batch(e_first, 0, steps, E, nbits, mine, lane);
@@ -385,6 +409,30 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
         count_batch(e_reg, s0, steps, E, nbits, mine, lane);
     }
     __syncthreads();
+
+    const bool sorted = PLAN && chunk <= kPlanMaxTile;   // wave-uniform
+    if (sorted) {
+        // The chunk's plan slots: an exclusive scan over the experts of the
+        // chunk's pairs per expert (its four waves' counts) places each
+        // expert's run; the run's first row is the chunk base base[e].
+        // (wave_sums is free: the scan above is behind a barrier.)
+        int32_t t4[4], tsum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = threadIdx.x * 4 + j;
+            t4[j] = e < E ? cnt[e] + cnt[E + e] + cnt[2 * E + e] + cnt[3 * E + e] : 0;
+            tsum += t4[j];
+        }
+        int32_t tvalid = 0;
+        int32_t trun = block_exclusive_scan<kWaves>(tsum, wave_sums, &tvalid);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = threadIdx.x * 4 + j;
+            if (e < E) tile_scan[e] = trun;
+            trun += t4[j];
+        }
+        if (threadIdx.x == 0) tile_valid_s = tvalid;
+    }
 
     // Per-wave bases: segment start + earlier chunks + earlier waves.
     for (int e = threadIdx.x; e < E; e += kThreads) {
@@ -398,11 +446,25 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     }
     __syncthreads();
 
-    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M);
+    int32_t* const plan = PLAN ? order : nullptr;
+    const int32_t tile_start = b * chunk;
+    const int32_t* const run_row = sorted ? base : nullptr;
+    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M, plan,
+               tile_scan, run_row, tile_start);
     for (int s0 = B; s0 < steps; s0 += B) {
         int32_t e_reg[B];
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
-        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M);
+        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M, plan,
+                   tile_scan, run_row, tile_start);
+    }
+    if (sorted) {
+        // The chunk's slots past its valid pairs (its masked and out-of-range
+        // pairs) hold -1.
+        if (active) {
+            const int32_t len = (int32_t)min((int64_t)(b + 1) * chunk, (int64_t)nk) - tile_start;
+            for (int32_t j = tile_valid_s + (int32_t)threadIdx.x; j < len; j += kThreads)
+                order[tile_start + j] = -1;
+        }
     }
 
     // Rows no pair landed in: past the used rows, and alignment padding.
@@ -441,26 +503,31 @@ static void launch_layout_b(const Plan& p, uint32_t assign_grid, const int32_t* 
                             int64_t stride, int64_t nk, int32_t K, int32_t E, int32_t align,
                             int32_t* H, int32_t* bad, int32_t* counts, int32_t* offsets,
                             int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
-                            int32_t M, hipStream_t stream) {
+                            int32_t M, int32_t* order, hipStream_t stream) {
     if (p.blocks > 0)
         layout_hist<B><<<p.blocks, kThreads, 0, stream>>>(ids, stride, (uint32_t)nk, (uint32_t)K,
                                                           E, p.chunk, p.nbits, H, bad);
-    layout_assign<B><<<assign_grid, kThreads, 0, stream>>>(
-        ids, stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H, bad,
-        counts, offsets, status, pos, row_pair, cap, M);
+    if (order != nullptr)
+        layout_assign<B, true><<<assign_grid, kThreads, 0, stream>>>(
+            ids, stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H, bad,
+            counts, offsets, status, pos, row_pair, cap, M, order);
+    else
+        layout_assign<B, false><<<assign_grid, kThreads, 0, stream>>>(
+            ids, stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H, bad,
+            counts, offsets, status, pos, row_pair, cap, M, nullptr);
 }
 
 static void launch_layout(const Plan& p, uint32_t assign_grid, const int32_t* ids,
                           int64_t stride, int64_t nk, int32_t K, int32_t E, int32_t align,
                           int32_t* H, int32_t* bad, int32_t* counts, int32_t* offsets,
                           int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
-                          int32_t M, hipStream_t stream) {
+                          int32_t M, int32_t* order, hipStream_t stream) {
     if (p.chunk / kThreads > kBatchSmall)
         launch_layout_b<kBatchLarge>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
-                                     offsets, status, pos, row_pair, cap, M, stream);
+                                     offsets, status, pos, row_pair, cap, M, order, stream);
     else
         launch_layout_b<kBatchSmall>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
-                                     offsets, status, pos, row_pair, cap, M, stream);
+                                     offsets, status, pos, row_pair, cap, M, order, stream);
 }
 
 extern "C" int64_t moe_required_capacity(int32_t N, int32_t K, int32_t E, int32_t align) {
@@ -481,7 +548,8 @@ extern "C" size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E) {
 static int check_layout_args(const char* fn, const int32_t* ids, int64_t ids_row_stride,
                              int32_t N, int32_t K, int32_t E, int32_t align,
                              const int32_t* counts, const int32_t* offsets, const int32_t* pos,
-                             const int32_t* row_pair, int64_t cap, const int32_t* status) {
+                             const int32_t* row_pair, int64_t cap, const int32_t* order,
+                             const int32_t* status) {
     if (N < 0 || K < 1 || E < 1 || align < 1)
         return fail(MOE_ERR_ARG, "%s: need N >= 0, K >= 1, E >= 1, align >= 1 "
                     "(got N=%d K=%d E=%d align=%d)", fn, N, K, E, align);
@@ -507,7 +575,7 @@ static int check_layout_args(const char* fn, const int32_t* ids, int64_t ids_row
     if (cap > 0 && row_pair == nullptr)
         return fail(MOE_ERR_ARG, "%s: row_pair must not be NULL", fn);
     if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pos, 4) ||
-        !aligned(row_pair, 4) || !aligned(status, 4))
+        !aligned(row_pair, 4) || !aligned(order, 4) || !aligned(status, 4))
         return fail(MOE_ERR_ALIGN, "%s: int32 pointers must be 4-byte aligned", fn);
     return MOE_OK;
 }
@@ -516,26 +584,27 @@ static int check_layout_args(const char* fn, const int32_t* ids, int64_t ids_row
 // least workspace_for(make_plan(N, K, E), E) bytes).
 static int run_layout(const char* fn, const int32_t* ids, int64_t ids_row_stride, int32_t N,
                       int32_t K, int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
-                      int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* H, int32_t* status,
-                      hipStream_t stream) {
+                      int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* order, int32_t* H,
+                      int32_t* status, hipStream_t stream) {
     const int64_t nk = (int64_t)N * K;
     if (N > 0 && nk <= kOneLaunchPairs)
         return layout_one_launch(ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
-                                 row_pair, cap, status, stream);
+                                 row_pair, cap, order, status, stream);
     const Plan p = make_plan(N, K, E);
     clear_launch_error();
     int32_t* bad = H + (int64_t)p.blocks * E;
     launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
-                  counts, offsets, status, pos, row_pair, cap, 0, stream);
+                  counts, offsets, status, pos, row_pair, cap, 0, order, stream);
     return check_launch(fn);
 }
 
 extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                               int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
-                              int32_t* pos, int32_t* row_pair, int64_t cap, void* workspace,
-                              size_t workspace_bytes, int32_t* status, hipStream_t stream) {
+                              int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* order,
+                              void* workspace, size_t workspace_bytes, int32_t* status,
+                              hipStream_t stream) {
     const int rc = check_layout_args("moe_get_layout", ids, ids_row_stride, N, K, E, align,
-                                     counts, offsets, pos, row_pair, cap, status);
+                                     counts, offsets, pos, row_pair, cap, order, status);
     if (rc != MOE_OK) return rc;
     const size_t ws = workspace_for(make_plan(N, K, E), E);
     if (workspace == nullptr || workspace_bytes < ws)
@@ -544,7 +613,7 @@ extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_
     if (!aligned(workspace, 4))
         return fail(MOE_ERR_ALIGN, "moe_get_layout: workspace must be 4-byte aligned");
     return run_layout("moe_get_layout", ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
-                      row_pair, cap, static_cast<int32_t*>(workspace), status, stream);
+                      row_pair, cap, order, static_cast<int32_t*>(workspace), status, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -600,10 +669,11 @@ static int scratch_on(hipStream_t stream, int32_t** out) {
 extern "C" int moe_get_layout_noalloc(const int32_t* ids, int64_t ids_row_stride, int32_t N,
                                       int32_t K, int32_t E, int32_t align, int32_t* counts,
                                       int32_t* offsets, int32_t* pos, int32_t* row_pair,
-                                      int64_t cap, int32_t* status, hipStream_t stream) {
+                                      int64_t cap, int32_t* order, int32_t* status,
+                                      hipStream_t stream) {
     const char* fn = "moe_get_layout_noalloc";
     int rc = check_layout_args(fn, ids, ids_row_stride, N, K, E, align, counts, offsets, pos,
-                               row_pair, cap, status);
+                               row_pair, cap, order, status);
     if (rc != MOE_OK) return rc;
     const size_t ws = workspace_for(make_plan(N, K, E), E);
     if (ws > sizeof(scratch))
@@ -613,7 +683,7 @@ extern "C" int moe_get_layout_noalloc(const int32_t* ids, int64_t ids_row_stride
     rc = scratch_on(stream, &H);
     if (rc != MOE_OK) return rc;
     return run_layout(fn, ids, ids_row_stride, N, K, E, align, counts, offsets, pos, row_pair,
-                      cap, H, status, stream);
+                      cap, order, H, status, stream);
 }
 
 extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
@@ -662,6 +732,6 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     if (grid < p.blocks) grid = p.blocks;
     if (grid < 1) grid = 1;
     launch_layout(p, (uint32_t)grid, ids, ids_row_stride, nk, K, E, 1, H, bad, counts, nullptr,
-                  status, pos, row_pair, cap, M, stream);
+                  status, pos, row_pair, cap, M, nullptr, stream);
     return check_launch("moe_get_layout_padded");
 }

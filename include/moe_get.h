@@ -105,6 +105,21 @@ size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E);
  *        padding rows and rows >= offsets[E].
  *   cap             rows of the receive buffer; must be at least
  *        moe_required_capacity(N, K, E, align) and below 2^31.
+ *   order[N*K]      (device, out, may be NULL) the dispatch plan: the order
+ *        in which moe_dispatch should visit the pairs. It is not part of the
+ *        layout's definition, and any permutation gives the same dispatch:
+ *        every valid pair (pos >= 0) appears once, and the remaining entries
+ *        are -1. Its arrangement is this library's choice for the memory:
+ *        the pairs are taken in tiles of C consecutive pairs, C = N*K / B
+ *        rounded up to a multiple of 256 (B = 64 tiles for E <= 256, 32 for
+ *        E <= 512, 16 beyond), and a tile lists its valid pairs by
+ *        ascending receive row, then -1 for its masked and out-of-range
+ *        pairs. The dispatch then writes each tile's rows as one sorted
+ *        sweep over the receive buffer, while the tile's source rows stay
+ *        in one XCD's L2 (at the prefill shape a tile is 512 pairs, 64
+ *        tokens). Batches of at most 2048 pairs, and batches whose tiles
+ *        would exceed 4096 pairs, take the index order (-1 for the masked
+ *        pairs).
  *   workspace       (device) at least moe_layout_workspace_bytes(N, K, E)
  *        bytes, 4-byte aligned; not shared with a concurrent call.
  *   status          (device, out, may be NULL) number of ids >= E.
@@ -115,8 +130,8 @@ size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E);
  */
 int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K, int32_t E,
                    int32_t align, int32_t* counts, int32_t* offsets, int32_t* pos,
-                   int32_t* row_pair, int64_t cap, void* workspace, size_t workspace_bytes,
-                   int32_t* status, hipStream_t stream);
+                   int32_t* row_pair, int64_t cap, int32_t* order, void* workspace,
+                   size_t workspace_bytes, int32_t* status, hipStream_t stream);
 
 /*
  * moe_get_layout without a workspace argument, for callers that cannot
@@ -133,8 +148,8 @@ int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_
  */
 int moe_get_layout_noalloc(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                            int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
-                           int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* status,
-                           hipStream_t stream);
+                           int32_t* pos, int32_t* row_pair, int64_t cap, int32_t* order,
+                           int32_t* status, hipStream_t stream);
 
 /*
  * One payload field of a dispatch: `row_bytes` bytes per token, read from
@@ -166,6 +181,15 @@ typedef struct moe_field {
  *   pos  (device, [N, K] row-major) rows from moe_get_layout. pos == NULL
  *        means the identity pos[t] = t and requires K == 1: that call packs
  *        separate tensors into records or unpacks records into tensors.
+ *   order  (device, [N*K], may be NULL) the dispatch plan moe_get_layout
+ *        wrote for the same pos: the pairs are copied in the plan's order
+ *        (entries -1 are skipped) instead of in index order. The result is
+ *        the same byte for byte; only the order of the writes changes, which
+ *        the receive buffer's memory prefers (see moe_get_layout). It is a
+ *        hint: payloads above 8 KiB per token are copied in index order
+ *        whatever order holds, because a tile's source rows would no longer
+ *        stay in L2. Entries must be -1 or pair indices below N*K, each
+ *        valid pair exactly once; they are trusted, as pos is.
  *
  * Rows no pair maps to are left untouched. Two pairs must not share a row
  * (moe_get_layout guarantees it). Alignment: row_bytes, both strides and
@@ -178,7 +202,7 @@ typedef struct moe_field {
  * MOE_ERR_ALIGN, MOE_ERR_HIP.
  */
 int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N, int32_t K,
-                 const int32_t* pos, hipStream_t stream);
+                 const int32_t* pos, const int32_t* order, hipStream_t stream);
 
 /*
  * Combine. For every token t < N and h < Hc:

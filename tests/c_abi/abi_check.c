@@ -99,7 +99,7 @@ int main(void) {
     /* device buffers and a stream of our own */
     hipStream_t stream;
     HIP_OK(hipStreamCreate(&stream));
-    int32_t *d_ids, *d_counts, *d_offsets, *d_pos, *d_row_pair, *d_status;
+    int32_t *d_ids, *d_counts, *d_offsets, *d_pos, *d_row_pair, *d_order, *d_status;
     float* d_w;
     void* d_ws;
     uint16_t *d_y, *d_out;
@@ -109,6 +109,7 @@ int main(void) {
     HIP_OK(hipMalloc((void**)&d_offsets, sizeof(int32_t) * (E + 1)));
     HIP_OK(hipMalloc((void**)&d_pos, sizeof(int32_t) * N * K));
     HIP_OK(hipMalloc((void**)&d_row_pair, sizeof(int32_t) * cap));
+    HIP_OK(hipMalloc((void**)&d_order, sizeof(int32_t) * N * K));
     HIP_OK(hipMalloc((void**)&d_status, sizeof(int32_t)));
     HIP_OK(hipMalloc((void**)&d_w, sizeof(float) * N * K));
     HIP_OK(hipMalloc(&d_ws, ws_bytes));
@@ -130,9 +131,9 @@ int main(void) {
         fields[f].row_bytes = row_bytes[f];
     }
 
-    MOE_OK_(moe_get_layout(d_ids, K, N, K, E, 1, d_counts, d_offsets, d_pos, d_row_pair, cap, d_ws,
-                           ws_bytes, d_status, stream));
-    MOE_OK_(moe_dispatch(fields, NF, N, K, d_pos, stream));
+    MOE_OK_(moe_get_layout(d_ids, K, N, K, E, 1, d_counts, d_offsets, d_pos, d_row_pair, cap,
+                           d_order, d_ws, ws_bytes, d_status, stream));
+    MOE_OK_(moe_dispatch(fields, NF, N, K, d_pos, d_order, stream));
     MOE_OK_(moe_combine(d_y, HC, d_w, K, d_pos, N, K, HC, d_out, HC, stream));
     HIP_OK(hipStreamSynchronize(stream));
 
@@ -191,6 +192,17 @@ int main(void) {
         if (d > max_ulp) max_ulp = d;
     }
     bad |= (max_ulp > 1) << 9;
+    /* the dispatch plan: every valid pair once, -1 in the other entries */
+    int32_t* g_order = malloc(sizeof(int32_t) * N * K);
+    int32_t* seen = calloc(N * K, sizeof(int32_t));
+    HIP_OK(hipMemcpy(g_order, d_order, sizeof(int32_t) * N * K, hipMemcpyDeviceToHost));
+    int n_skip = 0, n_valid = 0;
+    for (int i = 0; i < N * K; ++i) {
+        n_valid += pos[i] >= 0;
+        if (g_order[i] < 0) { ++n_skip; continue; }
+        if (g_order[i] >= N * K || pos[g_order[i]] < 0 || seen[g_order[i]]++) bad |= 1 << 10;
+    }
+    bad |= (n_skip != N * K - n_valid) << 10;
     if (bad) {
         fprintf(stderr, "abi_check: mismatch mask 0x%x (max combine ulp %d)\n", bad, max_ulp);
         return 1;

@@ -66,7 +66,7 @@ def lib():
 
 
 def test_version_and_sizes(lib):
-    assert lib.version() >= 100
+    assert lib.version() >= 200
     assert lib.moe_required_capacity(4096, 8, 256, 1) == 32768
     assert lib.moe_required_capacity(4, 2, 3, 2) == 11
     assert lib.moe_required_capacity(-1, 8, 256, 1) == -1
@@ -89,21 +89,22 @@ def test_layout_validation(lib):
     P = 0x1000  # a fake, aligned pointer: validation must fail before any use
     ws = lib.moe_layout_workspace_bytes(8, 8, 64)
     cases = [
-        ((P, 8, -1, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),
-        ((P, 8, 8, 0, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),
-        ((P, 8, 8, 33, 64, 1, P, P, P, P, 264, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
-        ((P, 8, 8, 8, 1025, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
-        ((P, 8, 8, 8, 64, 0, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),
-        ((P, 4, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),      # stride < K
-        ((0, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ARG),      # NULL ids
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 63, P, ws, 0, 0), lib.MOE_ERR_CAPACITY),
-        ((P, 8, 8, 8, 64, 2, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_CAPACITY), # padding room
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, ws, 0, 0), lib.MOE_ERR_WORKSPACE),
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws - 4, 0, 0), lib.MOE_ERR_WORKSPACE),
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P + 2, ws, 0, 0), lib.MOE_ERR_ALIGN),
-        ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, P, ws, 0, 0), lib.MOE_ERR_ALIGN),
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 1 << 31, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
-        ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, -1, 8, 64, 1, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 0, 64, 1, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 33, 64, 1, P, P, P, P, 264, 0, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 1025, 1, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 64, 0, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 4, 8, 8, 64, 1, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_ARG),      # stride < K
+        ((0, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_ARG),      # NULL ids
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 63, 0, P, ws, 0, 0), lib.MOE_ERR_CAPACITY),
+        ((P, 8, 8, 8, 64, 2, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_CAPACITY), # padding room
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0, ws, 0, 0), lib.MOE_ERR_WORKSPACE),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, P, ws - 4, 0, 0), lib.MOE_ERR_WORKSPACE),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, P + 2, ws, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, P, ws, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 1 << 31, 0, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, 0, P, ws, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 64, P + 2, P, ws, 0, 0), lib.MOE_ERR_ALIGN),  # order
     ]
     for args, code in cases:
         assert L.moe_get_layout(*args) == code, (args, _err(lib))
@@ -116,14 +117,14 @@ def test_layout_noalloc_validation(lib):
     L = lib._lib
     P = 0x1000
     cases = [
-        ((P, 8, -1, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ARG),
-        ((P, 8, 8, 33, 64, 1, P, P, P, P, 264, 0, 0), lib.MOE_ERR_LIMIT),
-        ((P, 8, 8, 8, 1025, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_LIMIT),
-        ((P, 4, 8, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ARG),
-        ((0, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ARG),
-        ((P, 8, 8, 8, 64, 1, P, P, P, P, 63, 0, 0), lib.MOE_ERR_CAPACITY),
-        ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0), lib.MOE_ERR_ALIGN),
-        ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, -1, 8, 64, 1, P, P, P, P, 64, 0, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 33, 64, 1, P, P, P, P, 264, 0, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 8, 8, 8, 1025, 1, P, P, P, P, 64, 0, 0, 0), lib.MOE_ERR_LIMIT),
+        ((P, 4, 8, 8, 64, 1, P, P, P, P, 64, 0, 0, 0), lib.MOE_ERR_ARG),
+        ((0, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0, 0), lib.MOE_ERR_ARG),
+        ((P, 8, 8, 8, 64, 1, P, P, P, P, 63, 0, 0, 0), lib.MOE_ERR_CAPACITY),
+        ((P + 2, 8, 8, 8, 64, 1, P, P, P, P, 64, 0, 0, 0), lib.MOE_ERR_ALIGN),
+        ((P, 8, 1 << 28, 8, 64, 1, P, P, P, P, 1 << 31, 0, 0, 0), lib.MOE_ERR_LIMIT),
     ]
     for args, code in cases:
         assert L.moe_get_layout_noalloc(*args) == code, (args, _err(lib))
@@ -142,27 +143,28 @@ def test_dispatch_validation(lib):
     P = 0x10000
     good = (P, 64, P * 2, 64, 64)
     f = _fields(lib, [good])
-    assert L.moe_dispatch(f, 0, 4, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(f, 5, 4, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(None, 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(f, 1, -1, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(f, 1, 4, 33, P, 0) == lib.MOE_ERR_LIMIT
-    assert L.moe_dispatch(f, 1, 1 << 28, 8, P, 0) == lib.MOE_ERR_LIMIT  # N*K = 2^31
+    assert L.moe_dispatch(f, 0, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(f, 5, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(None, 1, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(f, 1, -1, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(f, 1, 4, 33, P, 0, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_dispatch(f, 1, 1 << 28, 8, P, 0, 0) == lib.MOE_ERR_LIMIT  # N*K = 2^31
     # one wave per (pair, 64-vector segment): 2^31 waves are refused
     two = _fields(lib, [(P, 1040, P * 2, 1040, 1040)])                 # 65 vectors: 2 segments
-    assert L.moe_dispatch(two, 1, 1 << 27, 8, P, 0) == lib.MOE_ERR_LIMIT
-    assert L.moe_dispatch(f, 1, 4, 2, 0, 0) == lib.MOE_ERR_ARG         # identity needs K == 1
-    assert L.moe_dispatch(f, 1, 4, 2, P + 1, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_dispatch(two, 1, 1 << 27, 8, P, 0, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_dispatch(f, 1, 4, 2, 0, 0, 0) == lib.MOE_ERR_ARG         # identity needs K == 1
+    assert L.moe_dispatch(f, 1, 4, 2, P + 1, 0, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_dispatch(f, 1, 4, 2, P, P + 2, 0) == lib.MOE_ERR_ALIGN    # order
     for bad in [(P + 2, 64, P * 2, 64, 64), (P, 66, P * 2, 64, 64), (P, 64, P * 2, 64, 62),
                 (P, 64, P * 2 + 6, 64, 64)]:
-        assert L.moe_dispatch(_fields(lib, [bad]), 1, 4, 2, P, 0) == lib.MOE_ERR_ALIGN, bad
-    assert L.moe_dispatch(_fields(lib, [(P, 32, P * 2, 64, 64)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(_fields(lib, [(P, 64, P * 2, 32, 64)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(_fields(lib, [(0, 64, P * 2, 64, 64)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
-    assert L.moe_dispatch(_fields(lib, [(P, -1, P, 64, -16)]), 1, 4, 2, P, 0) == lib.MOE_ERR_ARG
+        assert L.moe_dispatch(_fields(lib, [bad]), 1, 4, 2, P, 0, 0) == lib.MOE_ERR_ALIGN, bad
+    assert L.moe_dispatch(_fields(lib, [(P, 32, P * 2, 64, 64)]), 1, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(_fields(lib, [(P, 64, P * 2, 32, 64)]), 1, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(_fields(lib, [(0, 64, P * 2, 64, 64)]), 1, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
+    assert L.moe_dispatch(_fields(lib, [(P, -1, P, 64, -16)]), 1, 4, 2, P, 0, 0) == lib.MOE_ERR_ARG
     # nothing to copy: returns before any launch
-    assert L.moe_dispatch(f, 1, 0, 2, P, 0) == lib.MOE_OK
-    assert L.moe_dispatch(_fields(lib, [(P, 64, P, 64, 0)]), 1, 4, 2, P, 0) == lib.MOE_OK
+    assert L.moe_dispatch(f, 1, 0, 2, P, 0, 0) == lib.MOE_OK
+    assert L.moe_dispatch(_fields(lib, [(P, 64, P, 64, 0)]), 1, 4, 2, P, 0, 0) == lib.MOE_OK
 
 
 def test_combine_validation(lib):

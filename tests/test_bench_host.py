@@ -116,3 +116,45 @@ def test_source_hash_ignores_comments_not_code(tmp_path):
     assert bench.source_hash(str(a)) == h
     a.write_text("// header\n__global__ void k(int* p) {\n    p[0] = 2;  /* one */\n}\n")
     assert bench.source_hash(str(a)) != h
+
+
+def test_kernel_names_keep_template_arguments():
+    k = bench.kernel_name_with_args
+    assert k("void (anonymous namespace)::read_kernel<true, 1>(unsigned int __vector(4) const*, "
+             "long, unsigned int*)") == "read_kernel<true, 1>"
+    assert k("(anonymous namespace)::mix_kernel(unsigned int __vector(4) const*, long, int)") == \
+        "mix_kernel"
+    assert k("void moe::(anonymous namespace)::combine_kernel<4, false, false>(unsigned short "
+             "const*, long)") == "combine_kernel<4, false, false>"
+    assert k("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_write_request_summary(tmp_path, capsys):
+    """Per-channel counter rows of a rocprofv3 database become requests per
+    launch, the 64-byte share, bytes, and the channel spread."""
+    import sqlite3
+
+    con = sqlite3.connect(tmp_path / "q_results.db")
+    con.execute("create table pmc_events (id integer primary key, dispatch_id int, name text, "
+                "counter_name text, counter_value real)")
+    name = "void moe::(anonymous namespace)::dispatch_kernel<int>(Args)"
+    rows = []
+    for disp in (1, 2):
+        for ch in range(128):
+            rows += [(disp, name, "TCC_EA0_WRREQ", 100.0 + ch % 2),
+                     (disp, name, "TCC_EA0_WRREQ_64B", 90.0),
+                     (disp, name, "TCC_EA0_WRREQ_DRAM_CREDIT_STALL", float(ch))]
+    con.executemany("insert into pmc_events (dispatch_id, name, counter_name, counter_value) "
+                    "values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    bench.summarize_write_requests(str(tmp_path))
+    out = capsys.readouterr().out.splitlines()
+    line = next(l for l in out if l.startswith("| dispatch_kernel<int>"))
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    req = 64 * 100 + 64 * 101
+    b64 = 128 * 90
+    assert cells[1] == "2" and cells[2] == str(req)
+    assert cells[3] == f"{b64 / req:.3f}"
+    assert cells[4] == f"{(64 * b64 + 32 * (req - b64)) / 1e6:.2f}"
+    assert cells[5] == "100 / 100 / 101" and cells[6] == "0 / 64 / 127"

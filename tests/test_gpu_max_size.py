@@ -11,8 +11,10 @@ the GPU in chunks:
     unused rows -1;
   * inside a segment row_pair increases (the stable order), and in the
     padded form every dropped pair comes after its expert's last kept one.
-A stable counting sort is the only layout with all of these. The dispatch
-and the combine then run on that layout with 16-byte rows: every received
+A stable counting sort is the only layout with all of these. The layout's
+dispatch plan must list every valid pair once (each used row hit once). The
+dispatch (in the plan's order) and the combine then run on that layout with
+16-byte rows: every received
 row equals its token's row (compared on the host), and with small-integer
 payloads and power-of-two weights every step of the combine is exact, so its
 output equals bf16(x * sum of the token's valid weights).
@@ -90,6 +92,24 @@ def check_layout(flat, E, hist, nbad, counts, offsets, pos, rp, status):
     return R
 
 
+def check_plan(order, pos, R):
+    """The dispatch plan: every valid pair once (each of the R used rows is
+    hit by exactly one entry), -1 in the other NK - R entries."""
+    hits = torch.zeros(R, dtype=torch.int32, device=order.device)
+    nskip = 0
+    for s, e in chunks(order.numel()):
+        o = order[s:e].long()
+        v = o >= 0
+        assert (o[~v] == -1).all()
+        ov = o[v]
+        assert ((ov >= 0) & (ov < NK)).all()
+        rows = pos[ov].long()
+        assert ((rows >= 0) & (rows < R)).all()
+        hits.index_add_(0, rows, torch.ones_like(rows, dtype=torch.int32))
+        nskip += int((~v).sum())
+    assert bool((hits == 1).all()) and nskip == order.numel() - R
+
+
 def check_padded(flat, E, M, hist, nbad, counts, pos, rp, status):
     """The padded layout's defining properties; every expert must overflow
     its M rows (so each has a last kept pair to compare the dropped with)."""
@@ -149,13 +169,17 @@ def test_layout_dispatch_combine_at_the_pair_limit(mg, routed):
     check_layout(ids.view(-1), E, hist, nbad, lay.counts, lay.offsets, lay.pos.view(-1),
                  lay.row_pair, lay.status[0])
 
-    say("dispatch of 16-byte rows")
+    say("layout: checking the dispatch plan")
+    check_plan(lay.order, lay.pos.view(-1), int(lay.offsets[E]))
+    torch.cuda.empty_cache()
+
+    say("dispatch of 16-byte rows in the plan's order")
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
     x = torch.randint(-16, 17, (N, 8), dtype=torch.int16, device="cuda",
                       generator=g).to(torch.bfloat16)
     y = torch.empty((NK, 8), dtype=torch.bfloat16, device="cuda")
-    mg.moe_dispatch([x], [y], lay.pos, K)
+    mg.moe_dispatch([x], [y], lay.pos, K, order=lay.order)
     torch.cuda.synchronize()
     # Used row r holds the row of token row_pair[r] / K (row_pair inverts
     # pos, checked above). Compared on the host for the first, a middle and

@@ -60,6 +60,34 @@ def check_layout(mg, lay, ids_np, E, align=1, cap=None):
     return p
 
 
+def check_plan(order_d, pos_np, tile=None):
+    """The layout's dispatch plan: every valid pair (pos >= 0) exactly once,
+    -1 in the other entries. With `tile` (pairs per tile, where the header
+    documents it), also its arrangement: each tile lists pairs of its own
+    range, valid ones first and by ascending receive row."""
+    o = host(order_d).reshape(-1)
+    p = pos_np.reshape(-1)
+    valid = o >= 0
+    assert (o[~valid] == -1).all()
+    assert np.array_equal(np.sort(o[valid]), np.flatnonzero(p >= 0))
+    if tile:
+        for s in range(0, o.size, tile):
+            seg = o[s:s + tile]
+            nv = int((p[s:s + tile] >= 0).sum())
+            assert (seg[:nv] >= s).all() and (seg[:nv] < s + tile).all()
+            assert (seg[nv:] == -1).all()
+            assert (np.diff(p[seg[:nv]]) > 0).all()
+
+
+def dispatch_with_plan(mg, srcs, lay, K, fill, rows=None):
+    """Dispatch in the layout's plan order into fresh buffers; host copies."""
+    rows = lay.cap if rows is None else rows
+    dsts = [torch.full((rows, a.shape[1]), fill, dtype=torch.uint8, device="cuda") for a in srcs]
+    mg.moe_dispatch([dev(a) for a in srcs], dsts, lay.pos, K, order=lay.order)
+    torch.cuda.synchronize()
+    return [host(d) for d in dsts]
+
+
 def check_combine(out_d, y_bits, w_np, pos_np):
     ref = oracle.combine(y_bits, np.ascontiguousarray(w_np), pos_np)
     got = host_bf16(out_d)
@@ -86,6 +114,10 @@ def test_named_workload(mg, name):
     ref = oracle.dispatch(srcs, pos, wl.K, fill=0xA5)
     for f, (r, d) in enumerate(zip(ref, dsts_d)):
         assert np.array_equal(host(d), r), f"field {f}"
+    # the same dispatch visiting the pairs in the layout's plan
+    check_plan(lay.order, pos, tile=512 if wl.N * wl.K > 2048 else 1)   # N*K/64 or index order
+    for f, (r, d) in enumerate(zip(ref, dispatch_with_plan(mg, srcs, lay, wl.K, 0xA5))):
+        assert np.array_equal(d, r), f"field {f}, planned"
 
     y = wl.y()
     out = mg.combine(dev_bf16(y), dev(wl.weights), lay)
@@ -112,6 +144,10 @@ def test_large_packed_records(mg):
     mg.moe_dispatch([rec_d], [recv], lay.pos, wl.K)
     torch.cuda.synchronize()
     (ref,) = oracle.dispatch([wl.records], pos, wl.K)
+    assert np.array_equal(host(recv), ref)
+    check_plan(lay.order, pos, tile=4096)       # 262144 pairs / 64 tiles
+    mg.moe_dispatch([rec_d], [recv], lay.pos, wl.K, order=lay.order)
+    torch.cuda.synchronize()
     assert np.array_equal(host(recv), ref)
     del ref, recv
     say("large: drawing expert outputs")
@@ -155,13 +191,50 @@ def test_random_stress(mg):
         dsts_d = [torch.full((cap, a.shape[1]), 0x5A, dtype=torch.uint8, device="cuda") for a in srcs]
         mg.moe_dispatch([dev(a) for a in srcs], dsts_d, lay.pos, K)
         torch.cuda.synchronize()
-        for r, d in zip(oracle.dispatch(srcs, pos, K, rows=cap, fill=0x5A), dsts_d):
+        ref = oracle.dispatch(srcs, pos, K, rows=cap, fill=0x5A)
+        for r, d in zip(ref, dsts_d):
             assert np.array_equal(host(d), r)
+        check_plan(lay.order, pos)
+        for r, d in zip(ref, dispatch_with_plan(mg, srcs, lay, K, 0x5A, rows=cap)):
+            assert np.array_equal(d, r)
         rng = np.random.default_rng(seed + 1)
         y = mw.bf16_bits_from_f32(rng.standard_normal((max(cap, 1), wl.Hc)).astype(np.float32))
         out = torch.empty((N, wl.Hc), dtype=torch.bfloat16, device="cuda")
         mg.moe_combine(dev_bf16(y), dev(wl.weights), lay.pos, out)
         check_combine(out, y, wl.weights, pos)
+
+
+def plan_tile(N, K, E):
+    """Pairs per tile of the dispatch plan as the header states it: N*K / B
+    rounded up to a multiple of 256 (B = 64 tiles for E <= 256, 32 for
+    E <= 512, 16 beyond); 1 (the index order) for at most 2048 pairs or for
+    tiles above 4096 pairs."""
+    nk = N * K
+    if nk <= 2048:
+        return 1
+    B = 64 if E <= 256 else 32 if E <= 512 else 16
+    C = -(-(-(-nk // B)) // 256) * 256
+    return C if C <= 4096 else 1
+
+
+@pytest.mark.parametrize("N,K,E", [(4096, 8, 512), (4096, 8, 1024), (3000, 8, 64), (2731, 3, 256),
+                                   (40000, 8, 256), (20000, 4, 1024)])
+def test_dispatch_plan_arrangement(mg, N, K, E):
+    """The plan's tiles at E past 256 (fewer, larger tiles), a short last
+    tile, K = 3, and the index order once tiles would pass 4096 pairs; masked
+    and out-of-range ids; the dispatch in the plan's order byte for byte."""
+    rng = np.random.default_rng(N + K + E)
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.1] = -1
+    ids[rng.random((N, K)) < 0.01] = E + 1
+    say(f"plan arrangement N={N} K={K} E={E} tile={plan_tile(N, K, E)}")
+    lay = mg.layout(dev(ids), E)
+    pos = check_layout(mg, lay, ids, E)
+    check_plan(lay.order, pos, tile=plan_tile(N, K, E))
+    src = rng.integers(0, 256, size=(N, 160), dtype=np.uint8)
+    (ref,) = oracle.dispatch([src], pos, K, fill=0x3C)
+    (got,) = dispatch_with_plan(mg, [src], lay, K, 0x3C)
+    assert np.array_equal(got, ref)
 
 
 def test_strided_views_and_untouched_padding(mg):

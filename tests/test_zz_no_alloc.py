@@ -34,7 +34,7 @@ def _outputs(N, K, E, cap):
     i32 = dict(dtype=torch.int32, device="cuda")
     return (torch.full((E,), -7, **i32), torch.full((E + 1,), -7, **i32),
             torch.full((N, K), -7, **i32), torch.full((cap,), -7, **i32),
-            torch.full((1,), -7, **i32))
+            torch.full((1,), -7, **i32), torch.full((N * K,), -7, **i32))
 
 
 def _cases():
@@ -59,9 +59,9 @@ def test_noalloc_matches_workspace_layout(mg):
         ids_d = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
         a = _outputs(N, K, E, cap)
         b = _outputs(N, K, E, cap)
-        mg.moe_get_layout_noalloc(ids_d, E, align, *a[:4], status=a[4])
+        mg.moe_get_layout_noalloc(ids_d, E, align, *a[:4], status=a[4], order=a[5])
         ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device="cuda")
-        mg.moe_get_layout(ids_d, E, align, *b[:4], ws, status=b[4])
+        mg.moe_get_layout(ids_d, E, align, *b[:4], ws, status=b[4], order=b[5])
         torch.cuda.synchronize()
         for x, y in zip(a, b):
             assert torch.equal(x, y)
