@@ -443,6 +443,10 @@ class LowLatencySet:
         self.out = torch.empty((N, Hc), dtype=torch.bfloat16, device=d)
         # Expert outputs in the padded layout: pair (t, k) finds the
         # workload's y row t*K + k at its padded row; other rows are unused.
+        # the receive metadata of the pages' low-latency dispatch: each
+        # expert's row range and its running count of received rows
+        self.layout_range = torch.empty(E, dtype=torch.int64, device=d)
+        self.recv_stats = torch.zeros(E, dtype=torch.int32, device=d)
         mg.moe_get_layout_padded(self.ids, E, M, self.counts, self.pos, self.row_pair,
                                  self.ws, self.status)
         torch.cuda.synchronize()
@@ -460,8 +464,8 @@ class LowLatencySet:
         N, K, E, Hc, H, M = wl.N, wl.K, wl.E, wl.Hc, self.H, self.M
         srs = H // 128 if self.fmt == 0 else 0
         lay = (self.ids.data_ptr(), K, N, K, E, M, self.counts.data_ptr(), self.pos.data_ptr(),
-               self.row_pair.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
-               self.status.data_ptr(), stream)
+               self.row_pair.data_ptr(), self.layout_range.data_ptr(), self.recv_stats.data_ptr(),
+               self.ws.data_ptr(), self.ws.numel(), self.status.data_ptr(), stream)
         dis = (self.x.data_ptr(), H, N, K, H, self.pos.data_ptr(), self.codes.data_ptr(), H,
                self.scales.data_ptr(), self.fmt, srs, M, self.round_scale, stream)
         com = (self.y.data_ptr(), Hc, self.w.data_ptr(), K, self.pos.data_ptr(), N, K, Hc,
@@ -476,6 +480,7 @@ class LowLatencySet:
         if self.fused:
             fu = (self.ids.data_ptr(), K, N, K, E, M, self.x.data_ptr(), H, H,
                   self.counts.data_ptr(), self.pos.data_ptr(), self.row_pair.data_ptr(),
+                  self.layout_range.data_ptr(), self.recv_stats.data_ptr(),
                   self.status.data_ptr(), self.codes.data_ptr(), H, self.scales.data_ptr(),
                   self.fmt, srs, self.round_scale, stream)
             return (L.moe_dispatch_fp8_padded, fu), (L.moe_combine, com)

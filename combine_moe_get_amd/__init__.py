@@ -83,7 +83,7 @@ def _load():
     L.moe_dispatch.restype = ctypes.c_int
     L.moe_combine.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P]
     L.moe_combine.restype = ctypes.c_int
-    L.moe_get_layout_padded.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, sz, P, P]
+    L.moe_get_layout_padded.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, sz, P, P]
     L.moe_get_layout_padded.restype = ctypes.c_int
     L.moe_dispatch_fp8.argtypes = [P, i64, i32, i32, i32, P, P, i64, P, i32, i64, i32, i32, P]
     L.moe_dispatch_fp8.restype = ctypes.c_int
@@ -99,8 +99,8 @@ def _load():
     L.moe_layout_dispatch.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, i64, P,
                                       ctypes.POINTER(moe_field), i32, P]
     L.moe_layout_dispatch.restype = ctypes.c_int
-    L.moe_dispatch_fp8_padded.argtypes = [P, i64, i32, i32, i32, i32, P, i64, i32, P, P, P, P, P,
-                                          i64, P, i32, i64, i32, P]
+    L.moe_dispatch_fp8_padded.argtypes = [P, i64, i32, i32, i32, i32, P, i64, i32, P, P, P, P, P, P,
+                                          P, i64, P, i32, i64, i32, P]
     L.moe_dispatch_fp8_padded.restype = ctypes.c_int
     L.moe_dispatch_backward.argtypes = [P, i64, P, i64, P, i32, i32, i32, P, i64, P, i64, P]
     L.moe_dispatch_backward.restype = ctypes.c_int
@@ -227,11 +227,24 @@ def moe_get_layout_noalloc(ids: torch.Tensor, num_experts: int, align: int,
                                        _dev(status, "status"), _stream(stream)))
 
 
+def _range_and_stats(layout_range, recv_stats, E):
+    if layout_range is not None and (layout_range.dtype != torch.int64 or
+                                     not layout_range.is_contiguous() or layout_range.numel() < E):
+        raise TypeError("layout_range must be a contiguous int64 tensor of E entries")
+    if recv_stats is not None and (recv_stats.dtype != torch.int32 or
+                                   not recv_stats.is_contiguous() or recv_stats.numel() < E):
+        raise TypeError("recv_stats must be a contiguous int32 tensor of E entries")
+
+
 def moe_get_layout_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: int,
                           counts: torch.Tensor, pos: torch.Tensor, row_pair: torch.Tensor,
                           workspace: torch.Tensor, status: Optional[torch.Tensor] = None,
-                          stream=None) -> None:
-    """Padded per-expert layout: expert e owns rows e*M .. e*M+M-1."""
+                          stream=None, layout_range: Optional[torch.Tensor] = None,
+                          recv_stats: Optional[torch.Tensor] = None) -> None:
+    """Padded per-expert layout: expert e owns rows e*M .. e*M+M-1.
+    layout_range (int64 [E]) receives each expert's (begin << 32) | count;
+    counts are added to recv_stats (int32 [E])."""
+    _range_and_stats(layout_range, recv_stats, num_experts)
     if ids.dtype != torch.int32:
         raise TypeError("ids must be int32")
     for n, t in (("counts", counts), ("pos", pos), ("row_pair", row_pair)):
@@ -246,7 +259,9 @@ def moe_get_layout_padded(ids: torch.Tensor, num_experts: int, rows_per_expert: 
     ip, istride = _rows(ids, "ids") if N > 0 else (0, K)
     _check(_lib.moe_get_layout_padded(ip, istride, N, K, num_experts, rows_per_expert,
                                       _dev(counts, "counts"), _dev(pos, "pos"),
-                                      _dev(row_pair, "row_pair"), _dev(workspace, "workspace"),
+                                      _dev(row_pair, "row_pair"),
+                                      _dev(layout_range, "layout_range"),
+                                      _dev(recv_stats, "recv_stats"), _dev(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
                                       _dev(status, "status"), _stream(stream)))
 
@@ -396,8 +411,11 @@ def moe_dispatch_fp8_padded(ids: torch.Tensor, num_experts: int, rows_per_expert
                             x: torch.Tensor, counts: torch.Tensor, pos: torch.Tensor,
                             row_pair: torch.Tensor, status: torch.Tensor, dst: torch.Tensor,
                             scales: torch.Tensor, scale_format: int = MOE_SCALE_COLS,
-                            round_scale: bool = False, stream=None) -> None:
+                            round_scale: bool = False, stream=None,
+                            layout_range: Optional[torch.Tensor] = None,
+                            recv_stats: Optional[torch.Tensor] = None) -> None:
     """moe_get_layout_padded + moe_dispatch_fp8 in one launch (N*K <= 8192)."""
+    _range_and_stats(layout_range, recv_stats, num_experts)
     if ids.dtype != torch.int32 or ids.dim() != 2:
         raise TypeError("ids must be int32 [N, K]")
     if x.dtype != torch.bfloat16:
@@ -427,6 +445,8 @@ def moe_dispatch_fp8_padded(ids: torch.Tensor, num_experts: int, rows_per_expert
         srs = 0
     _check(_lib.moe_dispatch_fp8_padded(ip, istr, N, K, E, M, xp, xs, H, _dev(counts, "counts"),
                                         _dev(pos, "pos"), _dev(row_pair, "row_pair"),
+                                        _dev(layout_range, "layout_range"),
+                                        _dev(recv_stats, "recv_stats"),
                                         _dev(status, "status"), dp, ds, _dev(scales, "scales"),
                                         scale_format, srs, int(bool(round_scale)),
                                         _stream(stream)))

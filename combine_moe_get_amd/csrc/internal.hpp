@@ -70,7 +70,8 @@ int layout_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int
                       hipStream_t stream);
 int layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                              int32_t E, int32_t M, int32_t* counts, int32_t* pos,
-                             int32_t* row_pair, int32_t* status, hipStream_t stream);
+                             int32_t* row_pair, int64_t* layout_range, int32_t* recv_stats,
+                             int32_t* status, hipStream_t stream);
 
 // The one-pass layout of the one-launch forms (small batches): every
 // workgroup counts the whole batch itself. tot[E], bef[E] and *nbad live in

@@ -302,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
     const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ status, int32_t* __restrict__ pos, int32_t* __restrict__ row_pair,
-    int64_t cap, int32_t M, int32_t* __restrict__ order) {
+    int64_t cap, int32_t M, int32_t* __restrict__ order, int64_t* __restrict__ layout_range,
+    int32_t* __restrict__ recv_stats) {
     __shared__ int32_t cnt[kWaves * MOE_MAX_EXPERTS];   // per-wave counts, then bases
     __shared__ int32_t total_s[MOE_MAX_EXPERTS];       // valid pairs per expert
     __shared__ int32_t start_s[MOE_MAX_EXPERTS];       // segment start (offsets[e])
@@ -369,8 +370,14 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
         if (e < E) {
             const int32_t start = M > 0 ? e * M : run;
             if (b == 0) {
-                counts[e] = M > 0 ? min(total_s[e], M) : total_s[e];
+                const int32_t kept = M > 0 ? min(total_s[e], M) : total_s[e];
+                counts[e] = kept;
                 if (offsets != nullptr) offsets[e] = start;
+                // Padded form, one source: the range of expert e's rows that
+                // came from it (begin 0 in the high half, count in the low),
+                // and the running count of rows received.
+                if (layout_range != nullptr) layout_range[e] = (int64_t)kept;
+                if (recv_stats != nullptr) recv_stats[e] += kept;
             }
             if (M > 0) dropped4 += max(total_s[e] - M, 0);
             start_s[e] = start;
@@ -503,31 +510,35 @@ static void launch_layout_b(const Plan& p, uint32_t assign_grid, const int32_t* 
                             int64_t stride, int64_t nk, int32_t K, int32_t E, int32_t align,
                             int32_t* H, int32_t* bad, int32_t* counts, int32_t* offsets,
                             int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
-                            int32_t M, int32_t* order, hipStream_t stream) {
+                            int32_t M, int32_t* order, int64_t* layout_range, int32_t* recv_stats,
+                            hipStream_t stream) {
     if (p.blocks > 0)
         layout_hist<B><<<p.blocks, kThreads, 0, stream>>>(ids, stride, (uint32_t)nk, (uint32_t)K,
                                                           E, p.chunk, p.nbits, H, bad);
     if (order != nullptr)
         layout_assign<B, true><<<assign_grid, kThreads, 0, stream>>>(
             ids, stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H, bad,
-            counts, offsets, status, pos, row_pair, cap, M, order);
+            counts, offsets, status, pos, row_pair, cap, M, order, layout_range, recv_stats);
     else
         layout_assign<B, false><<<assign_grid, kThreads, 0, stream>>>(
             ids, stride, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, H, bad,
-            counts, offsets, status, pos, row_pair, cap, M, nullptr);
+            counts, offsets, status, pos, row_pair, cap, M, nullptr, layout_range, recv_stats);
 }
 
 static void launch_layout(const Plan& p, uint32_t assign_grid, const int32_t* ids,
                           int64_t stride, int64_t nk, int32_t K, int32_t E, int32_t align,
                           int32_t* H, int32_t* bad, int32_t* counts, int32_t* offsets,
                           int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
-                          int32_t M, int32_t* order, hipStream_t stream) {
+                          int32_t M, int32_t* order, int64_t* layout_range, int32_t* recv_stats,
+                          hipStream_t stream) {
     if (p.chunk / kThreads > kBatchSmall)
         launch_layout_b<kBatchLarge>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
-                                     offsets, status, pos, row_pair, cap, M, order, stream);
+                                     offsets, status, pos, row_pair, cap, M, order, layout_range,
+                                     recv_stats, stream);
     else
         launch_layout_b<kBatchSmall>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
-                                     offsets, status, pos, row_pair, cap, M, order, stream);
+                                     offsets, status, pos, row_pair, cap, M, order, layout_range,
+                                     recv_stats, stream);
 }
 
 extern "C" int64_t moe_required_capacity(int32_t N, int32_t K, int32_t E, int32_t align) {
@@ -594,7 +605,7 @@ static int run_layout(const char* fn, const int32_t* ids, int64_t ids_row_stride
     clear_launch_error();
     int32_t* bad = H + (int64_t)p.blocks * E;
     launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
-                  counts, offsets, status, pos, row_pair, cap, 0, order, stream);
+                  counts, offsets, status, pos, row_pair, cap, 0, order, nullptr, nullptr, stream);
     return check_launch(fn);
 }
 
@@ -688,9 +699,9 @@ extern "C" int moe_get_layout_noalloc(const int32_t* ids, int64_t ids_row_stride
 
 extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
                                      int32_t K, int32_t E, int32_t M, int32_t* counts,
-                                     int32_t* pos, int32_t* row_pair, void* workspace,
-                                     size_t workspace_bytes, int32_t* status,
-                                     hipStream_t stream) {
+                                     int32_t* pos, int32_t* row_pair, int64_t* layout_range,
+                                     int32_t* recv_stats, void* workspace, size_t workspace_bytes,
+                                     int32_t* status, hipStream_t stream) {
     if (N < 0 || K < 1 || E < 1 || M < 1)
         return fail(MOE_ERR_ARG, "moe_get_layout_padded: need N >= 0, K >= 1, E >= 1, M >= 1 "
                     "(got N=%d K=%d E=%d M=%d)", N, K, E, M);
@@ -708,8 +719,9 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     if (counts == nullptr || row_pair == nullptr)
         return fail(MOE_ERR_ARG, "moe_get_layout_padded: counts and row_pair must not be NULL");
     if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(pos, 4) || !aligned(row_pair, 4) ||
-        !aligned(status, 4))
-        return fail(MOE_ERR_ALIGN, "moe_get_layout_padded: int32 pointers must be 4-byte aligned");
+        !aligned(recv_stats, 4) || !aligned(status, 4) || !aligned(layout_range, 8))
+        return fail(MOE_ERR_ALIGN, "moe_get_layout_padded: int32 pointers must be 4-byte aligned "
+                    "and layout_range 8-byte aligned");
     const Plan p = make_plan(N, K, E);
     const size_t ws = workspace_for(p, E);
     if (workspace == nullptr || workspace_bytes < ws)
@@ -721,7 +733,7 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     // batches with at most 2^18 padded rows (and a status word to write).
     if (N > 0 && nk <= kOneLaunchPairs && cap <= (1 << 18) && status != nullptr)
         return layout_padded_one_launch(ids, ids_row_stride, N, K, E, M, counts, pos, row_pair,
-                                        status, stream);
+                                        layout_range, recv_stats, status, stream);
     clear_launch_error();
     int32_t* H = static_cast<int32_t*>(workspace);
     int32_t* bad = H + (int64_t)p.blocks * E;
@@ -732,6 +744,6 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     if (grid < p.blocks) grid = p.blocks;
     if (grid < 1) grid = 1;
     launch_layout(p, (uint32_t)grid, ids, ids_row_stride, nk, K, E, 1, H, bad, counts, nullptr,
-                  status, pos, row_pair, cap, M, nullptr, stream);
+                  status, pos, row_pair, cap, M, nullptr, layout_range, recv_stats, stream);
     return check_launch("moe_get_layout_padded");
 }

@@ -170,6 +170,8 @@ struct FusedArgs {
     int32_t* counts;
     int32_t* pos;
     int32_t* row_pair;
+    int64_t* layout_range;   // may be NULL
+    int32_t* recv_stats;     // may be NULL
     int32_t* status;
 };
 
@@ -231,7 +233,12 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
     if (blockIdx.x == 0) {
         int32_t d = 0;
         for (int e = threadIdx.x; e < E; e += kFusedThreads) {
-            f.counts[e] = min(tot[e], M);
+            const int32_t kept = min(tot[e], M);
+            f.counts[e] = kept;
+            // one source: its range of expert e's rows (begin 0 in the high
+            // half, count in the low) and the running count received
+            if (f.layout_range != nullptr) f.layout_range[e] = (int64_t)kept;
+            if (f.recv_stats != nullptr) f.recv_stats[e] += kept;
             d += max(tot[e] - M, 0);
         }
         if (d) atomicAdd(&drop_s, d);
@@ -336,7 +343,8 @@ using namespace moe;
 // row_pair entry are outputs.
 static int launch_padded_one_launch(const Fp8Args& a, const int32_t* ids, int64_t ids_row_stride,
                                     int32_t E, int32_t* counts, int32_t* pos, int32_t* row_pair,
-                                    int32_t* status, hipStream_t stream, const char* who) {
+                                    int64_t* layout_range, int32_t* recv_stats, int32_t* status,
+                                    hipStream_t stream, const char* who) {
     FusedArgs f;
     f.ids = ids;
     f.ids_stride = ids_row_stride;
@@ -345,6 +353,8 @@ static int launch_padded_one_launch(const Fp8Args& a, const int32_t* ids, int64_
     f.counts = counts;
     f.pos = pos;
     f.row_pair = row_pair;
+    f.layout_range = layout_range;
+    f.recv_stats = recv_stats;
     f.status = status;
     const int64_t blocks = a.N > 0 ? (int64_t)a.N * f.groups : 1;
     if (blocks > kMaxLaunchItems / kFusedThreads)
@@ -358,7 +368,8 @@ static int launch_padded_one_launch(const Fp8Args& a, const int32_t* ids, int64_
 extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,
                                        int32_t K, int32_t E, int32_t M, const void* x,
                                        int64_t x_row_stride, int32_t H, int32_t* counts,
-                                       int32_t* pos, int32_t* row_pair, int32_t* status, void* dst,
+                                       int32_t* pos, int32_t* row_pair, int64_t* layout_range,
+                                       int32_t* recv_stats, int32_t* status, void* dst,
                                        int64_t dst_row_stride, void* scales, int32_t scale_format,
                                        int64_t scale_row_stride, int32_t round_scale,
                                        hipStream_t stream) {
@@ -397,9 +408,10 @@ extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_strid
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: dst must be 16-byte aligned with a "
                     "row stride that is a multiple of 16 bytes and >= H");
     if (!aligned(scales, 4) || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(pos, 4) ||
-        !aligned(row_pair, 4) || !aligned(status, 4))
+        !aligned(row_pair, 4) || !aligned(recv_stats, 4) || !aligned(status, 4) ||
+        !aligned(layout_range, 8))
         return fail(MOE_ERR_ALIGN, "moe_dispatch_fp8_padded: int32 and scale pointers must be "
-                    "4-byte aligned");
+                    "4-byte aligned and layout_range 8-byte aligned");
 
     Fp8Args a;
     a.x = static_cast<const uint16_t*>(x);
@@ -416,19 +428,20 @@ extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_strid
     a.srs = scale_row_stride;
     a.M = M;
     a.round_scale = round_scale ? 1 : 0;
-    return launch_padded_one_launch(a, ids, ids_row_stride, E, counts, pos, row_pair, status,
-                                    stream, "moe_dispatch_fp8_padded");
+    return launch_padded_one_launch(a, ids, ids_row_stride, E, counts, pos, row_pair, layout_range,
+                                    recv_stats, status, stream, "moe_dispatch_fp8_padded");
 }
 
 int moe::layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t N,
                                   int32_t K, int32_t E, int32_t M, int32_t* counts, int32_t* pos,
-                                  int32_t* row_pair, int32_t* status, hipStream_t stream) {
+                                  int32_t* row_pair, int64_t* layout_range, int32_t* recv_stats,
+                                  int32_t* status, hipStream_t stream) {
     Fp8Args a{};        // no channels: the kernel's layout part only
     a.N = N;
     a.K = K;
     a.M = M;
-    return launch_padded_one_launch(a, ids, ids_row_stride, E, counts, pos, row_pair, status,
-                                    stream, "moe_get_layout_padded");
+    return launch_padded_one_launch(a, ids, ids_row_stride, E, counts, pos, row_pair, layout_range,
+                                    recv_stats, status, stream, "moe_get_layout_padded");
 }
 
 extern "C" int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K,

@@ -245,6 +245,18 @@ int moe_combine(const void* y, int64_t y_row_stride, const float* w, int64_t w_r
  *   pos[N*K]       (device, out) row of pair (t, k), -1 if masked, out of
  *                  range or dropped.
  *   row_pair[E*M]  (device, out) t*K + k of each row, -1 for unfilled rows.
+ *   layout_range[E]  (device, out, int64, may be NULL, 8-byte aligned) the
+ *                  single-source form of packed_recv_layout_range
+ *                  [num_local_experts, num_ranks]: for expert e, the rows
+ *                  that came from this (the only) source, as
+ *                  (begin << 32) | count with begin = 0 and count =
+ *                  counts[e]. The pages give the tensor's shape and type,
+ *                  not the packing of the two numbers into 64 bits; this
+ *                  packing is this library's reading.
+ *   recv_stats[E]  (device, in/out, int32, may be NULL) the diagnosis
+ *                  tensor cumulative_local_expert_recv_stats: counts[e] is
+ *                  added to recv_stats[e], so that over calls it holds the
+ *                  rows each expert has received.
  *   status         (device, out, may be NULL) two int32: [0] ids >= E,
  *                  [1] pairs dropped for capacity.
  *   workspace      as for moe_get_layout (moe_layout_workspace_bytes).
@@ -254,8 +266,8 @@ int moe_combine(const void* y, int64_t y_row_stride, const float* w, int64_t w_r
  */
 int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                           int32_t E, int32_t M, int32_t* counts, int32_t* pos, int32_t* row_pair,
-                          void* workspace, size_t workspace_bytes, int32_t* status,
-                          hipStream_t stream);
+                          int64_t* layout_range, int32_t* recv_stats, void* workspace,
+                          size_t workspace_bytes, int32_t* status, hipStream_t stream);
 
 /* Scale layouts of moe_dispatch_fp8. */
 #define MOE_SCALE_ROWS 0   /* fp32 [rows, H/128]: scales[row*scale_row_stride + b] */
@@ -437,8 +449,9 @@ int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N, i
  *
  * Arguments, layouts and alignment are those of the two calls it replaces
  * (ids with a row stride in elements; x bf16; dst, scales as in
- * moe_dispatch_fp8 with rows_per_expert = M; status[2]). counts, row_pair and
- * status are written even when N = 0. Limits: N*K <= 8192 (larger batches:
+ * moe_dispatch_fp8 with rows_per_expert = M; status[2]; layout_range and
+ * recv_stats optional, as in moe_get_layout_padded). counts, row_pair,
+ * status, layout_range and recv_stats are written even when N = 0. Limits: N*K <= 8192 (larger batches:
  * the two calls), 1 <= K <= 32, 1 <= E <= 1024, M >= 1, E*M < 2^31,
  * H % 128 == 0, and at most 2^23 workgroups in the one launch:
  * N * ceil(H / 4096). Errors: MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_LIMIT,
@@ -446,7 +459,8 @@ int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N, i
  */
 int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
                             int32_t E, int32_t M, const void* x, int64_t x_row_stride, int32_t H,
-                            int32_t* counts, int32_t* pos, int32_t* row_pair, int32_t* status,
+                            int32_t* counts, int32_t* pos, int32_t* row_pair,
+                            int64_t* layout_range, int32_t* recv_stats, int32_t* status,
                             void* dst, int64_t dst_row_stride, void* scales, int32_t scale_format,
                             int64_t scale_row_stride, int32_t round_scale, hipStream_t stream);
 

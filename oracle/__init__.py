@@ -66,6 +66,8 @@ def lib():
         L.oracle_bf16_from_f64.restype = ctypes.c_uint16
         L.oracle_layout_padded.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P]
         L.oracle_layout_padded.restype = ctypes.c_int
+        L.oracle_padded_recv_meta.argtypes = [P, i32, P, P]
+        L.oracle_padded_recv_meta.restype = None
         L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
         L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
         L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
@@ -298,6 +300,18 @@ def layout_padded(ids: np.ndarray, E: int, M: int):
     if rc != OK:
         raise OracleError(rc, "layout_padded")
     return counts, pos, row_pair, (int(status[0]), int(status[1]))
+
+
+def padded_recv_meta(counts: np.ndarray, recv_stats: Optional[np.ndarray] = None):
+    """The padded layout's receive metadata for one source: (layout_range
+    int64 [E], recv_stats int32 [E] after adding counts; a zeroed array when
+    none is given)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    E = counts.size
+    rng = np.empty(E, np.int64)
+    stats = np.zeros(E, np.int32) if recv_stats is None else np.array(recv_stats, np.int32)
+    lib().oracle_padded_recv_meta(_ptr(counts), E, _ptr(rng), _ptr(stats))
+    return rng, stats
 
 
 SCALE_ROWS, SCALE_COLS, SCALE_UE8M0, SCALE_TOKENS = 0, 1, 2, 3

@@ -48,6 +48,8 @@
  *    block are 0 under any positive floor, and that is pinned) and the
  *    element step as one fp32 division x / s rather than a product with a
  *    reciprocal;
+ *  - padded receive metadata: each expert's row range from the single
+ *    source packed as (begin << 32) | count in the int64 the pages name;
  *  - backward: the sums over k as fp32 additions in ascending k (the
  *    combine's order) and the weight-gradient dot products formed in double
  *    and rounded once. The pages give the backward's dataflow only; the
@@ -363,6 +365,23 @@ int oracle_layout_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N, 
         status[1] = dropped;
     }
     return ORC_OK;
+}
+
+/* Receive metadata of the padded layout for one source (DeepEP repository
+ * dump, deep_ep.cpp, Buffer::low_latency_dispatch, which returns
+ * packed_recv_layout_range int64 [num_local_experts, num_ranks] and updates
+ * the int32 diagnosis tensor cumulative_local_expert_recv_stats
+ * [num_local_experts]; the kernel that fills them is not on the pages).
+ * With one source, expert e's rows from it are all its rows: begin 0 and
+ * count counts[e], packed as (begin << 32) | count -- the packing is this
+ * oracle's reading (parity unpinned); the stats gain each expert's rows. */
+void oracle_padded_recv_meta(const int32_t* counts, int32_t E, int64_t* layout_range,
+                             int32_t* recv_stats) {
+    for (int32_t e = 0; e < E; ++e) {
+        const int64_t begin = 0, count = counts[e];
+        if (layout_range) layout_range[e] = (begin << 32) | count;
+        if (recv_stats) recv_stats[e] += counts[e];
+    }
 }
 
 /* fp32 -> e4m3fn, round to nearest even, finite overflow saturates to

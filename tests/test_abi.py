@@ -220,11 +220,13 @@ def test_layout_padded_and_fp8_validation(lib):
     L = lib._lib
     P = 0x10000
     ws = lib.moe_layout_workspace_bytes(8, 8, 64)
-    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 0, P, P, P, P, ws, P, 0) == lib.MOE_ERR_ARG    # M = 0
-    assert L.moe_get_layout_padded(P, 8, 8, 8, 1025, 4, P, P, P, P, ws, P, 0) == lib.MOE_ERR_LIMIT
-    assert L.moe_get_layout_padded(P, 8, 8, 8, 1024, 1 << 21, P, P, P, P, ws, P, 0) == lib.MOE_ERR_LIMIT
-    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 4, P, P, P, 0, ws, P, 0) == lib.MOE_ERR_WORKSPACE
-    assert L.moe_get_layout_padded(P + 2, 8, 8, 8, 64, 4, P, P, P, P, ws, P, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 0, P, P, P, 0, 0, P, ws, P, 0) == lib.MOE_ERR_ARG    # M = 0
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 1025, 4, P, P, P, 0, 0, P, ws, P, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 1024, 1 << 21, P, P, P, 0, 0, P, ws, P, 0) == lib.MOE_ERR_LIMIT
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 4, P, P, P, 0, 0, 0, ws, P, 0) == lib.MOE_ERR_WORKSPACE
+    assert L.moe_get_layout_padded(P + 2, 8, 8, 8, 64, 4, P, P, P, 0, 0, P, ws, P, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 4, P, P, P, P + 4, 0, P, ws, P, 0) == lib.MOE_ERR_ALIGN
+    assert L.moe_get_layout_padded(P, 8, 8, 8, 64, 4, P, P, P, 0, P + 2, P, ws, P, 0) == lib.MOE_ERR_ALIGN
     F = L.moe_dispatch_fp8
     assert F(P, 256, 4, 2, 200, P, P, 256, P, 0, 2, 0, 0, 0) == lib.MOE_ERR_ALIGN         # H % 128
     assert F(P, 512, 4, 2, 256, P, P, 256, P, 2, 0, 4, 0, 0) == lib.MOE_ERR_ARG           # ue8m0 w/o round
@@ -298,11 +300,12 @@ def test_backward_validation(lib):
 def test_fused_padded_fp8_validation(lib):
     F = lib._lib.moe_dispatch_fp8_padded
     P = 0x10000
-    # (ids, istr, N, K, E, M, x, xs, H, counts, pos, row_pair, status, dst, ds, scales, fmt, srs, round, stream)
+    # (ids, istr, N, K, E, M, x, xs, H, counts, pos, row_pair, layout_range, recv_stats, status,
+    #  dst, ds, scales, fmt, srs, round, stream)
     ok = lambda **kw: [kw.get(n, d) for n, d in (
         ("ids", P), ("istr", 8), ("N", 16), ("K", 8), ("E", 32), ("M", 16), ("x", P), ("xs", 256),
-        ("H", 256), ("counts", P), ("pos", P), ("rp", P), ("st", P), ("dst", P), ("ds", 256),
-        ("sc", P), ("fmt", 1), ("srs", 0), ("rnd", 0), ("stream", 0))]
+        ("H", 256), ("counts", P), ("pos", P), ("rp", P), ("lr", 0), ("rs", 0), ("st", P),
+        ("dst", P), ("ds", 256), ("sc", P), ("fmt", 1), ("srs", 0), ("rnd", 0), ("stream", 0))]
     assert F(*ok(N=1025)) == lib.MOE_ERR_LIMIT            # N*K > 8192
     assert F(*ok(K=33)) == lib.MOE_ERR_LIMIT
     assert F(*ok(M=0)) == lib.MOE_ERR_ARG
@@ -315,6 +318,8 @@ def test_fused_padded_fp8_validation(lib):
     assert F(*ok(x=P + 8)) == lib.MOE_ERR_ALIGN
     assert F(*ok(ds=264)) == lib.MOE_ERR_ALIGN
     assert F(*ok(pos=P + 2)) == lib.MOE_ERR_ALIGN
+    assert F(*ok(lr=P + 4)) == lib.MOE_ERR_ALIGN               # layout_range is int64
+    assert F(*ok(rs=P + 2)) == lib.MOE_ERR_ALIGN
     # one launch: 8192 tokens x ceil(H/4096) workgroups must stay within 2^23
     H = 4096 * 1024 + 128
     assert F(*ok(N=8192, K=1, H=H, xs=H, ds=H)) == lib.MOE_ERR_LIMIT

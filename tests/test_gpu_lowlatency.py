@@ -32,20 +32,35 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def check_recv_meta(layout_range, recv_stats, stats0, counts_np):
+    """The receive metadata against the oracle's (layout_range from counts;
+    recv_stats = stats0 + counts)."""
+    rng, stats = oracle.padded_recv_meta(counts_np, stats0)
+    assert np.array_equal(layout_range.cpu().numpy(), rng)
+    assert np.array_equal(recv_stats.cpu().numpy(), stats)
+
+
 def padded(mg, ids_np, E, M):
+    """The padded layout with its receive metadata (the stats starting from
+    arbitrary values), every output against the oracle."""
     N, K = ids_np.shape
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     pos = torch.empty((N, K), dtype=torch.int32, device="cuda")
     row_pair = torch.empty(E * M, dtype=torch.int32, device="cuda")
     status = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    layout_range = torch.full((E,), -7, dtype=torch.int64, device="cuda")
+    stats0 = np.random.default_rng(N + E + M).integers(0, 1 << 20, size=E).astype(np.int32)
+    recv_stats = dev(stats0)
     ws = torch.empty(max(mg.moe_layout_workspace_bytes(N, K, E), 256), dtype=torch.uint8, device="cuda")
-    mg.moe_get_layout_padded(dev(ids_np), E, M, counts, pos, row_pair, ws, status)
+    mg.moe_get_layout_padded(dev(ids_np), E, M, counts, pos, row_pair, ws, status,
+                             layout_range=layout_range, recv_stats=recv_stats)
     torch.cuda.synchronize()
     c, p, rp, st = oracle.layout_padded(ids_np, E, M)
     assert np.array_equal(counts.cpu().numpy(), c)
     assert np.array_equal(pos.cpu().numpy(), p)
     assert np.array_equal(row_pair.cpu().numpy(), rp)
     assert tuple(status.cpu().tolist()) == st
+    check_recv_meta(layout_range, recv_stats, stats0, c)
     return pos, p
 
 
@@ -230,10 +245,14 @@ def test_padded_layout_empty_batch(mg):
     ws = torch.empty(max(mg.moe_layout_workspace_bytes(0, 8, E), 256), dtype=torch.uint8, device="cuda")
     ids = torch.empty((0, 8), dtype=torch.int32, device="cuda")
     pos = torch.empty((0, 8), dtype=torch.int32, device="cuda")
-    mg.moe_get_layout_padded(ids, E, M, counts, pos, row_pair, ws, status)
+    layout_range = torch.full((E,), 9, dtype=torch.int64, device="cuda")
+    recv_stats = torch.full((E,), 5, dtype=torch.int32, device="cuda")
+    mg.moe_get_layout_padded(ids, E, M, counts, pos, row_pair, ws, status,
+                             layout_range=layout_range, recv_stats=recv_stats)
     torch.cuda.synchronize()
     assert (counts.cpu() == 0).all() and (row_pair.cpu() == -1).all()
     assert status.cpu().tolist() == [0, 0]
+    assert (layout_range.cpu() == 0).all() and (recv_stats.cpu() == 5).all()
 
 
 def _fused_case(mg, ids, E, M, x_bits, fmt, round_scale, fill=0x3C):
@@ -249,14 +268,19 @@ def _fused_case(mg, ids, E, M, x_bits, fmt, round_scale, fill=0x3C):
     dst = torch.full((rows, H), fill, dtype=torch.uint8, device="cuda")
     shape = {0: (rows, H // 128), 1: (E, H // 128, M), 2: (E, H // 512, M), 3: (N, H // 128)}[fmt]
     scales = torch.zeros(shape, dtype=torch.int32 if fmt == 2 else torch.float32, device="cuda")
+    layout_range = torch.full((E,), -9, dtype=torch.int64, device="cuda")
+    stats0 = np.arange(E, dtype=np.int32) * 3
+    recv_stats = dev(stats0)
     mg.moe_dispatch_fp8_padded(dev(ids), E, M, dev(x_bits.view(np.int16)).view(torch.bfloat16),
-                               counts, pos, row_pair, status, dst, scales, fmt, round_scale)
+                               counts, pos, row_pair, status, dst, scales, fmt, round_scale,
+                               layout_range=layout_range, recv_stats=recv_stats)
     torch.cuda.synchronize()
     c, p, rp, st = oracle.layout_padded(ids, E, M)
     assert np.array_equal(counts.cpu().numpy(), c)
     assert np.array_equal(pos.cpu().numpy(), p)
     assert np.array_equal(row_pair.cpu().numpy(), rp)
     assert tuple(status.cpu().tolist()) == st
+    check_recv_meta(layout_range, recv_stats, stats0, c)
     codes, ref_scales = oracle.dispatch_fp8(x_bits, p, rows, fmt, M, round_scale, fill=fill)
     assert np.array_equal(dst.cpu().numpy(), codes)
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))

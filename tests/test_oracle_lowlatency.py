@@ -64,6 +64,37 @@ def _torch_e4m3(v):
     return torch.tensor(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_padded_receive_metadata(orc, seed):
+    """What the receive metadata must say, checked against the layout itself
+    rather than against its formula: for each expert, the range's begin and
+    count (in the packing this library reads into the int64, begin in the
+    high half) cover exactly the rows of the expert's segment that hold a
+    pair; the stats gain, over two calls, the rows each expert received, and
+    one call's gains add up to the pairs that were neither masked, out of
+    range nor dropped."""
+    rng = np.random.default_rng(seed)
+    N, K, E, M = 300, 8, 40, 50
+    ids = rng.integers(-1, E + 1, size=(N, K)).astype(np.int32)
+    counts, pos, row_pair, (nbad, ndrop) = orc.layout_padded(ids, E, M)
+    start = rng.integers(0, 1000, size=E).astype(np.int32)
+    rngs, stats = orc.padded_recv_meta(counts, start)
+    begin, count = rngs >> 32, rngs & 0xFFFFFFFF
+    filled = (row_pair.reshape(E, M) >= 0)
+    for e in range(E):
+        rows = np.flatnonzero(filled[e])
+        assert np.array_equal(rows, np.arange(begin[e], begin[e] + count[e]))
+    valid = int(((ids >= 0) & (ids < E)).sum())
+    assert int((stats - start).sum()) == valid - ndrop
+    ids2 = rng.integers(0, E, size=(17, K)).astype(np.int32)
+    counts2 = orc.layout_padded(ids2, E, M)[0]
+    _, stats2 = orc.padded_recv_meta(counts2, stats)
+    assert np.array_equal(stats2 - start, counts.astype(np.int64) + counts2)
+    empty = orc.layout_padded(np.zeros((0, K), np.int32), E, M)[0]
+    r0, s0 = orc.padded_recv_meta(empty, stats2)
+    assert (r0 == 0).all() and np.array_equal(s0, stats2)
+
+
 def test_e4m3_matches_torch_in_range(orc):
     rng = np.random.default_rng(0)
     v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-4, 3, 20000),

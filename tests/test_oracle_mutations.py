@@ -65,6 +65,12 @@ MUTANTS = [
      "        if (scale_mode == 3)\n            for (int32_t b = 0; b < nb; ++b)",
      "        if (scale_mode == 3 && pos[(int64_t)t * K] >= 0)\n            for (int32_t b = 0; b < nb; ++b)",
      "test_oracle_lowlatency.py"),
+    ("receive range swaps begin and count",
+     "if (layout_range) layout_range[e] = (begin << 32) | count;",
+     "if (layout_range) layout_range[e] = (count << 32) | begin;", "test_oracle_lowlatency.py"),
+    ("receive stats overwritten instead of added",
+     "if (recv_stats) recv_stats[e] += counts[e];",
+     "if (recv_stats) recv_stats[e] = counts[e];", "test_oracle_lowlatency.py"),
     ("combine backward scales by the first weight",
      "float wk = w[(int64_t)t * w_row_stride + k];", "float wk = w[(int64_t)t * w_row_stride];",
      "test_oracle_backward.py"),
