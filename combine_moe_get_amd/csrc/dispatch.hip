@@ -188,12 +188,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(const Dispatc
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) sum4 += mine[j];
-    int32_t x = sum4;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    const int32_t x = wave_inclusive_scan(sum4);
     if (lane == kWave - 1) wave_sums[wave] = x;
     __syncthreads();
     int32_t run = x - sum4, used = 0;

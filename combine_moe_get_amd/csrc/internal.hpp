@@ -51,6 +51,27 @@ inline void in_pieces(int64_t total, int64_t piece, F&& launch) {
 // 16-byte and 4-byte lane payloads.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane i gets the sum of
+// lanes 0 .. i), in six DPP steps instead of a chain of LDS-routed shuffles:
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from
+// outside the row add 0), then lane 15 of rows 0 and 2 added to rows 1 and 3
+// (row_bcast:15), then lane 31 added to rows 2 and 3 (row_bcast:31). Every
+// lane of the wave must be active.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+// Sum over the 64 lanes of a wave, in every lane (all lanes active).
+__device__ __forceinline__ int32_t wave_sum(int32_t x) {
+    return __builtin_amdgcn_readlane(wave_inclusive_scan(x), kWave - 1);
+}
+
 // Third word of a gfx9 buffer descriptor for raw (untyped) loads, which are
 // range-checked against num_records: loads past it return 0 and touch no
 // memory.

@@ -7,28 +7,33 @@
 // as written by mask_topk_ids (vLLM branch compare ds-exp-2...ds-exp-ag).
 // Rows inside one expert's segment follow ascending (t, k).
 //
-// Two launches on the caller's stream, no atomics deciding any order:
-//   1. hist   -- each workgroup takes a contiguous chunk of pairs; each of
-//                its 4 waves a contiguous quarter. A wave finds the lanes that
-//                share an expert with one ballot per id bit, and the lowest
-//                such lane adds the group size to the wave's own LDS row.
-//                The workgroup writes its per-expert totals H[b][e].
-//   2. assign -- every workgroup reduces the whole (small) H matrix itself:
-//                per expert, the sum over earlier chunks and the total; an
-//                exclusive scan of the aligned totals gives the offsets
-//                (workgroup 0 also writes counts, offsets and status). It
-//                then recounts its waves, turns the counts into per-wave
-//                bases (offset + earlier chunks + earlier waves), and walks
-//                its pairs again in order: the row of a pair is its wave's
-//                base for the expert plus the number of lower lanes in the
-//                same 64-pair step with that expert. Finally all workgroups
-//                mark unused rows with -1.
+// Three forms, all on the caller's stream, none with an atomic that decides
+// any order (LDS atomics only add counts, and sums do not depend on order):
+//   - two launches, for any batch:
+//     1. hist   -- each workgroup takes a contiguous chunk of pairs; each of
+//                  its 4 waves a contiguous quarter. A wave finds the lanes
+//                  that share an expert with one ballot per id bit, and the
+//                  lowest such lane adds the group size to the wave's own LDS
+//                  row. The workgroup writes its per-expert totals H[b][e].
+//     2. assign -- every workgroup reduces the whole (small) H matrix itself:
+//                  per expert, the sum over earlier chunks and the total; an
+//                  exclusive scan of the aligned totals gives the offsets
+//                  (workgroup 0 also writes counts, offsets and status). It
+//                  then recounts its waves, turns the counts into per-wave
+//                  bases (offset + earlier chunks + earlier waves), and walks
+//                  its pairs again in order: the row of a pair is its wave's
+//                  base for the expert plus the number of lower lanes in the
+//                  same 64-pair step with that expert. Finally all workgroups
+//                  mark unused rows with -1. H has at most 16384 entries, so
+//                  the redundant reduction costs each workgroup at most 64
+//                  loads per thread.
+//   - one launch for mid-size batches of contiguous ids (layout_onepass):
+//     every workgroup counts the whole batch itself with LDS atomics instead
+//     of reading H, then assigns its chunk as `assign` does;
+//   - one launch for batches of at most kOneLaunchPairs pairs: the layout
+//     part of the one-launch dispatch kernels (dispatch.hip, quant.hip).
 // The kernel boundary is the only grid-wide ordering used, so the result
-// does not depend on scheduling. Batches of at most kOneLaunchPairs pairs
-// take one launch instead, the layout part of the one-launch dispatch
-// kernels (dispatch.hip, quant.hip), where every workgroup counts the whole
-// batch: below that size it is the faster of the two. H has at most 16384 entries, so the
-// redundant reduction costs each workgroup at most 64 loads per thread.
+// does not depend on scheduling, and every form gives the same outputs.
 #include <mutex>
 
 #include "internal.hpp"
@@ -88,15 +93,25 @@ __device__ __forceinline__ int32_t load_id(const int32_t* __restrict__ ids, int6
 }
 
 // Lanes of this wave holding the same valid expert as the calling lane
-// (valid for valid lanes only): one ballot per bit of the id.
-__device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool valid, int nbits) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
+// (valid for valid lanes only). Per id bit b, a ballot m of the lanes with
+// bit b set; the lanes that differ from this lane in bit b are m, or ~m
+// when this lane has the bit: m ^ s with s = bit b spread over all 32 bits
+// (0 or -1). The lanes that differ in no bit and are valid are the peers.
+// All kMaxIdBits bits, without a branch: past the id's top bit (E <= 2^bits)
+// every valid lane has 0, so only invalid lanes differ there.
+constexpr int kMaxIdBits = 10;
+static_assert((1 << kMaxIdBits) >= MOE_MAX_EXPERTS, "expert ids fit kMaxIdBits bits");
+
+__device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool valid, int /*nbits*/) {
+    uint32_t dlo = 0, dhi = 0;   // lanes that differ in some bit
+#pragma unroll
+    for (int b = 0; b < kMaxIdBits; ++b) {
+        const int32_t sb = (int32_t)((uint32_t)e << (31 - b)) >> 31;   // bit b: 0 or -1
+        const uint64_t m = __ballot(sb != 0);
+        dlo |= (uint32_t)sb ^ (uint32_t)m;
+        dhi |= (uint32_t)sb ^ (uint32_t)(m >> 32);
     }
-    return peers;
+    return ~(((uint64_t)dhi << 32) | dlo) & __ballot(valid);
 }
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
@@ -125,11 +140,12 @@ __device__ __forceinline__ void load_ids(int32_t (&e_reg)[B],
 }
 
 // Adds one batch of steps to the wave's counts cnt_row[e]; returns the number
-// of ids >= E in the batch.
+// of ids >= E in the batch. With peers_out, also keeps each step's
+// same-expert lanes for rank_batch.
 template <int B>
 __device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[B], int s0,
                                                int steps, int32_t E, int nbits, int32_t* cnt_row,
-                                               int lane) {
+                                               int lane, uint64_t* peers_out = nullptr) {
     int32_t bad = 0;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -138,6 +154,7 @@ __device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[B], int s0
             const bool valid = e >= 0 && e < E;
             bad += __popcll(__ballot(e >= E));
             const uint64_t peers = same_expert_lanes(e, valid, nbits);
+            if (peers_out != nullptr) peers_out[j] = peers;
             if (valid && lane == __ffsll((long long)peers) - 1) cnt_row[e] += __popcll(peers);
             __builtin_amdgcn_wave_barrier();
         }
@@ -146,7 +163,8 @@ __device__ __forceinline__ int32_t count_batch(const int32_t (&e_reg)[B], int s0
 }
 
 // Gives every pair of one batch its row: the wave's running base for the
-// expert plus the number of lower lanes in the same step with that expert.
+// expert plus the number of lower lanes in the same step with that expert
+// (peers_in: the steps' same-expert lanes kept by count_batch).
 // In the padded form (M > 0) expert e's segment is rows e*M .. e*M+M-1 and
 // a pair ranked past it is dropped (pos = -1).
 // With a plan (order != nullptr), a valid pair also takes its slot in the
@@ -164,14 +182,16 @@ __device__ __forceinline__ void rank_batch(const int32_t (&e_reg)[B], int s0, in
                                            int32_t M, int32_t* __restrict__ order = nullptr,
                                            const int32_t* tile_scan = nullptr,
                                            const int32_t* tile_row = nullptr,
-                                           int32_t tile_start = 0) {
+                                           int32_t tile_start = 0,
+                                           const uint64_t* peers_in = nullptr) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
         if (s0 + j < steps) {   // wave-uniform
             const uint32_t i = first + (uint32_t)(s0 + j) * kWave + lane;
             const int32_t e = e_reg[j];
             const bool valid = e >= 0 && e < E;
-            const uint64_t peers = same_expert_lanes(e, valid, nbits);
+            const uint64_t peers =
+                peers_in != nullptr ? peers_in[j] : same_expert_lanes(e, valid, nbits);
             int32_t p = -1;
             if (valid) p = base_row[e] + __popcll(peers & lanes_below(lane));
             __builtin_amdgcn_wave_barrier();
@@ -233,12 +253,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
                                                         int32_t* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    int32_t x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int32_t y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    const int32_t x = wave_inclusive_scan(v);
     if (lane == kWave - 1) wave_sums[wave] = x;
     __syncthreads();
     int32_t before = 0, all = 0;
@@ -296,60 +311,43 @@ __device__ __forceinline__ void reduce_chunks(const int32_t* __restrict__ H, int
 // kPlanMaxTile pairs write the index order instead.
 constexpr int32_t kPlanMaxTile = 4096;
 
-template <int B, bool PLAN>
-__global__ __launch_bounds__(kThreads) void layout_assign(
-    const int32_t* __restrict__ ids, int64_t stride, uint32_t nk, uint32_t K, int32_t E,
-    int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
-    const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ status, int32_t* __restrict__ pos, int32_t* __restrict__ row_pair,
-    int64_t cap, int32_t M, int32_t* __restrict__ order, int64_t* __restrict__ layout_range,
-    int32_t* __restrict__ recv_stats) {
-    __shared__ int32_t cnt[kWaves * MOE_MAX_EXPERTS];   // per-wave counts, then bases
-    __shared__ int32_t total_s[MOE_MAX_EXPERTS];       // valid pairs per expert
-    __shared__ int32_t start_s[MOE_MAX_EXPERTS];       // segment start (offsets[e])
-    __shared__ int32_t base[MOE_MAX_EXPERTS];          // pairs in earlier chunks, then chunk base
-    __shared__ int32_t tile_scan[PLAN ? MOE_MAX_EXPERTS : 1];   // chunk's pairs of lower experts
-    __shared__ int32_t wave_sums[kWaves];
-    __shared__ int32_t used_s;
-    __shared__ int32_t tile_valid_s;
+// LDS of the assign step, shared by both layout forms.
+template <bool PLAN>
+struct AssignLds {
+    int32_t cnt[kWaves * MOE_MAX_EXPERTS];   // per-wave counts, then bases
+    int32_t total_s[MOE_MAX_EXPERTS];       // valid pairs per expert
+    int32_t start_s[MOE_MAX_EXPERTS];       // segment start (offsets[e])
+    int32_t base[MOE_MAX_EXPERTS];          // pairs in earlier chunks, then chunk base
+    int32_t tile_scan[PLAN ? MOE_MAX_EXPERTS : 1];   // chunk's pairs of lower experts
+    int32_t wave_sums[kWaves];
+    int32_t used_s;
+    int32_t tile_valid_s;
+};
+
+// Segment starts from the per-expert totals (total_s) and the pairs in
+// earlier chunks (base): an exclusive scan of the aligned totals, or e*M in
+// the padded form; base[e] becomes the chunk's first row of expert e. Thread
+// i owns experts 4i .. 4i+3 (E <= 1024); their total_s and base entries must
+// have been written by this thread or before a barrier. Workgroup 0 writes
+// counts, offsets, the padded form's drop count (status[1]) and receive
+// metadata; status[0] is left to the caller. Contains barriers: every thread
+// of the workgroup calls it.
+template <bool PLAN>
+__device__ __forceinline__ void segment_starts(AssignLds<PLAN>& s, int b, int32_t E,
+                                               int32_t align, int32_t M,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ status,
+                                               int64_t* __restrict__ layout_range,
+                                               int32_t* __restrict__ recv_stats) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int b = blockIdx.x;
-    const bool active = b < blocks;
-    const int quarter = chunk / kWaves;
-    const int steps = active ? quarter / kWave : 0;
-    const uint32_t first = (uint32_t)b * chunk + wave * quarter;
-
-    // The ids of the first batch and the chunk histograms are fetched
-    // together; the ids stay in registers for both passes below.
-    int32_t e_first[B];
-    load_ids(e_first, ids, stride, nk, K, first, 0, steps, lane);
-    // Few chunks (small batches) take a short form of the reduction: the
-    // straight-line code a workgroup runs once is fetched into a cold
-    // instruction cache, so its length shows in small-batch latency.
-    if (blocks <= 16) {
-        if (E <= kThreads)
-            reduce_chunks<1, 16>(H, blocks, E, b, total_s, base);
-        else
-            reduce_chunks<4, 16>(H, blocks, E, b, total_s, base);
-    } else if (E <= kThreads) {
-        reduce_chunks<1, kMaxChunks>(H, blocks, E, b, total_s, base);
-    } else if (E <= 2 * kThreads) {
-        reduce_chunks<2, kMaxChunks / 2>(H, blocks, E, b, total_s, base);
-    } else {
-        reduce_chunks<4, kMaxChunks / 4>(H, blocks, E, b, total_s, base);
-    }
-    for (int x = threadIdx.x; x < kWaves * E; x += kThreads) cnt[x] = 0;
-    __syncthreads();
-
-    // Offsets: exclusive scan of the aligned totals; thread i owns experts
-    // 4i .. 4i+3 (E <= 1024).
     int32_t mine4[4];
     int32_t sum4 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = threadIdx.x * 4 + j;
-        mine4[j] = e < E ? total_s[e] : 0;
+        mine4[j] = e < E ? s.total_s[e] : 0;
     }
     if (align > 1) {
         // The host checks cap >= N*K + E*(align - 1) and cap < 2^31, so
@@ -362,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
 #pragma unroll
     for (int j = 0; j < 4; ++j) sum4 += mine4[j];
     int32_t used = 0;
-    int32_t run = block_exclusive_scan<kWaves>(sum4, wave_sums, &used);
+    int32_t run = block_exclusive_scan<kWaves>(sum4, s.wave_sums, &used);
     int32_t dropped4 = 0;   // padded form: pairs beyond their expert's M rows
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -370,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
         if (e < E) {
             const int32_t start = M > 0 ? e * M : run;
             if (b == 0) {
-                const int32_t kept = M > 0 ? min(total_s[e], M) : total_s[e];
+                const int32_t kept = M > 0 ? min(s.total_s[e], M) : s.total_s[e];
                 counts[e] = kept;
                 if (offsets != nullptr) offsets[e] = start;
                 // Padded form, one source: the range of expert e's rows that
@@ -379,37 +377,46 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
                 if (layout_range != nullptr) layout_range[e] = (int64_t)kept;
                 if (recv_stats != nullptr) recv_stats[e] += kept;
             }
-            if (M > 0) dropped4 += max(total_s[e] - M, 0);
-            start_s[e] = start;
-            base[e] += start;
+            if (M > 0) dropped4 += max(s.total_s[e] - M, 0);
+            s.start_s[e] = start;
+            s.base[e] += start;
         }
         run += mine4[j];
     }
     if (threadIdx.x == 0) {
-        used_s = M > 0 ? E * M : used;
+        s.used_s = M > 0 ? E * M : used;
         if (b == 0 && offsets != nullptr) offsets[E] = M > 0 ? E * M : used;
     }
-    if (b == 0 && status != nullptr && threadIdx.x < kWave) {
-        int32_t nb = 0;
-        for (int g = lane; g < blocks; g += kWave) nb += bad[g];
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) nb += __shfl_xor(nb, off, kWave);
-        if (lane == 0) status[0] = nb;
-    }
     if (M > 0) {
-        // status[1]: one wave-reduced sum per wave, then wave 0 adds them
-        int32_t d = dropped4;
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, kWave);
+        // status[1]: one sum per wave, then thread 0 adds them
+        const int32_t d = wave_sum(dropped4);
         __syncthreads();   // wave_sums is free again after the scan
-        if (lane == 0) wave_sums[wave] = d;
+        if (lane == 0) s.wave_sums[wave] = d;
         __syncthreads();
         if (b == 0 && status != nullptr && threadIdx.x == 0)
-            status[1] = wave_sums[0] + wave_sums[1] + wave_sums[2] + wave_sums[3];
+            status[1] = s.wave_sums[0] + s.wave_sums[1] + s.wave_sums[2] + s.wave_sums[3];
     }
-    // Per-wave counts of this chunk.
-    int32_t* mine = cnt + wave * E;
-    count_batch(e_first, 0, steps, E, nbits, mine, lane);
+}
+
+// A chunk's assignment, first half (it needs only the chunk's own ids):
+// per-wave counts of chunk b into s.cnt, which must be zero behind a
+// barrier, and with a plan the chunk's tile_scan. e_first holds the first
+// batch of the wave's ids (later batches are loaded again); peers receives
+// the first batch's same-expert lanes for assign_rank. Contains barriers.
+template <int B, bool PLAN>
+__device__ __forceinline__ void assign_count(AssignLds<PLAN>& s, const int32_t (&e_first)[B],
+                                             uint64_t (&peers)[B],
+                                             const int32_t* __restrict__ ids, int64_t stride,
+                                             uint32_t nk, uint32_t K, int32_t E, int nbits,
+                                             int32_t chunk, int b, bool active) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int quarter = chunk / kWaves;
+    const int steps = active ? quarter / kWave : 0;
+    const uint32_t first = (uint32_t)b * chunk + wave * quarter;
+
+    int32_t* mine = s.cnt + wave * E;
+    count_batch(e_first, 0, steps, E, nbits, mine, lane, peers);
     for (int s0 = B; s0 < steps; s0 += B) {
         int32_t e_reg[B];
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
@@ -417,84 +424,291 @@ __global__ __launch_bounds__(kThreads) void layout_assign(
     }
     __syncthreads();
 
-    const bool sorted = PLAN && chunk <= kPlanMaxTile;   // wave-uniform
-    if (sorted) {
+    if (PLAN && chunk <= kPlanMaxTile) {
         // The chunk's plan slots: an exclusive scan over the experts of the
         // chunk's pairs per expert (its four waves' counts) places each
-        // expert's run; the run's first row is the chunk base base[e].
-        // (wave_sums is free: the scan above is behind a barrier.)
+        // expert's run; the run's first row will be the chunk base base[e].
         int32_t t4[4], tsum = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = threadIdx.x * 4 + j;
-            t4[j] = e < E ? cnt[e] + cnt[E + e] + cnt[2 * E + e] + cnt[3 * E + e] : 0;
+            t4[j] = e < E ? s.cnt[e] + s.cnt[E + e] + s.cnt[2 * E + e] + s.cnt[3 * E + e] : 0;
             tsum += t4[j];
         }
         int32_t tvalid = 0;
-        int32_t trun = block_exclusive_scan<kWaves>(tsum, wave_sums, &tvalid);
+        int32_t trun = block_exclusive_scan<kWaves>(tsum, s.wave_sums, &tvalid);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = threadIdx.x * 4 + j;
-            if (e < E) tile_scan[e] = trun;
+            if (e < E) s.tile_scan[e] = trun;
             trun += t4[j];
         }
-        if (threadIdx.x == 0) tile_valid_s = tvalid;
+        if (threadIdx.x == 0) s.tile_valid_s = tvalid;
+        __syncthreads();   // the t4 reads of cnt before assign_rank rewrites it
     }
+}
 
-    // Per-wave bases: segment start + earlier chunks + earlier waves.
+// Second half: the per-wave bases (chunk base + earlier waves) from s.cnt
+// and the final chunk bases s.base, both behind a barrier; then the rows
+// of the chunk's pairs in order, and the chunk's plan tile. Contains
+// barriers.
+template <int B, bool PLAN>
+__device__ __forceinline__ void assign_rank(AssignLds<PLAN>& s, const int32_t (&e_first)[B],
+                                            const uint64_t (&peers)[B],
+                                            const int32_t* __restrict__ ids, int64_t stride,
+                                            uint32_t nk, uint32_t K, int32_t E, int nbits,
+                                            int32_t chunk, int b, bool active,
+                                            int32_t* __restrict__ pos,
+                                            int32_t* __restrict__ row_pair, int64_t cap,
+                                            int32_t M, int32_t* __restrict__ order) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int quarter = chunk / kWaves;
+    const int steps = active ? quarter / kWave : 0;
+    const uint32_t first = (uint32_t)b * chunk + wave * quarter;
+    const bool sorted = PLAN && chunk <= kPlanMaxTile;   // wave-uniform
+
     for (int e = threadIdx.x; e < E; e += kThreads) {
-        int32_t r = base[e];
+        int32_t r = s.base[e];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const int32_t c = cnt[w * E + e];
-            cnt[w * E + e] = r;
+            const int32_t c = s.cnt[w * E + e];
+            s.cnt[w * E + e] = r;
             r += c;
         }
     }
     __syncthreads();
 
-    int32_t* const plan = PLAN ? order : nullptr;
+    int32_t* mine = s.cnt + wave * E;
     const int32_t tile_start = b * chunk;
-    const int32_t* const run_row = sorted ? base : nullptr;
-    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M, plan,
-               tile_scan, run_row, tile_start);
+    const int32_t* const run_row = sorted ? s.base : nullptr;
+    rank_batch(e_first, 0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M, order,
+               s.tile_scan, run_row, tile_start, peers);
     for (int s0 = B; s0 < steps; s0 += B) {
         int32_t e_reg[B];
         load_ids(e_reg, ids, stride, nk, K, first, s0, steps, lane);
-        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M, plan,
-                   tile_scan, run_row, tile_start);
+        rank_batch(e_reg, s0, steps, E, nbits, mine, first, nk, lane, pos, row_pair, cap, M, order,
+                   s.tile_scan, run_row, tile_start);
     }
-    if (sorted) {
+    if (sorted && active) {
         // The chunk's slots past its valid pairs (its masked and out-of-range
         // pairs) hold -1.
-        if (active) {
-            const int32_t len = (int32_t)min((int64_t)(b + 1) * chunk, (int64_t)nk) - tile_start;
-            for (int32_t j = tile_valid_s + (int32_t)threadIdx.x; j < len; j += kThreads)
-                order[tile_start + j] = -1;
-        }
+        const int32_t len = (int32_t)min((int64_t)(b + 1) * chunk, (int64_t)nk) - tile_start;
+        for (int32_t j = s.tile_valid_s + (int32_t)threadIdx.x; j < len; j += kThreads)
+            order[tile_start + j] = -1;
     }
+}
 
-    // Rows no pair landed in: past the used rows, and alignment padding.
+// Rows no pair landed in get -1: past the used rows and alignment padding,
+// or in the padded form the rows of each segment past its kept pairs. Every
+// workgroup of the grid (which may exceed the chunks) takes a strided share.
+template <bool PLAN>
+__device__ __forceinline__ void mark_unused_rows(const AssignLds<PLAN>& s, int b, int32_t E,
+                                                 int32_t align, int32_t M, int64_t cap,
+                                                 int32_t* __restrict__ row_pair) {
     if (M > 0) {
-        // padded form: every workgroup of the grid (which may exceed the
-        // chunks) takes a strided share of the E*M rows
         for (int64_t r = (int64_t)b * kThreads + threadIdx.x; r < cap;
              r += (int64_t)gridDim.x * kThreads) {
             const int32_t e = (int32_t)((uint32_t)r / (uint32_t)M);
-            if ((int32_t)r - e * M >= min(total_s[e], M)) row_pair[r] = -1;
+            if ((int32_t)r - e * M >= min(s.total_s[e], M)) row_pair[r] = -1;
         }
         return;
     }
-    for (int64_t r = used_s + (int64_t)b * kThreads + threadIdx.x; r < cap;
+    for (int64_t r = s.used_s + (int64_t)b * kThreads + threadIdx.x; r < cap;
          r += (int64_t)gridDim.x * kThreads)
         row_pair[r] = -1;
     if (align > 1) {
         for (int e = b; e < E; e += gridDim.x) {
-            const int32_t hi = e + 1 < E ? start_s[e + 1] : used_s;
-            for (int32_t r = start_s[e] + total_s[e] + threadIdx.x; r < hi; r += kThreads)
+            const int32_t hi = e + 1 < E ? s.start_s[e + 1] : s.used_s;
+            for (int32_t r = s.start_s[e] + s.total_s[e] + threadIdx.x; r < hi; r += kThreads)
                 row_pair[r] = -1;
         }
     }
+}
+
+template <int B, bool PLAN>
+__global__ __launch_bounds__(kThreads) void layout_assign(
+    const int32_t* __restrict__ ids, int64_t stride, uint32_t nk, uint32_t K, int32_t E,
+    int32_t chunk, int nbits, int32_t blocks, int32_t align, const int32_t* __restrict__ H,
+    const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ status, int32_t* __restrict__ pos, int32_t* __restrict__ row_pair,
+    int64_t cap, int32_t M, int32_t* __restrict__ order, int64_t* __restrict__ layout_range,
+    int32_t* __restrict__ recv_stats) {
+    __shared__ AssignLds<PLAN> s;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int b = blockIdx.x;
+    const bool active = b < blocks;
+    const int quarter = chunk / kWaves;
+    const int steps = active ? quarter / kWave : 0;
+    const uint32_t first = (uint32_t)b * chunk + wave * quarter;
+
+    // The ids of the first batch and the chunk histograms are fetched
+    // together; the ids stay in registers for both passes.
+    int32_t e_first[B];
+    load_ids(e_first, ids, stride, nk, K, first, 0, steps, lane);
+    // Few chunks (small batches) take a short form of the reduction: the
+    // straight-line code a workgroup runs once is fetched into a cold
+    // instruction cache, so its length shows in small-batch latency.
+    if (blocks <= 16) {
+        if (E <= kThreads)
+            reduce_chunks<1, 16>(H, blocks, E, b, s.total_s, s.base);
+        else
+            reduce_chunks<4, 16>(H, blocks, E, b, s.total_s, s.base);
+    } else if (E <= kThreads) {
+        reduce_chunks<1, kMaxChunks>(H, blocks, E, b, s.total_s, s.base);
+    } else if (E <= 2 * kThreads) {
+        reduce_chunks<2, kMaxChunks / 2>(H, blocks, E, b, s.total_s, s.base);
+    } else {
+        reduce_chunks<4, kMaxChunks / 4>(H, blocks, E, b, s.total_s, s.base);
+    }
+    for (int x = threadIdx.x; x < kWaves * E; x += kThreads) s.cnt[x] = 0;
+    __syncthreads();
+
+    segment_starts(s, b, E, align, M, counts, offsets, status, layout_range, recv_stats);
+    if (b == 0 && status != nullptr && wave == 0) {
+        int32_t nb = 0;
+        for (int g = lane; g < blocks; g += kWave) nb += bad[g];
+        nb = wave_sum(nb);
+        if (lane == 0) status[0] = nb;
+    }
+    uint64_t peers[B];
+    // (assign_count's first barrier also orders segment_starts' base writes
+    // before assign_rank reads them)
+    assign_count<B, PLAN>(s, e_first, peers, ids, stride, nk, K, E, nbits, chunk, b, active);
+    assign_rank<B, PLAN>(s, e_first, peers, ids, stride, nk, K, E, nbits, chunk, b, active, pos,
+                         row_pair, cap, M, PLAN ? order : nullptr);
+    mark_unused_rows(s, b, E, align, M, cap, row_pair);
+}
+
+// ---------------------------------------------------------------------------
+// One launch for mid-size batches (kOneLaunchPairs < N*K <= kOnePassMaxPairs,
+// contiguous 16-byte-aligned ids): no histogram kernel and no workspace.
+// Every workgroup counts the whole batch itself. Its threads issue all their
+// 16-byte id loads at once (kOnePassLoads per thread, one round), and while
+// they are in flight count the workgroup's own chunk per wave (the first
+// half of layout_assign's assignment, which needs no other chunk). Then each
+// valid pair adds to a counter of its expert with one LDS atomic: 1 in the
+// low half and, for a pair before the workgroup's chunk, also 1 in the high
+// half. Additions commute, so the totals and the earlier-chunk counts are
+// the same for any order of the atomics, and N*K < 2^16 keeps the halves
+// apart. The offsets and the rows of the chunk then follow as in
+// layout_assign. At the prefill size this replaces two launches (and a
+// second pass over the ids) with one; each workgroup reads the whole 128 KB
+// of ids, from L2 after the first workgroup of its XCD.
+// ---------------------------------------------------------------------------
+constexpr int kOnePassLoads = 32;   // 16-byte loads per thread
+constexpr uint32_t kOnePassRound = (uint32_t)kThreads * 4 * kOnePassLoads;   // pairs
+constexpr int kOnePassWords = 6144;  // LDS words of the counters
+
+// The counters: E + 2 slots of R = 2^RL copies each. Slot 0 takes masked
+// ids (< 0, never read), slot e + 1 expert e, slot E + 1 ids >= E; copy
+// (lane mod R) of slot q is word q*R + (lane mod R), so lanes of one wave
+// that count the same expert spread over R words instead of serialising on
+// one. R = 16 up to E = 382, 8 up to 766, else 4 (within kOnePassWords). A
+// slot's count is the sum of its copies; the low halves sum to at most
+// N*K < 2^16, so the words are summed whole.
+inline int onepass_copies_log2(int32_t E) {
+    return (E + 2) * 16 <= kOnePassWords ? 4 : (E + 2) * 8 <= kOnePassWords ? 3 : 2;
+}
+
+// The ids of pairs 0 .. kOnePassRound - 1, 16 bytes per load; reads past
+// the last id return 0 (and are skipped by count_ids).
+__device__ __forceinline__ void load_all_ids(u32x4 (&x)[kOnePassLoads],
+                                             const int32_t* __restrict__ ids, uint32_t nk) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(ids), 0, (int32_t)(nk * 4u), kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kOnePassLoads; ++j) {
+        const uint32_t i0 = ((uint32_t)j * kThreads + threadIdx.x) * 4u;
+        x[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int32_t)(i0 * 4u), 0, 0));
+    }
+}
+
+// Counts the loaded ids (CHECK: some of them past nk). The slot of an id is
+// a clamp to [-1, E] plus one: no branch around the atomic. `before` is a
+// multiple of 4 or at least nk, so the four ids of one 16-byte load lie on
+// the same side of it. `mine` is this lane's copy of slot 0.
+template <bool CHECK, int RL>
+__device__ __forceinline__ void count_ids(const u32x4 (&x)[kOnePassLoads], uint32_t nk,
+                                          int32_t E, uint32_t before,
+                                          uint32_t* __restrict__ mine) {
+#pragma unroll
+    for (int j = 0; j < kOnePassLoads; ++j) {
+        const uint32_t i0 = ((uint32_t)j * kThreads + threadIdx.x) * 4u;
+        const uint32_t add = i0 < before ? 0x10001u : 1u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int32_t q = min(max((int32_t)x[j][c], -1), E) + 1;
+            if (!CHECK || i0 + c < nk) atomicAdd(&mine[q << RL], add);
+        }
+    }
+}
+
+// Sum of the R copies of slot q (16-byte LDS reads; q*R*4 is a multiple of 16).
+template <int RL>
+__device__ __forceinline__ uint32_t slot_sum(const uint32_t* counters, int q) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(counters + (q << RL));
+    u32x4 a = v[0];
+#pragma unroll
+    for (int r = 1; r < (1 << RL) / 4; ++r) a += v[r];
+    return a[0] + a[1] + a[2] + a[3];
+}
+
+template <int B, int RL, bool PLAN>
+__global__ __launch_bounds__(kThreads) void layout_onepass(
+    const int32_t* __restrict__ ids, uint32_t nk, uint32_t K, int32_t E, int32_t chunk,
+    int nbits, int32_t blocks, int32_t align, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ status, int32_t* __restrict__ pos,
+    int32_t* __restrict__ row_pair, int64_t cap, int32_t M, int32_t* __restrict__ order,
+    int64_t* __restrict__ layout_range, int32_t* __restrict__ recv_stats) {
+    constexpr int R = 1 << RL;
+    __shared__ AssignLds<PLAN> s;
+    __shared__ __attribute__((aligned(16))) uint32_t counters[kOnePassWords];   // slot q, copy r at q*R + r
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x;
+    const bool active = b < blocks;
+    const int quarter = chunk / kWaves;
+    const int steps = active ? quarter / kWave : 0;
+    const uint32_t first = (uint32_t)b * chunk + (threadIdx.x / kWave) * quarter;
+
+    int32_t e_first[B];
+    load_ids(e_first, ids, (int64_t)K, nk, K, first, 0, steps, lane);
+    u32x4 x[kOnePassLoads];
+    load_all_ids(x, ids, nk);
+    u32x4* const c4 = reinterpret_cast<u32x4*>(counters);
+    for (int i = threadIdx.x; i < (E + 2) * (R / 4); i += kThreads) c4[i] = u32x4{0, 0, 0, 0};
+    for (int i = threadIdx.x; i < kWaves * E; i += kThreads) s.cnt[i] = 0;
+    __syncthreads();
+
+    // The own chunk, while the loads of all ids are in flight.
+    uint64_t peers[B];
+    assign_count<B, PLAN>(s, e_first, peers, ids, (int64_t)K, nk, K, E, nbits, chunk, b, active);
+
+    const uint32_t before = active ? (uint32_t)b * chunk : nk;
+    uint32_t* const mine = counters + (lane & (R - 1));
+    if (nk == kOnePassRound)
+        count_ids<false, RL>(x, nk, E, before, mine);
+    else
+        count_ids<true, RL>(x, nk, E, before, mine);
+    __syncthreads();
+    // Experts tid, tid + 256, ...: totals (low halves) and pairs before the
+    // chunk (high halves); thread 0 also takes the ids >= E.
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        const uint32_t w = slot_sum<RL>(counters, e + 1);
+        s.total_s[e] = (int32_t)(w & 0xffffu);
+        s.base[e] = (int32_t)(w >> 16);
+    }
+    const int32_t nbad = threadIdx.x == 0 ? (int32_t)(slot_sum<RL>(counters, E + 1) & 0xffffu) : 0;
+    __syncthreads();
+
+    segment_starts(s, b, E, align, M, counts, offsets, status, layout_range, recv_stats);
+    if (b == 0 && status != nullptr && threadIdx.x == 0) status[0] = nbad;
+    __syncthreads();   // segment_starts' base writes before assign_rank reads them
+    assign_rank<B, PLAN>(s, e_first, peers, ids, (int64_t)K, nk, K, E, nbits, chunk, b, active,
+                         pos, row_pair, cap, M, PLAN ? order : nullptr);
+    mark_unused_rows(s, b, E, align, M, cap, row_pair);
 }
 
 }  // namespace
@@ -539,6 +753,67 @@ static void launch_layout(const Plan& p, uint32_t assign_grid, const int32_t* id
         launch_layout_b<kBatchSmall>(p, assign_grid, ids, stride, nk, K, E, align, H, bad, counts,
                                      offsets, status, pos, row_pair, cap, M, order, layout_range,
                                      recv_stats, stream);
+}
+
+// Mid-size batches of contiguous, 16-byte-aligned ids take layout_onepass:
+// one launch, no workspace reads or writes. The limit keeps N*K below 2^16
+// (the packed counters) and one round of id loads per thread.
+constexpr int64_t kOnePassMaxPairs = (int64_t)kThreads * 4 * kOnePassLoads;
+static_assert(kOnePassMaxPairs < (1 << 16), "packed counters hold N*K < 2^16");
+
+static bool use_onepass(const int32_t* ids, int64_t stride, int32_t K, int64_t nk) {
+    return nk > kOneLaunchPairs && nk <= kOnePassMaxPairs && stride == (int64_t)K &&
+           aligned(ids, 16);
+}
+
+template <int B, int RL>
+static void launch_onepass_br(const Plan& p, uint32_t grid, const int32_t* ids, int64_t nk,
+                              int32_t K, int32_t E, int32_t align, int32_t* counts,
+                              int32_t* offsets, int32_t* status, int32_t* pos, int32_t* row_pair,
+                              int64_t cap, int32_t M, int32_t* order, int64_t* layout_range,
+                              int32_t* recv_stats, hipStream_t stream) {
+    if (order != nullptr)
+        layout_onepass<B, RL, true><<<grid, kThreads, 0, stream>>>(
+            ids, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, counts, offsets,
+            status, pos, row_pair, cap, M, order, layout_range, recv_stats);
+    else
+        layout_onepass<B, RL, false><<<grid, kThreads, 0, stream>>>(
+            ids, (uint32_t)nk, (uint32_t)K, E, p.chunk, p.nbits, p.blocks, align, counts, offsets,
+            status, pos, row_pair, cap, M, nullptr, layout_range, recv_stats);
+}
+
+template <int B>
+static void launch_onepass_b(const Plan& p, uint32_t grid, const int32_t* ids, int64_t nk,
+                             int32_t K, int32_t E, int32_t align, int32_t* counts,
+                             int32_t* offsets, int32_t* status, int32_t* pos, int32_t* row_pair,
+                             int64_t cap, int32_t M, int32_t* order, int64_t* layout_range,
+                             int32_t* recv_stats, hipStream_t stream) {
+    switch (onepass_copies_log2(E)) {
+    case 4:
+        launch_onepass_br<B, 4>(p, grid, ids, nk, K, E, align, counts, offsets, status, pos,
+                                row_pair, cap, M, order, layout_range, recv_stats, stream);
+        break;
+    case 3:
+        launch_onepass_br<B, 3>(p, grid, ids, nk, K, E, align, counts, offsets, status, pos,
+                                row_pair, cap, M, order, layout_range, recv_stats, stream);
+        break;
+    default:
+        launch_onepass_br<B, 2>(p, grid, ids, nk, K, E, align, counts, offsets, status, pos,
+                                row_pair, cap, M, order, layout_range, recv_stats, stream);
+    }
+}
+
+static void launch_onepass(const Plan& p, uint32_t grid, const int32_t* ids, int64_t nk,
+                           int32_t K, int32_t E, int32_t align, int32_t* counts, int32_t* offsets,
+                           int32_t* status, int32_t* pos, int32_t* row_pair, int64_t cap,
+                           int32_t M, int32_t* order, int64_t* layout_range, int32_t* recv_stats,
+                           hipStream_t stream) {
+    if (p.chunk / kThreads > kBatchSmall)
+        launch_onepass_b<kBatchLarge>(p, grid, ids, nk, K, E, align, counts, offsets, status, pos,
+                                      row_pair, cap, M, order, layout_range, recv_stats, stream);
+    else
+        launch_onepass_b<kBatchSmall>(p, grid, ids, nk, K, E, align, counts, offsets, status, pos,
+                                      row_pair, cap, M, order, layout_range, recv_stats, stream);
 }
 
 extern "C" int64_t moe_required_capacity(int32_t N, int32_t K, int32_t E, int32_t align) {
@@ -603,6 +878,11 @@ static int run_layout(const char* fn, const int32_t* ids, int64_t ids_row_stride
                                  row_pair, cap, order, status, stream);
     const Plan p = make_plan(N, K, E);
     clear_launch_error();
+    if (use_onepass(ids, ids_row_stride, K, nk)) {
+        launch_onepass(p, p.blocks, ids, nk, K, E, align, counts, offsets, status, pos, row_pair,
+                       cap, 0, order, nullptr, nullptr, stream);
+        return check_launch(fn);
+    }
     int32_t* bad = H + (int64_t)p.blocks * E;
     launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
                   counts, offsets, status, pos, row_pair, cap, 0, order, nullptr, nullptr, stream);
@@ -743,7 +1023,12 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
     if (grid > 256) grid = 256;
     if (grid < p.blocks) grid = p.blocks;
     if (grid < 1) grid = 1;
-    launch_layout(p, (uint32_t)grid, ids, ids_row_stride, nk, K, E, 1, H, bad, counts, nullptr,
-                  status, pos, row_pair, cap, M, nullptr, layout_range, recv_stats, stream);
+    if (use_onepass(ids, ids_row_stride, K, nk))
+        launch_onepass(p, (uint32_t)grid, ids, nk, K, E, 1, counts, nullptr, status, pos,
+                       row_pair, cap, M, nullptr, layout_range, recv_stats, stream);
+    else
+        launch_layout(p, (uint32_t)grid, ids, ids_row_stride, nk, K, E, 1, H, bad, counts,
+                      nullptr, status, pos, row_pair, cap, M, nullptr, layout_range, recv_stats,
+                      stream);
     return check_launch("moe_get_layout_padded");
 }

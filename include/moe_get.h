@@ -124,6 +124,11 @@ size_t moe_layout_workspace_bytes(int32_t N, int32_t K, int32_t E);
  *        bytes, 4-byte aligned; not shared with a concurrent call.
  *   status          (device, out, may be NULL) number of ids >= E.
  *
+ * Launches (the outputs are the same in every form): one for batches of at
+ * most 2048 pairs, and one for 2049 .. 32768 pairs whose ids are contiguous
+ * (ids_row_stride == K) and start on a 16-byte boundary; two otherwise. The
+ * one-launch forms do not touch the workspace, which is still checked.
+ *
  * Limits: 1 <= K <= 32, 1 <= E <= 1024, N >= 0, N*K < 2^31. Pointers must be
  * 4-byte aligned. Errors: MOE_ERR_ARG, MOE_ERR_LIMIT, MOE_ERR_CAPACITY,
  * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.

@@ -375,10 +375,71 @@ def test_wide_rows(mg, Hc, N):
         assert np.array_equal(host(scales).view(np.uint32), ref.view(np.uint32))
 
 
+def misaligned_copy(ids: np.ndarray) -> torch.Tensor:
+    """The ids on the GPU at an address 4 bytes past a 16-byte boundary (still
+    contiguous), which routes a layout away from its one-pass form."""
+    flat = torch.empty(ids.size + 1, dtype=torch.int32, device="cuda")
+    view = flat[1:].view(ids.shape)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(ids)))
+    assert view.data_ptr() % 16 == 4
+    return view
+
+
+@pytest.mark.parametrize("N,K,E,align", [(2049, 1, 64, 1), (1025, 4, 256, 16), (1537, 8, 1024, 1),
+                                         (4096, 8, 256, 1), (4096, 8, 256, 8), (4096, 8, 128, 1),
+                                         (8192, 4, 512, 4), (32768, 1, 256, 1),
+                                         (32769, 1, 256, 1), (4097, 8, 256, 1)])
+def test_layout_around_the_one_pass_limits(mg, N, K, E, align):
+    """Batches of 2049 .. 32768 contiguous, 16-byte-aligned pairs take the
+    one-pass layout (every workgroup counts the whole batch); a ragged last
+    round of loads (N*K not a multiple of 1024), E up to 1024 (16 chunks),
+    alignment padding, masks, ids >= E and a hot expert. The same ids 4 bytes
+    off a 16-byte boundary take the two kernels; both match the oracle, and
+    so do the plans' tiles."""
+    rng = np.random.default_rng(N * 7 + K + E + align)
+    ids = mw.uniform_distinct_ids(rng, N, K, E) if K <= E else rng.integers(0, E, (N, K))
+    ids = ids.astype(np.int32)
+    ids[rng.random((N, K)) < 0.05] = -1
+    ids[rng.random((N, K)) < 0.01] = E + 2
+    ids[rng.random((N, K)) < 0.1] = 3                 # hot expert
+    cap = oracle.required_cap(N, K, E, align) + 5
+    for form, ids_d in (("aligned", dev(ids)), ("misaligned", misaligned_copy(ids))):
+        say(f"layout N={N} K={K} E={E} align={align} ids {form}")
+        lay = mg.layout(ids_d, E, align=align, cap=cap)
+        pos = check_layout(mg, lay, ids, E, align, cap)
+        check_plan(lay.order, pos, tile=plan_tile(N, K, E))
+
+
+@pytest.mark.parametrize("N,E,M", [(4096, 256, 4096), (3000, 64, 200), (1024, 128, 96)])
+def test_padded_layout_one_pass(mg, N, E, M):
+    """The padded layout on 2049 .. 32768 pairs: the one-pass form marks the
+    E*M rows from more workgroups than chunks; pairs past an expert's M rows
+    dropped; the ids off a 16-byte boundary take the two kernels."""
+    rng = np.random.default_rng(N + E + M)
+    K = 8
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.05] = -1
+    ids[rng.random((N, K)) < 0.01] = E
+    c, p, rp, st = oracle.layout_padded(ids, E, M)
+    for form, ids_d in (("aligned", dev(ids)), ("misaligned", misaligned_copy(ids))):
+        counts = torch.full((E,), -3, dtype=torch.int32, device="cuda")
+        pos = torch.full((N, K), -3, dtype=torch.int32, device="cuda")
+        row_pair = torch.full((E * M,), -3, dtype=torch.int32, device="cuda")
+        status = torch.full((2,), -3, dtype=torch.int32, device="cuda")
+        ws = torch.empty(mg.moe_layout_workspace_bytes(N, K, E), dtype=torch.uint8, device="cuda")
+        say(f"padded layout N={N} E={E} M={M} ids {form}")
+        mg.moe_get_layout_padded(ids_d, E, M, counts, pos, row_pair, ws, status)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(counts), c) and np.array_equal(host(pos), p)
+        assert np.array_equal(host(row_pair), rp)
+        assert tuple(host(status).tolist()) == st
+
+
 @pytest.mark.parametrize("N,K,E", [(4096, 8, 256), (4097, 8, 256), (4096, 8, 600)])
 def test_layout_paths_agree_on_uniform_and_skewed_ids(mg, N, K, E):
-    """Both layout forms (one workgroup, and histogram + assign) against the
-    oracle on the same kind of routing, with masks and a hot expert."""
+    """The layout forms (one pass at 32768 pairs, histogram + assign past it)
+    against the oracle on the same kind of routing, with masks and a hot
+    expert."""
     rng = np.random.default_rng(N + E)
     ids = mw.uniform_distinct_ids(rng, N, K, E)
     ids[rng.random((N, K)) < 0.05] = -1
