@@ -26,7 +26,10 @@ from typing import List, Optional, Sequence, Tuple
 import torch  # loaded first so the library binds to the same HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_get.so")
+# MOE_DEBUG=1 loads the debug build, in which every layout call also checks
+# its outputs on the device (read the counts with debug_status()).
+DEBUG = os.environ.get("MOE_DEBUG", "") == "1"
+LIB_PATH = os.path.join(_PKG, "libmoe_get_debug.so" if DEBUG else "libmoe_get.so")
 
 MOE_OK = 0
 MOE_ERR_ARG = -1
@@ -66,8 +69,10 @@ class moe_epilogue(ctypes.Structure):
                 ("residual_out", ctypes.c_void_p), ("residual_out_row_stride", ctypes.c_int64)]
 
 
-def _load():
-    L = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH):
+    """The library at `path` (default: the one selected above) with every
+    entry point's argument and result types set."""
+    L = ctypes.CDLL(path)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.moe_version.restype = ctypes.c_int
     L.moe_last_error.restype = ctypes.c_char_p
@@ -109,6 +114,10 @@ def _load():
     L.moe_combine_backward.restype = ctypes.c_int
     L.moe_scatter_scales.argtypes = [P, i64, i32, i32, i32, P, i32, i32, P, i32, P]
     L.moe_scatter_scales.restype = ctypes.c_int
+    L.moe_check_layout.argtypes = [P, i32, i32, P, i64, P, P, P]
+    L.moe_check_layout.restype = ctypes.c_int
+    L.moe_debug_status.argtypes = [P, i32, P]
+    L.moe_debug_status.restype = ctypes.c_int
     return L
 
 
@@ -555,6 +564,39 @@ def moe_combine_epilogue(y: torch.Tensor, weights: torch.Tensor, pos: torch.Tens
     op, os_ = _rows(out, "out") if N else (0, Hc)
     _check(_lib.moe_combine_epilogue(yp, ys, wp, ws, _dev(pos, "pos"), N, K, Hc,
                                      ctypes.byref(ep), op, os_, _stream(stream)))
+
+
+def moe_check_layout(pos: torch.Tensor, row_pair: Optional[torch.Tensor],
+                     order: Optional[torch.Tensor], status: torch.Tensor, stream=None) -> None:
+    """Adds to status (int32 [4], device) the counts of a layout's
+    inconsistencies: pos entries outside [-1, cap), pairs whose row does not
+    name them, rows that name a pair not pointing back, plan entries that are
+    not pairs with a row. cap = row_pair.numel() (row_pair may be None only
+    with cap 0: then every valid pos counts as out of range)."""
+    if pos.dim() != 2:
+        raise ValueError("pos must be [N, K]")
+    N, K = pos.shape
+    for n, t in (("pos", pos), ("row_pair", row_pair), ("order", order), ("status", status)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    if status.numel() < 4:
+        raise ValueError("status needs 4 entries")
+    if order is not None and order.numel() != N * K:
+        raise ValueError("order must hold N*K entries")
+    cap = row_pair.numel() if row_pair is not None else 0
+    _check(_lib.moe_check_layout(_dev(pos, "pos"), N, K, _dev(row_pair, "row_pair"), cap,
+                                 _dev(order, "order"), _dev(status, "status"), _stream(stream)))
+
+
+def debug_status(reset: bool = False, stream=None) -> Tuple[int, int, int, int, int]:
+    """The debug build's counters (MOE_DEBUG=1): the sums of moe_check_layout's
+    four counts over every layout call since the library loaded or the last
+    reset, then the number of layout calls checked. Raises MoeError in the
+    release build."""
+    out = (ctypes.c_int32 * 5)()
+    _check(_lib.moe_debug_status(ctypes.cast(out, ctypes.c_void_p), int(bool(reset)),
+                                 _stream(stream)))
+    return tuple(int(v) for v in out)
 
 
 # ---------------------------------------------------------------------------

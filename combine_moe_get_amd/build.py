@@ -1,6 +1,9 @@
-"""Build libmoe_get.so (the C-ABI HIP library) in-tree for gfx950, and
-libmoe_ceilings.so, the bandwidth-ceiling kernels `bench.py --ceilings` times
-(a separate library: the product library holds none of them).
+"""Build libmoe_get.so (the C-ABI HIP library) in-tree for gfx950, its debug
+build libmoe_get_debug.so (the same sources with MOE_DEBUG: every layout call
+also checks its outputs on the device, see moe_debug_status; loaded by the
+binding when MOE_DEBUG=1 is set), and libmoe_ceilings.so, the
+bandwidth-ceiling kernels `bench.py --ceilings` times (a separate library:
+the product library holds none of them).
 
     python combine_moe_get_amd/build.py
 
@@ -23,7 +26,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_get.so")
-SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "quant.hip"]
+DEBUG_LIB = os.path.join(PKG, "libmoe_get_debug.so")
+SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip", "quant.hip", "check.hip"]
 CEIL_LIB = os.path.join(PKG, "libmoe_ceilings.so")
 CEIL_SOURCES = ["ceilings.hip"]
 ARCH = "gfx950"
@@ -51,20 +55,25 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
 
-    def compile_one(src):
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        out = _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    def compile_one(job):
+        src, debug = job
+        stem = os.path.splitext(src)[0] + ("_debug" if debug else "")
+        obj = os.path.join(objdir, stem + ".o")
+        flags = CFLAGS + (["-DMOE_DEBUG=1"] if debug else [])
+        out = _run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out:
             print(out, file=sys.stderr)
         return obj
 
-    srcs = SOURCES + CEIL_SOURCES
-    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
-    for lib, names in ((LIB, SOURCES), (CEIL_LIB, CEIL_SOURCES)):
+    jobs = [(s, False) for s in SOURCES + CEIL_SOURCES] + [(s, True) for s in SOURCES]
+    workers = min(len(jobs), os.cpu_count() or 4, 16)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = dict(zip(jobs, ex.map(compile_one, jobs)))
+    for lib, names, debug in ((LIB, SOURCES, False), (DEBUG_LIB, SOURCES, True),
+                              (CEIL_LIB, CEIL_SOURCES, False)):
         tmp = lib + ".tmp"
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[n] for n in names],
-              "-o", tmp])
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+              *[objs[(n, debug)] for n in names], "-o", tmp])
         os.replace(tmp, lib)
     return LIB
 

@@ -373,7 +373,9 @@ static int launch_layout_dispatch(const DispatchArgs& a, bool all16, const int32
         layout_dispatch_kernel<u32x4><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
     else
         layout_dispatch_kernel<uint32_t><<<(uint32_t)blocks, kThreads, 0, stream>>>(a, f);
-    return check_launch(who);
+    const int rc = check_launch(who);
+    if (rc != MOE_OK) return rc;
+    return debug_check_layout(who, pos, (int64_t)a.N * a.K, row_pair, cap, order, stream);
 }
 
 extern "C" int moe_layout_dispatch(const int32_t* ids, int64_t ids_row_stride, int32_t N,

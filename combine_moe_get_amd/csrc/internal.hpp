@@ -14,6 +14,15 @@ namespace moe {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// The debug build (compiled with -DMOE_DEBUG, libmoe_get_debug.so): every
+// layout call also checks its own outputs on the device and adds what it
+// finds to a per-device status (moe_debug_status).
+#ifdef MOE_DEBUG
+constexpr bool kDebug = true;
+#else
+constexpr bool kDebug = false;
+#endif
+
 // Records `fmt` as this thread's last error and returns `code`.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Clears this thread's last error and returns MOE_OK.
@@ -93,6 +102,12 @@ int layout_padded_one_launch(const int32_t* ids, int64_t ids_row_stride, int32_t
                              int32_t E, int32_t M, int32_t* counts, int32_t* pos,
                              int32_t* row_pair, int64_t* layout_range, int32_t* recv_stats,
                              int32_t* status, hipStream_t stream);
+
+// In the debug build, launches the check of moe_check_layout on a layout's
+// outputs (pos for nk pairs, row_pair for cap rows, the plan if given),
+// adding to the device's debug status; returns MOE_OK at once otherwise.
+int debug_check_layout(const char* fn, const int32_t* pos, int64_t nk, const int32_t* row_pair,
+                       int64_t cap, const int32_t* order, hipStream_t stream);
 
 // The one-pass layout of the one-launch forms (small batches): every
 // workgroup counts the whole batch itself. tot[E], bef[E] and *nbad live in

@@ -881,12 +881,15 @@ static int run_layout(const char* fn, const int32_t* ids, int64_t ids_row_stride
     if (use_onepass(ids, ids_row_stride, K, nk)) {
         launch_onepass(p, p.blocks, ids, nk, K, E, align, counts, offsets, status, pos, row_pair,
                        cap, 0, order, nullptr, nullptr, stream);
-        return check_launch(fn);
+    } else {
+        int32_t* bad = H + (int64_t)p.blocks * E;
+        launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H,
+                      bad, counts, offsets, status, pos, row_pair, cap, 0, order, nullptr, nullptr,
+                      stream);
     }
-    int32_t* bad = H + (int64_t)p.blocks * E;
-    launch_layout(p, p.blocks > 0 ? p.blocks : 1, ids, ids_row_stride, nk, K, E, align, H, bad,
-                  counts, offsets, status, pos, row_pair, cap, 0, order, nullptr, nullptr, stream);
-    return check_launch(fn);
+    const int rc = check_launch(fn);
+    if (rc != MOE_OK) return rc;
+    return debug_check_layout(fn, pos, nk, row_pair, cap, order, stream);
 }
 
 extern "C" int moe_get_layout(const int32_t* ids, int64_t ids_row_stride, int32_t N, int32_t K,
@@ -1030,5 +1033,7 @@ extern "C" int moe_get_layout_padded(const int32_t* ids, int64_t ids_row_stride,
         launch_layout(p, (uint32_t)grid, ids, ids_row_stride, nk, K, E, 1, H, bad, counts,
                       nullptr, status, pos, row_pair, cap, M, nullptr, layout_range, recv_stats,
                       stream);
-    return check_launch("moe_get_layout_padded");
+    const int rc = check_launch("moe_get_layout_padded");
+    if (rc != MOE_OK) return rc;
+    return debug_check_layout("moe_get_layout_padded", pos, nk, row_pair, cap, nullptr, stream);
 }

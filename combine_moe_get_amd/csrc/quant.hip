@@ -362,7 +362,10 @@ static int launch_padded_one_launch(const Fp8Args& a, const int32_t* ids, int64_
                     who, (long long)blocks, kFusedWaves * kChanPerWave);
     clear_launch_error();
     dispatch_fp8_padded_kernel<<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(a, f);
-    return check_launch(who);
+    const int rc = check_launch(who);
+    if (rc != MOE_OK) return rc;
+    return debug_check_layout(who, pos, (int64_t)a.N * a.K, row_pair, (int64_t)E * a.M, nullptr,
+                              stream);
 }
 
 extern "C" int moe_dispatch_fp8_padded(const int32_t* ids, int64_t ids_row_stride, int32_t N,

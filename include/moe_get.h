@@ -523,6 +523,54 @@ int moe_combine_backward(const void* grad_out, int64_t grad_out_row_stride, cons
                          int64_t grad_y_row_stride, float* grad_w, int64_t grad_w_row_stride,
                          hipStream_t stream);
 
+/*
+ * Device check of a layout's index arrays. moe_dispatch, moe_combine and the
+ * other calls that take pos do not bound-check it (a row outside the receive
+ * buffer is an out-of-bounds access); a caller whose pos comes from
+ * elsewhere can check it with this call first. What it checks restates the
+ * layout's definition (DeepEP, repository dump, deep_ep.cpp,
+ * Buffer::get_dispatch_layout, and the receive buffer whose recv_src_idx
+ * names each row's source): each pair has one row or none, each used row
+ * names its pair, and the dispatch plan lists pairs that have rows.
+ *
+ *   pos[N*K]       (device) rows of the pairs, as moe_get_layout writes them.
+ *   row_pair[cap]  (device, may be NULL) the pair of each row, -1 if none.
+ *   cap            rows of the receive buffer (E*M for a padded layout).
+ *   order[N*K]     (device, may be NULL) a dispatch plan.
+ *   status[4]      (device, in/out) counts added to it (it is not cleared):
+ *     [0] pairs whose pos is neither -1 nor a row < cap;
+ *     [1] pairs with a row whose row_pair entry does not name them (two pairs
+ *         in one row, or a row_pair that disagrees; row_pair given);
+ *     [2] rows whose row_pair entry is neither -1 nor a pair whose pos is
+ *         that row (row_pair given);
+ *     [3] plan entries that are neither -1 nor a pair with a row (order
+ *         given).
+ * All four zero: pos and row_pair are inverse maps between the valid pairs
+ * and the used rows, and every row moe_dispatch would write lies in the
+ * receive buffer. A plan that repeats or omits a pair is not detected (the
+ * dispatch then writes a row twice or not at all, within the buffer). Every
+ * read the check makes is guarded by the ranges it checks, so any input is
+ * safe. Limits: N*K and cap below 2^31. Errors: MOE_ERR_ARG, MOE_ERR_LIMIT,
+ * MOE_ERR_ALIGN (int32 pointers 4-byte aligned), MOE_ERR_HIP.
+ */
+int moe_check_layout(const int32_t* pos, int32_t N, int32_t K, const int32_t* row_pair,
+                     int64_t cap, const int32_t* order, int32_t* status, hipStream_t stream);
+
+/*
+ * The debug build's status (the library built with MOE_DEBUG,
+ * libmoe_get_debug.so). There, every call that writes a layout
+ * (moe_get_layout, moe_get_layout_noalloc, moe_get_layout_padded,
+ * moe_layout_dispatch, moe_dispatch_fp8_padded) also runs moe_check_layout
+ * on its own outputs, on its stream, adding to counters per GPU that start
+ * at zero when the library loads: out[0..3] as moe_check_layout's status,
+ * out[4] the number of layout calls checked. moe_debug_status copies the
+ * five to out[5] (host memory) after the stream's earlier work, and with
+ * reset != 0 then sets them to zero on the stream. out[0..3] all zero: every
+ * layout since the last reset was consistent. Errors: MOE_ERR_LIMIT in the
+ * release build; MOE_ERR_ARG (out NULL), MOE_ERR_HIP.
+ */
+int moe_debug_status(int32_t* out, int32_t reset, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -135,7 +135,14 @@ int main(void) {
                            d_order, d_ws, ws_bytes, d_status, stream));
     MOE_OK_(moe_dispatch(fields, NF, N, K, d_pos, d_order, stream));
     MOE_OK_(moe_combine(d_y, HC, d_w, K, d_pos, N, K, HC, d_out, HC, stream));
+    /* the device check of the layout's index arrays: nothing to report */
+    int32_t* d_check;
+    HIP_OK(hipMalloc((void**)&d_check, 4 * sizeof(int32_t)));
+    HIP_OK(hipMemsetAsync(d_check, 0, 4 * sizeof(int32_t), stream));
+    MOE_OK_(moe_check_layout(d_pos, N, K, d_row_pair, cap, d_order, d_check, stream));
     HIP_OK(hipStreamSynchronize(stream));
+    int32_t g_check[4];
+    HIP_OK(hipMemcpy(g_check, d_check, sizeof(g_check), hipMemcpyDeviceToHost));
 
     /* the oracle on the same inputs */
     int32_t counts[E], offsets[E + 1], status = 0;
@@ -203,6 +210,7 @@ int main(void) {
         if (g_order[i] >= N * K || pos[g_order[i]] < 0 || seen[g_order[i]]++) bad |= 1 << 10;
     }
     bad |= (n_skip != N * K - n_valid) << 10;
+    bad |= (g_check[0] | g_check[1] | g_check[2] | g_check[3]) != 0 ? 1 << 11 : 0;
     if (bad) {
         fprintf(stderr, "abi_check: mismatch mask 0x%x (max combine ulp %d)\n", bad, max_ulp);
         return 1;

@@ -29,16 +29,49 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
-def test_library_exports_every_declared_symbol():
+@pytest.mark.parametrize("name", ["libmoe_get.so", "libmoe_get_debug.so"])
+def test_library_exports_every_declared_symbol(name):
+    """The release library and its debug build (MOE_DEBUG) both export every
+    declared entry point."""
     import combine_moe_get_amd as m
 
-    lib = ctypes.CDLL(m.LIB_PATH)
+    path = os.path.join(os.path.dirname(m.__file__), name)
+    lib = ctypes.CDLL(path)
     for n in _declared_functions():
         assert hasattr(lib, n), n
-    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True,
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(_declared_functions()) <= exported
+
+
+def test_debug_build_is_selected_by_the_environment():
+    """MOE_DEBUG=1 makes the binding load libmoe_get_debug.so (checked in a
+    child process, which only imports the package)."""
+    code = ("import combine_moe_get_amd as m, os; "
+            "print(os.path.basename(m.LIB_PATH), m.DEBUG)")
+    for env_value, expect in (("1", "libmoe_get_debug.so True"), ("", "libmoe_get.so False")):
+        env = dict(os.environ, MOE_DEBUG=env_value)
+        r = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env,
+                           cwd=ROOT, timeout=300)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.strip().splitlines()[-1] == expect
+
+
+def test_debug_status_release_and_debug_argument_errors():
+    """moe_debug_status: the release build refuses (MOE_ERR_LIMIT); the debug
+    build rejects a NULL out before touching a GPU."""
+    import combine_moe_get_amd as m
+
+    pkg = os.path.dirname(m.__file__)
+    for name, code in (("libmoe_get.so", m.MOE_ERR_LIMIT), ("libmoe_get_debug.so", m.MOE_ERR_ARG)):
+        L = ctypes.CDLL(os.path.join(pkg, name))
+        L.moe_debug_status.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.moe_last_error.restype = ctypes.c_char_p
+        buf = (ctypes.c_int32 * 5)()
+        out = None if name.endswith("debug.so") else ctypes.cast(buf, ctypes.c_void_p)
+        assert L.moe_debug_status(out, 0, None) == code
+        assert b"moe_debug_status" in L.moe_last_error()
 
 
 def test_build_targets_gfx950_only():
@@ -266,6 +299,26 @@ def test_scatter_scales_validation(lib):
     assert S(*ok(sc=P + 2)) == lib.MOE_ERR_ALIGN
     assert S(*ok(N=0, ts=0)) == lib.MOE_OK                 # no pair can be valid: nothing to do
     assert S(*ok(E=0)) == lib.MOE_OK
+
+
+def test_check_layout_validation(lib):
+    C = lib._lib.moe_check_layout
+    P = 0x10000
+    # (pos, N, K, row_pair, cap, order, status, stream)
+    ok = lambda **kw: [kw.get(n, d) for n, d in (
+        ("pos", P), ("N", 16), ("K", 8), ("rp", P), ("cap", 128), ("order", P), ("st", P),
+        ("stream", 0))]
+    assert C(*ok(N=-1)) == lib.MOE_ERR_ARG
+    assert C(*ok(K=0)) == lib.MOE_ERR_ARG
+    assert C(*ok(cap=-1)) == lib.MOE_ERR_ARG
+    assert C(*ok(N=1 << 28, K=8)) == lib.MOE_ERR_LIMIT     # N*K >= 2^31
+    assert C(*ok(cap=1 << 31)) == lib.MOE_ERR_LIMIT
+    assert C(*ok(st=0)) == lib.MOE_ERR_ARG
+    assert C(*ok(pos=0)) == lib.MOE_ERR_ARG
+    assert C(*ok(pos=P + 2)) == lib.MOE_ERR_ALIGN
+    assert C(*ok(rp=P + 1)) == lib.MOE_ERR_ALIGN
+    assert C(*ok(order=P + 3)) == lib.MOE_ERR_ALIGN
+    assert C(*ok(st=P + 2)) == lib.MOE_ERR_ALIGN
 
 
 def test_backward_validation(lib):
