@@ -444,7 +444,8 @@ __device__ __forceinline__ void assign_count(AssignLds<PLAN>& s, const int32_t (
             trun += t4[j];
         }
         if (threadIdx.x == 0) s.tile_valid_s = tvalid;
-        __syncthreads();   // the t4 reads of cnt before assign_rank rewrites it
+        // (the scan's barrier already orders the t4 reads of cnt before
+        // assign_rank rewrites it)
     }
 }
 

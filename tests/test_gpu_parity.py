@@ -585,13 +585,20 @@ def test_concurrent_streams(mg):
             assert check_combine(out, y, w, pos) == 0
 
 
-@pytest.mark.parametrize("N", [256, 1024], ids=["one-launch layout", "two-kernel layout"])
-def test_graph_capture_replay(mg, N):
+@pytest.mark.parametrize("N,misalign", [(256, False), (1024, False), (1024, True)],
+                         ids=["one-launch layout", "one-pass layout", "two-kernel layout"])
+def test_graph_capture_replay(mg, N, misalign):
     """layout + dispatch + combine captured once and replayed on new inputs
     (eager work and a sync between replays); every replay checked. 2048
-    pairs take the one-launch layout, 8192 the two kernels."""
+    pairs take the one-launch layout, 8192 contiguous pairs the one-pass
+    kernel, and the same 8192 ids 4 bytes off a 16-byte boundary the two
+    kernels."""
     K, E, Hc = 8, 64, 512
-    ids_s = torch.zeros((N, K), dtype=torch.int32, device="cuda")
+    if misalign:
+        ids_s = torch.zeros(N * K + 1, dtype=torch.int32, device="cuda")[1:].view(N, K)
+        assert ids_s.data_ptr() % 16 == 4
+    else:
+        ids_s = torch.zeros((N, K), dtype=torch.int32, device="cuda")
     x_s = torch.zeros((N, 1024), dtype=torch.uint8, device="cuda")
     w_s = torch.zeros((N, K), dtype=torch.float32, device="cuda")
     y_s = torch.zeros((N * K, Hc), dtype=torch.bfloat16, device="cuda")
@@ -619,7 +626,7 @@ def test_graph_capture_replay(mg, N):
     with torch.cuda.graph(g):
         step()
     for rep in range(4):
-        say(f"graph replay {rep}, N={N}")
+        say(f"graph replay {rep}, N={N} misaligned ids={misalign}")
         rng = np.random.default_rng(50 + rep + N)
         ids = mw.uniform_distinct_ids(rng, N, K, E)
         ids[rng.random((N, K)) < 0.1] = -1
