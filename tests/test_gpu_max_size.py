@@ -185,7 +185,8 @@ def test_layout_dispatch_combine_at_the_pair_limit(mg, routed):
     # pos, checked above). Compared on the host for the first, a middle and
     # the last 2^27 rows (their pairs come from every launch piece): torch's
     # row gather (y[index] on a [2^31, 8] int16 tensor) returned wrong rows
-    # at this size. The combine below reads every received row.
+    # at this size. Then every used row, on the GPU (below). The combine
+    # reads every received row too.
     say("dispatch: checking on the host")
     R = int(lay.offsets[E])
     x_h = x.view(torch.int16).cpu().numpy()
@@ -194,6 +195,20 @@ def test_layout_dispatch_combine_at_the_pair_limit(mg, routed):
         t = lay.row_pair[s:e].cpu().numpy() // K
         assert np.array_equal(y[s:e].view(torch.int16).cpu().numpy(), x_h[t])
     del x_h
+    # Every used row, on the GPU, 2^22 rows at a time: the 16-byte rows as
+    # pairs of int64 gathered from the [2^28, 2] source (and the gather agrees
+    # with the host on the three ranges above).
+    say("dispatch: checking every used row on the GPU")
+    x64 = x.view(torch.int64)
+    y64 = y.view(torch.int64)
+    step = 1 << 22
+    for s in range(0, R, step):
+        e = min(s + step, R)
+        t = lay.row_pair[s:e].long() // K
+        assert torch.equal(y64[s:e], x64.index_select(0, t)), (s, e)
+        if s % CHUNK == 0:
+            say(f"dispatch: rows below {e} agree")
+    del x64, y64, t
 
     say("combine of the received rows")
     w = torch.randint(-2, 2, (N, K), dtype=torch.int32, device="cuda", generator=g)
