@@ -322,7 +322,12 @@ extern "C" int moe_dispatch(const moe_field* fields, int32_t nfields, int32_t N,
     if (rc != MOE_OK) return rc;
     if (N == 0 || total_bytes == 0) return ok();
     a.pos = pos;
-    a.order = total_bytes <= kPlanMaxPayloadBytes ? order : nullptr;
+    // The plan is followed only where it can pay: payloads whose tile of
+    // source rows stays in L2, and batches past kOneLaunchPairs pairs (for
+    // which the layout's plan is not the index order; below, reading a plan
+    // entry would only add a dependent load before each wave's row).
+    a.order = total_bytes <= kPlanMaxPayloadBytes && (int64_t)N * K > kOneLaunchPairs ? order
+                                                                                       : nullptr;
     a.N = N;
     a.K = K;
     const int64_t waves = (int64_t)N * K * a.segs;

@@ -193,8 +193,11 @@ typedef struct moe_field {
  *        the receive buffer's memory prefers (see moe_get_layout). It is a
  *        hint: payloads above 8 KiB per token are copied in index order
  *        whatever order holds, because a tile's source rows would no longer
- *        stay in L2. Entries must be -1 or pair indices below N*K, each
- *        valid pair exactly once; they are trusted, as pos is.
+ *        stay in L2, and so are batches of at most 2048 pairs (for which
+ *        moe_get_layout's plan is the index order anyway), sparing each wave
+ *        the dependent read of its plan entry. Entries must be -1 or pair
+ *        indices below N*K, each valid pair exactly once; they are trusted,
+ *        as pos is.
  *
  * Rows no pair maps to are left untouched. Two pairs must not share a row
  * (moe_get_layout guarantees it). Alignment: row_bytes, both strides and
