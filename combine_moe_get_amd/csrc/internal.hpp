@@ -115,25 +115,40 @@ int debug_check_layout(const char* fn, const int32_t* pos, int64_t nk, const int
 // stride; contiguous ids, stride == K, without a division by K): each valid
 // id to tot[id] and, for pairs of earlier tokens (i < before), to bef[id];
 // ids >= E to *nbad. LDS integer atomics: the sums do not depend on their
-// order. The caller synchronizes before and after.
+// order. Each thread loads kIdBatch ids, from clamped indices so that no
+// load sits under a branch, before it counts any: up to kIdBatch * blockDim.x
+// pairs cost one dependent memory round trip rather than one per
+// blockDim.x pairs. The caller synchronizes before and after.
+constexpr int kIdBatch = 8;
+
 __device__ __forceinline__ void count_batch_ids(const int32_t* __restrict__ ids, int64_t stride,
                                                 int32_t nk, int32_t K, int32_t E, int32_t before,
                                                 int32_t* tot, int32_t* bef, int32_t* nbad) {
     const bool contiguous = stride == (int64_t)K;
+    const int32_t step = (int32_t)blockDim.x;
     int32_t bad = 0;
-    for (int32_t i = threadIdx.x; i < nk; i += blockDim.x) {
-        int32_t e;
-        if (contiguous) {
-            e = ids[i];
-        } else {
-            const int32_t ti = i / K;
-            e = ids[(int64_t)ti * stride + (i - ti * K)];
+    for (int32_t i0 = threadIdx.x; i0 < nk; i0 += kIdBatch * step) {
+        int32_t e[kIdBatch];
+#pragma unroll
+        for (int j = 0; j < kIdBatch; ++j) {
+            const int32_t i = min(i0 + j * step, nk - 1);
+            if (contiguous) {
+                e[j] = ids[i];
+            } else {
+                const int32_t ti = i / K;
+                e[j] = ids[(int64_t)ti * stride + (i - ti * K)];
+            }
         }
-        if (e >= E) {
-            ++bad;
-        } else if (e >= 0) {
-            atomicAdd(&tot[e], 1);
-            if (i < before) atomicAdd(&bef[e], 1);
+#pragma unroll
+        for (int j = 0; j < kIdBatch; ++j) {
+            const int32_t i = i0 + j * step;
+            const int32_t ej = i < nk ? e[j] : -1;
+            if (ej >= E) {
+                ++bad;
+            } else if (ej >= 0) {
+                atomicAdd(&tot[ej], 1);
+                if (i < before) atomicAdd(&bef[ej], 1);
+            }
         }
     }
     if (bad) atomicAdd(nbad, bad);
