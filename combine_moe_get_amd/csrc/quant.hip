@@ -264,17 +264,20 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fp8_padded_kernel(cons
 // scale of block b is token_scales[(r / K)*tss + b]. Written by destination
 // row, every store is a run along m: one wave takes 64 consecutive rows of
 // one expert, loads their row_pair entries once, gathers each lane's token
-// scales (kGather blocks in flight) and stores one 256-byte run per block
-// (fp32) or per 4-block word (UE8M0). Entries outside [0, N*K) count as
-// unused, so the gathers stay inside the token scales whatever row_pair
-// holds. With M a power of two (a column stride of 4*M bytes) the rows in
-// use of all columns share their low address bits, so these stores crowd
-// onto a few memory channels and those channels, not the bytes written,
-// bound the kernel (measured: ~4x longer at M = 4096 than at M = 4128).
+// scales and stores one 256-byte run per block (fp32) or per 4-block word
+// (UE8M0). Entries outside [0, N*K) count as unused, so the gathers stay
+// inside the token scales whatever row_pair holds.
+//
+// The gathers are unconditional, so that all of them are in flight at once:
+// a lane without a row reads token 0's scales and stores nothing, and block
+// indices past the last block are clamped to it. (Loads under a per-lane
+// condition each wait for the one before: a wave's kGather gathers would
+// take kGather round trips.) With 16-byte aligned token rows and H % 512 ==
+// 0 a lane fetches four blocks per load.
 // ---------------------------------------------------------------------------
 
 constexpr int kScatterThreads = 256;
-constexpr int kGather = 32;   // blocks (fp32) or words (UE8M0) in flight per lane
+constexpr int kGather = 64;   // floats gathered per lane and pass
 
 struct ScatterArgs {
     const float* ts;
@@ -285,6 +288,35 @@ struct ScatterArgs {
     int32_t mode;
 };
 
+// Units u0 .. u0 + J - 1 of one token's scales, each index clamped to the
+// last unit (nu - 1). A unit is 4 blocks (QUAD: one 16-byte load when VEC) or
+// one block.
+template <bool VEC, bool QUAD, int J>
+__device__ __forceinline__ void gather_units(const float* src, int32_t u0, int32_t nu,
+                                             float (&v)[kGather]) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int32_t u = min(u0 + j, nu - 1);
+        if constexpr (QUAD && VEC) {
+            const u32x4 q = reinterpret_cast<const u32x4*>(src)[u];
+            v[4 * j] = __uint_as_float(q.x);
+            v[4 * j + 1] = __uint_as_float(q.y);
+            v[4 * j + 2] = __uint_as_float(q.z);
+            v[4 * j + 3] = __uint_as_float(q.w);
+        } else if constexpr (QUAD) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[4 * j + c] = src[4 * u + c];
+        } else {
+            v[j] = src[u];
+        }
+    }
+    // Keep the loads here: the stores that use them sit under a per-lane
+    // condition, into which the compiler would otherwise sink them.
+#pragma unroll
+    for (int j = 0; j < (QUAD ? 4 * J : J); ++j) asm volatile("" : "+v"(v[j]));
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kScatterThreads) void scatter_scales_kernel(const ScatterArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(
@@ -295,39 +327,54 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_scales_kernel(const S
     const int32_t r = m < a.M ? a.row_pair[(int64_t)e * a.M + m] : -1;
     const bool valid = r >= 0 && r < a.NK;
     if (__ballot(valid) == 0) return;
-    const float* src = a.ts + (valid ? (int64_t)(r / a.K) * a.tss : 0);
+    const float* src = a.ts + (valid ? (int64_t)(r / a.K) * a.tss : 0);   // N >= 1
 
+    if (a.mode == MOE_SCALE_COLS && !VEC) {   // any nb: one block per unit
+        float* dst = static_cast<float*>(a.out) + (int64_t)e * a.nb * a.M + m;
+        for (int32_t u0 = 0; u0 < a.nb; u0 += kGather) {
+            float v[kGather];
+            gather_units<false, false, kGather>(src, u0, a.nb, v);
+            if (!valid) continue;
+#pragma unroll
+            for (int j = 0; j < kGather; ++j)
+                if (u0 + j < a.nb) dst[(int64_t)(u0 + j) * a.M] = v[j];
+        }
+        return;
+    }
+    constexpr int J = kGather / 4;   // quads per pass
+    const int32_t nq = a.nb / 4;
     if (a.mode == MOE_SCALE_COLS) {
         float* dst = static_cast<float*>(a.out) + (int64_t)e * a.nb * a.M + m;
-        for (int32_t b0 = 0; b0 < a.nb; b0 += kGather) {
+        for (int32_t u0 = 0; u0 < nq; u0 += J) {
             float v[kGather];
+            gather_units<VEC, true, J>(src, u0, nq, v);
+            if (!valid) continue;
 #pragma unroll
-            for (int j = 0; j < kGather; ++j)
-                if (valid && b0 + j < a.nb) v[j] = src[b0 + j];
+            for (int j = 0; j < J; ++j) {
+                const int32_t q = u0 + j;
+                if (q >= nq) break;
 #pragma unroll
-            for (int j = 0; j < kGather; ++j)
-                if (valid && b0 + j < a.nb) dst[(int64_t)(b0 + j) * a.M] = v[j];
+                for (int c = 0; c < 4; ++c) dst[(int64_t)(4 * q + c) * a.M] = v[4 * j + c];
+            }
         }
     } else {
-        // UE8M0: byte j of word w is the exponent field of block 4w + j
+        // UE8M0: byte c of word q is the exponent field of block 4q + c
         // (the scales are powers of two, so the field is the whole value).
-        const int32_t nw = a.nb / 4;
-        uint32_t* dst = static_cast<uint32_t*>(a.out) + (int64_t)e * nw * a.M + m;
-        for (int32_t w0 = 0; w0 < nw; w0 += kGather) {
-            uint32_t v[kGather];
+        uint32_t* dst = static_cast<uint32_t*>(a.out) + (int64_t)e * nq * a.M + m;
+        for (int32_t u0 = 0; u0 < nq; u0 += J) {
+            float v[kGather];
+            gather_units<VEC, true, J>(src, u0, nq, v);
+            if (!valid) continue;
 #pragma unroll
-            for (int j = 0; j < kGather; ++j) {
-                if (valid && w0 + j < nw) {
-                    const float* q = src + 4 * (w0 + j);
-                    v[j] = ((__float_as_uint(q[0]) >> 23) & 0xFFu) |
-                           (((__float_as_uint(q[1]) >> 23) & 0xFFu) << 8) |
-                           (((__float_as_uint(q[2]) >> 23) & 0xFFu) << 16) |
-                           (((__float_as_uint(q[3]) >> 23) & 0xFFu) << 24);
-                }
+            for (int j = 0; j < J; ++j) {
+                const int32_t q = u0 + j;
+                if (q >= nq) break;
+                const uint32_t w = ((__float_as_uint(v[4 * j]) >> 23) & 0xFFu) |
+                                   (((__float_as_uint(v[4 * j + 1]) >> 23) & 0xFFu) << 8) |
+                                   (((__float_as_uint(v[4 * j + 2]) >> 23) & 0xFFu) << 16) |
+                                   (((__float_as_uint(v[4 * j + 3]) >> 23) & 0xFFu) << 24);
+                dst[(int64_t)q * a.M] = w;
             }
-#pragma unroll
-            for (int j = 0; j < kGather; ++j)
-                if (valid && w0 + j < nw) dst[(int64_t)(w0 + j) * a.M] = v[j];
         }
     }
 }
@@ -546,7 +593,11 @@ extern "C" int moe_scatter_scales(const float* token_scales, int64_t token_scale
     a.mode = scale_format;
     const int64_t waves = (int64_t)E * a.chunks;
     const int64_t blocks = ceil_div<int64_t>(waves, kScatterThreads / kWave);
+    const bool vec = aligned(token_scales, 16) && token_scale_row_stride % 4 == 0 && a.nb % 4 == 0;
     clear_launch_error();
-    scatter_scales_kernel<<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(a);
+    if (vec)
+        scatter_scales_kernel<true><<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(a);
+    else
+        scatter_scales_kernel<false><<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(a);
     return check_launch("moe_scatter_scales");
 }
