@@ -192,6 +192,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 }
 
 
+// A token's K pairs (K <= MOE_MAX_TOPK) for the one-workgroup-per-token
+// kernels, staged in LDS: threads k < K load pair k's row and weight, and
+// after one barrier every wave reads them from LDS. Loading them per wave as
+// scalars waits once per pair before the pair's row can be fetched. Must be
+// called by every thread of the workgroup (it holds a barrier).
+struct TokenPairs {
+    int32_t row[MOE_MAX_TOPK];
+    float w[MOE_MAX_TOPK];
+};
+
+__device__ __forceinline__ void stage_token_pairs(TokenPairs& tp, const int32_t* prow,
+                                                  const float* wrow, int32_t K) {
+    if ((int32_t)threadIdx.x < K) {
+        tp.row[threadIdx.x] = prow[threadIdx.x];
+        tp.w[threadIdx.x] = wrow[threadIdx.x];
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Combine with an epilogue (biases; residual add + RMSNorm).
 //
@@ -254,8 +273,8 @@ __global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const Epi
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int32_t t = first_token + (int32_t)blockIdx.x;
-    const int32_t* prow = a.pos + (int64_t)t * a.K;
-    const float* wrow = a.w + (int64_t)t * a.wst;
+    __shared__ TokenPairs tp;
+    stage_token_pairs(tp, a.pos + (int64_t)t * a.K, a.w + (int64_t)t * a.wst, a.K);
 
     float acc[VPT][8];
 #pragma unroll
@@ -272,8 +291,8 @@ __global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const Epi
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) {
                 const int k = k0 + i;
-                p[i] = k < a.K ? prow[k] : -1;
-                wk[i] = k < a.K ? wrow[k] : 0.0f;
+                p[i] = k < a.K ? tp.row[k] : -1;
+                wk[i] = k < a.K ? tp.w[k] : 0.0f;
                 val[i] = load_row_words<4>(row_rsrc(a.y, a.ys, p[i], (uint32_t)a.V * 16),
                                            (uint32_t)col * 2);
             }
@@ -372,7 +391,6 @@ __global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const Bac
     const int wave = threadIdx.x / kWave;
     const int32_t t = first_token + (int32_t)blockIdx.x;
     const int32_t* prow = a.pos + (int64_t)t * a.K;
-    const float* wrow = a.w + (int64_t)t * a.wst;
     const bool want_w = a.gw != nullptr;
 
     // the token's gradient row, kept as packed bf16 (half the registers of
@@ -388,6 +406,8 @@ __global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const Bac
             for (int q = 0; q < 4; ++q) g[j].w[q] = 0u;
         }
     }
+    __shared__ TokenPairs tp;
+    stage_token_pairs(tp, prow, a.w + (int64_t)t * a.wst, a.K);
 
     for (int k0 = 0; k0 < a.K; k0 += kBatch) {
         int32_t p[kBatch];
@@ -395,8 +415,8 @@ __global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const Bac
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int k = k0 + i;
-            p[i] = k < a.K ? prow[k] : -1;
-            wk[i] = k < a.K ? wrow[k] : 0.0f;
+            p[i] = k < a.K ? tp.row[k] : -1;
+            wk[i] = k < a.K ? tp.w[k] : 0.0f;
             d[i] = 0.0f;
         }
 #pragma unroll
