@@ -333,11 +333,17 @@ STAGED_CASES = [
     ("drops, M % 64 != 0", 300, 3, 5, 1536, 50, "random"),
     ("E = 1000, tiny M", 500, 8, 1000, 512, 3, "random"),
     ("one token", 1, 4, 16, 1024, 1, "random"),
+    ("two gather passes, H = 16384", 64, 4, 16, 16384, 40, "random"),
+    ("nb % 4 != 0, H = 1152", 70, 3, 12, 1152, 30, "random"),
 ]
 
 
-@pytest.mark.parametrize("case", STAGED_CASES, ids=[c[0] for c in STAGED_CASES])
-@pytest.mark.parametrize("fmt", [1, 2], ids=["cols", "ue8m0"])
+# UE8M0 words need H % 512 == 0
+STAGED_RUNS = [(fmt, c) for fmt in (1, 2) for c in STAGED_CASES if fmt == 1 or c[4] % 512 == 0]
+
+
+@pytest.mark.parametrize("fmt,case", STAGED_RUNS,
+                         ids=[("cols-" if f == 1 else "ue8m0-") + c[0] for f, c in STAGED_RUNS])
 def test_fp8_cols_direct_and_staged(mg, case, fmt):
     """Column-major and UE8M0 scales of the padded layout, both ways: the
     one-call dispatch, and per-token scales (MOE_SCALE_TOKENS) placed by
@@ -379,16 +385,20 @@ def test_fp8_cols_direct_and_staged(mg, case, fmt):
     assert np.array_equal(dst.cpu().numpy()[used], ref_codes[used])
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
 
-    say(f"fp8 {name} format={fmt} staged")
-    dst.fill_(0xA5)
-    scales.fill_(sentinel)
-    tok = torch.full((N, H // 128 + 3), -1.0, dtype=torch.float32, device="cuda")[:, : H // 128]
-    mg.moe_dispatch_fp8(x_d, pos_d, K, dst, tok, mg.MOE_SCALE_TOKENS, 0, round_scale)
-    mg.moe_scatter_scales(tok, K, H, row_pair, E, M, scales, fmt)
-    torch.cuda.synchronize()
-    assert np.array_equal(dst.cpu().numpy(), ref_codes)
-    assert np.array_equal(tok.cpu().numpy().view(np.uint32), ref_tok.view(np.uint32))
-    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
+    # token scales with a padded row stride (one block per gather) and
+    # contiguous (four blocks per 16-byte gather when H % 512 == 0)
+    for pad in (3, 0):
+        say(f"fp8 {name} format={fmt} staged, token-scale row padding {pad}")
+        dst.fill_(0xA5)
+        scales.fill_(sentinel)
+        tok = torch.full((N, H // 128 + pad), -1.0, dtype=torch.float32,
+                         device="cuda")[:, : H // 128]
+        mg.moe_dispatch_fp8(x_d, pos_d, K, dst, tok, mg.MOE_SCALE_TOKENS, 0, round_scale)
+        mg.moe_scatter_scales(tok, K, H, row_pair, E, M, scales, fmt)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy(), ref_codes)
+        assert np.array_equal(tok.cpu().numpy().view(np.uint32), ref_tok.view(np.uint32))
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_scales.view(np.uint32))
 
 
 def test_scatter_scales_ignores_out_of_range_pairs(mg):
