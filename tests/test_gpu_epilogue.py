@@ -60,7 +60,8 @@ def _inputs(seed, N, K, E, Hc, mask=0.1):
 
 @pytest.mark.parametrize("N,K,E,Hc", [(4096, 8, 256, 7168), (64, 8, 32, 8), (37, 3, 16, 64),
                                       (100, 8, 64, 2048), (100, 8, 64, 2056), (50, 4, 16, 4096),
-                                      (30, 8, 64, 8192), (9, 2, 4, 16384), (0, 8, 16, 64)])
+                                      (30, 8, 64, 8192), (9, 2, 4, 16384), (0, 8, 16, 64),
+                                      (40, 32, 64, 256), (33, 12, 40, 1024), (20, 32, 8, 64)])
 def test_epilogue_parity(mg, N, K, E, Hc):
     say(f"N={N} K={K} E={E} Hc={Hc}")
     ids, w, y, b0, b1, res, gamma = _inputs(N * 7 + Hc, N, K, E, Hc)
