@@ -520,6 +520,40 @@ def test_explicit_stream_argument(mg):
         del junk
 
 
+@pytest.mark.parametrize("N,fused", [(281, False), (282, False), (1016, True), (1017, True)])
+def test_dispatch_on_both_sides_of_the_store_form_switch(mg, N, fused):
+    """Receives of at most 16 MiB are written with ordinary stores, larger
+    ones with non-temporal stores. moe_dispatch of the prefill fields (7456
+    bytes per row, 8 rows per token) at 281 tokens (16 761 088 bytes) and 282
+    (16 820 736); moe_layout_dispatch of 2064-byte rows at 1016 tokens
+    (16 776 192 bytes) and 1017 (16 792 704). Every byte, untouched rows
+    included, against the oracle."""
+    K, E = 8, 64
+    rng = np.random.default_rng(900 + N)
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.1] = -1
+    sizes = [2064] if fused else [7168, 224, 32, 32]
+    srcs = [rng.integers(0, 256, (N, b), dtype=np.uint8) for b in sizes]
+    _, _, pos, rp, _ = oracle.layout(ids, E)
+    ref = oracle.dispatch(srcs, pos, K, rows=N * K, fill=0xEE)
+    say(f"store forms: N={N} fused={fused}, {N * K * sum(sizes)} receive bytes")
+    if fused:
+        i32 = lambda *sh: torch.empty(sh, dtype=torch.int32, device="cuda")
+        dsts = [torch.full((N * K, b), 0xEE, dtype=torch.uint8, device="cuda") for b in sizes]
+        pos_d, rp_d = i32(N, K), i32(N * K)
+        mg.moe_layout_dispatch(dev(ids), E, 1, i32(E), i32(E + 1), pos_d, rp_d, i32(1),
+                               [dev(x) for x in srcs], dsts)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pos_d), pos) and np.array_equal(host(rp_d), rp)
+        got = [host(d) for d in dsts]
+    else:
+        lay = mg.layout(dev(ids), E)
+        check_layout(mg, lay, ids, E)
+        got = dispatch_with_plan(mg, srcs, lay, K, 0xEE)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
 @pytest.mark.parametrize("Hc,N,K", [(7168, 2340, 8), (7168, 2341, 8), (6, 32768, 12),
                                      (6, 32769, 12), (7168, 2341, 12)])
 def test_combine_on_both_sides_of_the_load_form_switch(mg, Hc, N, K):
