@@ -321,9 +321,16 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_scales_kernel(const S
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(
         blockIdx.x * (kScatterThreads / kWave) + threadIdx.x / kWave);
-    const uint32_t e = wave / (uint32_t)a.chunks;
-    if (e >= (uint32_t)a.E) return;
-    const int32_t m = (int32_t)(wave - e * (uint32_t)a.chunks) * kWave + lane;
+    // Chunk-major numbering: waves 0 .. E-1 take chunk 0 of every expert,
+    // the next E chunk 1, and so on. The used rows of an expert are its first
+    // ones, so the waves with work come first and their workgroups spread
+    // over all XCDs (workgroup i runs on XCD i mod 8). Expert-major numbering
+    // put them on the workgroups 16e at M = 4096, all on one XCD (28 us
+    // against 10 us at M = 4128 for the same bytes).
+    const uint32_t c = wave / (uint32_t)a.E;
+    if (c >= (uint32_t)a.chunks) return;
+    const uint32_t e = wave - c * (uint32_t)a.E;
+    const int32_t m = (int32_t)c * kWave + lane;
     const int32_t r = m < a.M ? a.row_pair[(int64_t)e * a.M + m] : -1;
     const bool valid = r >= 0 && r < a.NK;
     if (__ballot(valid) == 0) return;

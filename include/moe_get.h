@@ -323,9 +323,10 @@ int moe_dispatch_fp8(const void* x, int64_t x_row_stride, int32_t N, int32_t K, 
  * dump, deep_ep.cpp, Buffer::low_latency_dispatch: per expert, column-major
  * over the expert's rows; with use_ue8m0, four exponents per int32).
  * It also places per-token scales a caller already holds (its own
- * quantiser's) into the receive layout. It is not faster than the one-call
- * form: with M a power of two the rows in use of every column share the same
- * low address bits, and the stores crowd onto a few memory channels.
+ * quantiser's) into the receive layout. For fp32 column-major scales the two
+ * calls are faster than the one-call form: written by destination row, each
+ * 128-byte line of a column is stored whole, where the one-call form stores
+ * each scale on its own beside other tokens' rows.
  *
  * For every row p = e*M + m (e < E, m < M) with 0 <= row_pair[p] < N*K, i.e.
  * pair r = row_pair[p] of token t = r / K:
