@@ -81,6 +81,7 @@ _HDRS = (os.path.join(_CSRC, "internal.hpp"), os.path.join(_CSRC, "fp8.hpp"))
 KERNEL_SOURCES = {k: (os.path.join(_CSRC, f),) + _HDRS for k, f in (
     ("combine_epilogue_kernel", "combine.hip"),
     ("combine_kernel", "combine.hip"),
+    ("combine_held_kernel", "combine.hip"),
     ("dispatch_kernel", "dispatch.hip"),
     ("layout_hist", "layout.hip"),
     ("layout_assign", "layout.hip"),
@@ -91,6 +92,19 @@ KERNEL_SOURCES = {k: (os.path.join(_CSRC, f),) + _HDRS for k, f in (
     ("layout_dispatch_kernel", "dispatch.hip"),
     ("scatter_scales_kernel", "quant.hip"),
 )}
+def combine_kernel_name(N, K, Hc):
+    """The kernel moe_combine runs for N tokens, top-K and Hc channels of
+    16-byte-aligned rows (every workload here): the held form past 32768
+    waves (one per token and 64-vector segment) for K <= 8 and 8 to 224
+    segments per row, else combine_kernel. The same rule as the library's
+    (combine.hip), which also needs the device's compute-unit count (always
+    known on these GPUs) and a grid of at most 2^22 workgroups."""
+    segs = -(-(Hc // 8) // 64)
+    if N * segs > 32768 and K <= 8 and 8 <= segs <= 224:
+        return "combine_held_kernel"
+    return "combine_kernel"
+
+
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 2 << 30     # bytes read (and written) per launch by copy_bandwidth()
 
@@ -751,7 +765,7 @@ def ceilings(torch, mg, mw, reps):
         ("moe_dispatch (the product kernel), prefill, pairs in index order", "dispatch_kernel",
          algorithmic_bytes(N, K, wl.E, wl.payload_bytes(), Hc, R, sets[0].cap)[1],
          lambda i: mg.moe_dispatch(sets[i].srcs, sets[i].dsts, sets[i].pos, K)),
-        ("moe_combine (the product kernel), prefill", "combine_kernel",
+        ("moe_combine (the product kernel), prefill", combine_kernel_name(N, K, Hc),
          algorithmic_bytes(N, K, wl.E, wl.payload_bytes(), Hc, R, sets[0].cap)[2],
          lambda i: mg.moe_combine(sets[i].y, sets[i].w, sets[i].pos, sets[i].out)),
     ]
@@ -924,7 +938,7 @@ def main():
                 for _ in range(max(1, args.sets))]
         names = ("layout", "dispatch", "combine")
         op_bytes = ll_algorithmic_bytes(N, K, E, M, 7168, Hc, R, args.scale_format)
-        kernels = {"dispatch": "dispatch_fp8_kernel", "combine": "combine_kernel"}
+        kernels = {"dispatch": "dispatch_fp8_kernel", "combine": combine_kernel_name(N, K, Hc)}
         if staged:
             # the codes kernel and the scale placement, each with its share of
             # the algorithmic bytes (the staging buffer's traffic is overhead)
@@ -932,11 +946,12 @@ def main():
             names = ("layout", "dispatch", "scales", "combine")
             op_bytes = (op_bytes[0], op_bytes[1] - sb, sb, op_bytes[2])
             kernels = {"dispatch": "dispatch_fp8_kernel", "scales": "scatter_scales_kernel",
-                       "combine": "combine_kernel"}
+                       "combine": combine_kernel_name(N, K, Hc)}
         if args.fused:
             names = ("layout+dispatch", "combine")
             op_bytes = (op_bytes[0] + op_bytes[1], op_bytes[2])
-            kernels = {"layout+dispatch": "dispatch_fp8_padded_kernel", "combine": "combine_kernel"}
+            kernels = {"layout+dispatch": "dispatch_fp8_padded_kernel",
+                       "combine": combine_kernel_name(N, K, Hc)}
     elif args.backward:
         rng = np.random.default_rng(wl.seed + 7)
         host = {"y": y, "grad_out": mw.make_y(N, Hc, wl.seed + 11),
@@ -953,11 +968,13 @@ def main():
         names = ("layout", "dispatch", "combine")
         op_bytes = algorithmic_bytes(N, K, E, P, Hc, R, sets[0].cap, args.epilogue)
         kernels = {"dispatch": "dispatch_kernel",
-                   "combine": "combine_epilogue_kernel" if args.epilogue else "combine_kernel"}
+                   "combine": "combine_epilogue_kernel" if args.epilogue
+                   else combine_kernel_name(N, K, Hc)}
         if args.fused:
             names = ("layout+dispatch", "combine")
             op_bytes = (op_bytes[0] + op_bytes[1], op_bytes[2])
-            kernels = {"layout+dispatch": "layout_dispatch_kernel", "combine": "combine_kernel"}
+            kernels = {"layout+dispatch": "layout_dispatch_kernel",
+                       "combine": combine_kernel_name(N, K, Hc)}
     nops = len(names)
     stream = torch.cuda.current_stream()
     calls = [s.calls(mg, wl, stream.cuda_stream, args.epilogue) for s in sets]

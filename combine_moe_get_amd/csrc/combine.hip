@@ -14,10 +14,16 @@
 // The token's K rows and weights are wave-uniform scalar loads. Each lane
 // loads up to 8 expert rows before the first FMA; each load instruction of a
 // wave reads 1 KiB contiguous of one expert row. Small batches issue the 8
-// loads together, large ones one at a time (combine_kernel's PIPE). No MFMA:
-// nothing here is a contraction.
+// loads together, large ones one at a time (combine_kernel's PIPE). Large
+// batches of 16-byte rows with K <= 8 take the held form instead
+// (combine_held_kernel): one workgroup per compute unit at a time keeps its
+// tokens' sums in registers and stores them after its last row load. No
+// MFMA: nothing here is a contraction.
 // The final rounding uses gfx950's v_cvt_pk_bf16_f32 (round to nearest
 // even).
+#include <algorithm>
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace moe {
@@ -191,6 +197,167 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     store_words<W>(out + (int64_t)t * os + col, r);
 }
 
+
+// ---------------------------------------------------------------------------
+// The held form of the combine, for large batches of 16-byte rows with
+// K <= 8 and at least 8 segments per row.
+//
+// combine_kernel stores each output vector as soon as it is summed, so its
+// writes stream out interleaved with the expert-row reads all through the
+// launch. Here each workgroup takes T consecutive tokens (one workgroup per
+// compute unit at a time: its registers allow no second one) and keeps all
+// of their summed vectors in registers until its last row load has been
+// issued and used, then stores them together. The reads of a round of
+// workgroups then run without writes between them. The sums are the same
+// fp32 chains in k order with one rounding, so the output is bit-identical
+// to combine_kernel's. Measured at 4096 tokens of 7168 channels: 85.3-86.5
+// us against 88.7-89.0 us.
+//
+// Each wave holds up to kHeldUnits vectors (4 registers each); units are
+// (token, 64-vector segment) pairs, numbered token-major over the
+// workgroup's tokens, unit u on wave u % 8. Two units' 16 row loads are in
+// flight together. The token's pairs are staged in LDS, padded to 8 (row
+// -1, weight 0 past K), so no load waits behind a scalar fetch.
+// ---------------------------------------------------------------------------
+constexpr int kHeldThreads = 512;
+constexpr int kHeldWaves = kHeldThreads / kWave;
+constexpr int kHeldUnits = 28;        // output vectors held per lane
+constexpr int kHeldGroup = 2;         // units whose row loads are in flight together
+constexpr int kHeldMaxTokens = 64;    // tokens a workgroup stages (8 pairs each)
+
+__global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
+    const uint16_t* __restrict__ y, int64_t ys, const float* __restrict__ w, int64_t wst,
+    const int32_t* __restrict__ pos, int32_t N, int32_t K, int32_t V, int32_t segs, int32_t T,
+    uint16_t* __restrict__ out, int64_t os) {
+    __shared__ int32_t srow[kHeldMaxTokens * kBatch];
+    __shared__ float sw[kHeldMaxTokens * kBatch];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x / kWave));
+    const int64_t t0 = (int64_t)blockIdx.x * T;
+    const int32_t nt = (int32_t)min((int64_t)T, (int64_t)N - t0);
+    for (int32_t j = threadIdx.x; j < nt * kBatch; j += kHeldThreads) {
+        const int32_t tl = j / kBatch, k = j % kBatch;
+        srow[j] = k < K ? pos[(t0 + tl) * K + k] : -1;
+        sw[j] = k < K ? w[(t0 + tl) * wst + k] : 0.0f;
+    }
+    __syncthreads();
+    const int32_t units = nt * segs;
+    const uint32_t row_bytes = 16u * (uint32_t)V;
+
+    Words<4> held[kHeldUnits];
+#pragma unroll
+    for (int i0 = 0; i0 < kHeldUnits; i0 += kHeldGroup) {
+        // wave-uniform; units past the last one (g > 0) repeat its loads and
+        // are never stored
+        if (wave + kHeldWaves * i0 < units) {
+            Words<4> val[kHeldGroup][kBatch];
+            float wk[kHeldGroup][kBatch];
+            int32_t p[kHeldGroup][kBatch];
+#pragma unroll
+            for (int g = 0; g < kHeldGroup; ++g) {
+                const int32_t u = min(wave + kHeldWaves * (i0 + g), units - 1);
+                const int32_t tl = u / segs;
+                const int32_t v = (u - tl * segs) * kWave + lane;
+                int32_t pr[kBatch];
+                float wr[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    pr[k] = srow[tl * kBatch + k];
+                    wr[k] = sw[tl * kBatch + k];
+                }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    p[g][k] = __builtin_amdgcn_readfirstlane(pr[k]);
+                    wk[g][k] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int32_t, wr[k])));
+                    // lanes past the row (v >= V) read beyond the range: 0
+                    val[g][k] = load_row_words<4>(row_rsrc(y, ys, p[g][k], row_bytes),
+                                                  (uint32_t)v * 16u);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < kHeldGroup; ++g) {
+                float acc[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    if (p[g][k] < 0) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = __builtin_fmaf(wk[g][k], lo_bf16(val[g][k].w[q]), acc[2 * q]);
+                        acc[2 * q + 1] =
+                            __builtin_fmaf(wk[g][k], hi_bf16(val[g][k].w[q]), acc[2 * q + 1]);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    held[i0 + g].w[q] = pack_bf16_rne(acc[2 * q], acc[2 * q + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kHeldUnits; ++i) {
+        const int32_t u = wave + kHeldWaves * i;
+        if (u < units) {
+            const int32_t tl = u / segs;
+            const int32_t v = (u - tl * segs) * kWave + lane;
+            if (v < V) store_words<4>(out + (t0 + tl) * os + (int64_t)v * 8, held[i]);
+        }
+    }
+}
+
+// Whether combine_held_kernel keeps everything in registers (no scratch
+// memory) on this build; checked once. If it ever spilled, the plain form is
+// used throughout.
+bool held_kernel_ok() {
+    static std::once_flag once;
+    static bool ok = false;
+    std::call_once(once, [] {
+        hipFuncAttributes attr{};
+        ok = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&combine_held_kernel)) ==
+                 hipSuccess &&
+             attr.localSizeBytes == 0 && attr.maxThreadsPerBlock >= kHeldThreads;
+        (void)hipGetLastError();
+    });
+    return ok;
+}
+
+// Compute units of the device that runs `stream` (0 if unknown), looked up
+// once per device.
+int stream_cus(hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int cus[kMaxDevices];
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 0;
+        (void)hipGetLastError();
+        cus[dev] = n > 0 ? n : -1;
+    }
+    return cus[dev] > 0 ? cus[dev] : 0;
+}
+
+// Tokens per workgroup of the held form for N tokens of `segs` segments on
+// `cus` compute units, or 0 where the form does not apply. A workgroup holds
+// at most 8 * kHeldUnits units; T is the smallest count that covers the
+// batch in the fewest rounds of `cus` workgroups, so the last round is
+// nearly full.
+int32_t held_tokens(int64_t N, int32_t segs, int cus) {
+    if (cus <= 0 || segs < 8 || segs > kHeldWaves * kHeldUnits) return 0;
+    const int64_t tmax = std::min<int64_t>(kHeldWaves * kHeldUnits / segs, kHeldMaxTokens);
+    const int64_t rounds = ceil_div<int64_t>(N, (int64_t)cus * tmax);
+    const int64_t T = ceil_div<int64_t>(N, (int64_t)cus * rounds);
+    if (ceil_div<int64_t>(N, T) > kMaxLaunchItems / kHeldThreads) return 0;   // one launch
+    return (int32_t)T;
+}
 
 // A token's K pairs (K <= MOE_MAX_TOPK) for the one-workgroup-per-token
 // kernels, staged in LDS: threads k < K load pair k's row and weight, and
@@ -529,6 +696,15 @@ extern "C" int moe_combine(const void* y, int64_t y_row_stride, const float* w,
     const RowSums none = {nullptr, 0, nullptr, 0};
     clear_launch_error();
     const bool pipe = (int64_t)N * segs <= kPipeMaxWaves;
+    // Large batches of 16-byte rows with K <= 8 take the held form.
+    const int32_t T = !pipe && vec16 && K <= kBatch && held_kernel_ok()
+                          ? held_tokens(N, segs, stream_cus(stream))
+                          : 0;
+    if (T > 0) {
+        combine_held_kernel<<<(uint32_t)ceil_div<int64_t>(N, T), kHeldThreads, 0, stream>>>(
+            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, T, oo, out_row_stride);
+        return check_launch("moe_combine");
+    }
     in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
         if (vec16)
             launch_combine_piece<4, false>(pipe, first, count, stream, yy, y_row_stride, w,

@@ -158,3 +158,18 @@ def test_write_request_summary(tmp_path, capsys):
     assert cells[3] == f"{b64 / req:.3f}"
     assert cells[4] == f"{(64 * b64 + 32 * (req - b64)) / 1e6:.2f}"
     assert cells[5] == "100 / 100 / 101" and cells[6] == "0 / 64 / 127"
+
+
+def test_combine_kernel_name_follows_the_held_form_rule():
+    """bench.py names the kernel moe_combine runs: the held form past 32768
+    waves with K <= 8 and 8 to 224 segments of 64 16-byte vectors per row."""
+    import bench
+
+    assert bench.combine_kernel_name(4096, 8, 7168) == "combine_held_kernel"    # 57344 waves
+    assert bench.combine_kernel_name(4096, 8, 4096) == "combine_kernel"         # 32768 waves
+    assert bench.combine_kernel_name(4097, 8, 4096) == "combine_held_kernel"
+    assert bench.combine_kernel_name(4097, 9, 4096) == "combine_kernel"         # K > 8
+    assert bench.combine_kernel_name(40000, 8, 3584) == "combine_kernel"        # 7 segments
+    assert bench.combine_kernel_name(147, 3, 114688) == "combine_held_kernel"   # 224 segments
+    assert bench.combine_kernel_name(150, 2, 115200) == "combine_kernel"        # 225 segments
+    assert bench.combine_kernel_name(128, 8, 7168) == "combine_kernel"          # decode

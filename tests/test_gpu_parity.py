@@ -561,7 +561,9 @@ def test_combine_on_both_sides_of_the_load_form_switch(mg, Hc, N, K):
     issue a lane's row loads together, larger ones one at a time: both forms,
     16-byte (Hc = 7168: 14 segments per token) and 4-byte (Hc = 6) loads,
     one and two batches of 8 pairs, masked pairs, for the combine and the
-    dispatch backward (unit weights, weight-gradient sums)."""
+    dispatch backward (unit weights, weight-gradient sums). Past the switch,
+    the combine of 16-byte rows with K <= 8 takes the held form (2341 x 8);
+    with K = 12 it loads one row at a time."""
     rng = np.random.default_rng(N * 31 + K)
     E = 64
     ids = mw.uniform_distinct_ids(rng, N, K, E)
@@ -582,6 +584,47 @@ def test_combine_on_both_sides_of_the_load_form_switch(mg, Hc, N, K):
     ref_x, ref_w = oracle.dispatch_backward(y, pos, grw)
     assert np.array_equal(host_bf16(gx), ref_x)
     assert np.array_equal(gw.cpu().numpy().view(np.uint32), ref_w.view(np.uint32))
+
+
+@pytest.mark.parametrize("Hc,N,K,mask,strided", [
+    (4096, 4096, 8, 0.0, False),      # 32768 waves: the loads issued together
+    (4096, 4097, 8, 0.0, False),      # 32776 waves: held, 17 tokens per workgroup
+    (7168, 2341, 8, 0.1, True),       # held, a last workgroup of 1 token, strided rows
+    (7176, 2400, 5, 0.1, False),      # 15 segments, the last one a single vector
+    (8192, 4096, 8, 0.2, False),      # 2 rounds of 8 tokens per workgroup
+    (4104, 5000, 1, 0.0, True),       # 9 segments, K = 1
+    (4096, 20000, 8, 0.05, False),    # 3 rounds
+    (114688, 147, 3, 0.0, False),     # 224 segments: 1 token per workgroup
+    (115200, 150, 2, 0.0, False),     # 225 segments: past the held form, one load at a time
+    (4096, 4100, 12, 0.1, False),     # K > 8: one load at a time
+])
+def test_combine_held_form(mg, Hc, N, K, mask, strided):
+    """Large batches of 16-byte rows with K <= 8 and 8 to 224 segments per
+    row take the held form (each workgroup stores its tokens' sums after its
+    last row load): bit-identical to the oracle on both sides of every limit
+    of the form, with ragged last workgroups, several rounds of workgroups,
+    a one-vector last segment, masked pairs, all-masked tokens and strided
+    rows whose padding stays untouched."""
+    rng = np.random.default_rng(Hc * 7 + N * 3 + K)
+    E = 64
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < mask] = -1
+    if mask > 0:
+        ids[::97] = -1                       # tokens with every pair masked
+    lay = mg.layout(dev(ids), E)
+    pos = check_layout(mg, lay, ids, E)
+    say(f"held form: Hc={Hc} N={N} K={K} mask={mask} strided={strided}")
+    y = mw.bf16_bits_from_f32(rng.standard_normal((lay.cap, Hc)).astype(np.float32))
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    pad = 24 if strided else 0
+    y_d = torch.zeros((lay.cap, Hc + pad), dtype=torch.bfloat16, device="cuda")
+    y_d[:, :Hc] = dev_bf16(y)
+    out = torch.full((N, Hc + pad), -7.0, dtype=torch.bfloat16, device="cuda")
+    mg.moe_combine(y_d[:, :Hc], dev(w), lay.pos, out[:, :Hc])
+    torch.cuda.synchronize()
+    assert check_combine(out[:, :Hc], y, w, pos) == 0
+    if strided:
+        assert bool((out[:, Hc:] == -7.0).all())
 
 
 def test_concurrent_streams(mg):
@@ -680,6 +723,40 @@ def test_graph_capture_replay(mg, N, misalign):
         used = host(lay.row_pair) >= 0
         assert np.array_equal(got[used], ref[used])
         check_combine(out, y, w, pos)
+        _ = (y_s.float() * 2).sum().item()             # unrelated eager work between replays
+
+
+def test_graph_capture_replay_held_combine(mg):
+    """The held form of the combine (2400 tokens of 7168 channels, top-8)
+    captured in a HIP graph and replayed on new expert rows and weights, with
+    eager work between the replays: every replay equals the oracle."""
+    N, K, E, Hc = 2400, 8, 64, 7168
+    rng = np.random.default_rng(4242)
+    ids = mw.uniform_distinct_ids(rng, N, K, E)
+    ids[rng.random((N, K)) < 0.05] = -1
+    lay = mg.layout(dev(ids), E)
+    pos = check_layout(mg, lay, ids, E)
+    y_s = torch.zeros((lay.cap, Hc), dtype=torch.bfloat16, device="cuda")
+    w_s = torch.zeros((N, K), dtype=torch.float32, device="cuda")
+    out = torch.empty((N, Hc), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mg.moe_combine(y_s, w_s, lay.pos, out)          # warm up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mg.moe_combine(y_s, w_s, lay.pos, out)
+    for rep in range(3):
+        say(f"held combine graph replay {rep}")
+        y = mw.bf16_bits_from_f32(rng.standard_normal((lay.cap, Hc)).astype(np.float32))
+        w = rng.standard_normal((N, K)).astype(np.float32)
+        y_s.copy_(dev_bf16(y))
+        w_s.copy_(dev(w))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert check_combine(out, y, w, pos) == 0
         _ = (y_s.float() * 2).sum().item()             # unrelated eager work between replays
 
 
