@@ -225,10 +225,11 @@ constexpr int kHeldUnits = 28;        // output vectors held per lane
 constexpr int kHeldGroup = 2;         // units whose row loads are in flight together
 constexpr int kHeldMaxTokens = 64;    // tokens a workgroup stages (8 pairs each)
 
+template <bool UNIT>
 __global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
     const uint16_t* __restrict__ y, int64_t ys, const float* __restrict__ w, int64_t wst,
     const int32_t* __restrict__ pos, int32_t N, int32_t K, int32_t V, int32_t segs, int32_t T,
-    uint16_t* __restrict__ out, int64_t os) {
+    uint16_t* __restrict__ out, int64_t os, const RowSums rs) {
     __shared__ int32_t srow[kHeldMaxTokens * kBatch];
     __shared__ float sw[kHeldMaxTokens * kBatch];
     const int lane = threadIdx.x & (kWave - 1);
@@ -238,11 +239,12 @@ __global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
     for (int32_t j = threadIdx.x; j < nt * kBatch; j += kHeldThreads) {
         const int32_t tl = j / kBatch, k = j % kBatch;
         srow[j] = k < K ? pos[(t0 + tl) * K + k] : -1;
-        sw[j] = k < K ? w[(t0 + tl) * wst + k] : 0.0f;
+        sw[j] = UNIT ? 1.0f : (k < K ? w[(t0 + tl) * wst + k] : 0.0f);
     }
     __syncthreads();
     const int32_t units = nt * segs;
     const uint32_t row_bytes = 16u * (uint32_t)V;
+    const bool sums = UNIT && rs.gout != nullptr;
 
     Words<4> held[kHeldUnits];
 #pragma unroll
@@ -253,11 +255,14 @@ __global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
             Words<4> val[kHeldGroup][kBatch];
             float wk[kHeldGroup][kBatch];
             int32_t p[kHeldGroup][kBatch];
+            float gsum[kHeldGroup][kBatch];   // the weight-gradient rows (UNIT, segment 0)
+            int32_t seg0[kHeldGroup];
 #pragma unroll
             for (int g = 0; g < kHeldGroup; ++g) {
                 const int32_t u = min(wave + kHeldWaves * (i0 + g), units - 1);
                 const int32_t tl = u / segs;
                 const int32_t v = (u - tl * segs) * kWave + lane;
+                seg0[g] = u == wave + kHeldWaves * (i0 + g) && u - tl * segs == 0 ? tl : -1;
                 int32_t pr[kBatch];
                 float wr[kBatch];
 #pragma unroll
@@ -274,6 +279,20 @@ __global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
                     val[g][k] = load_row_words<4>(row_rsrc(y, ys, p[g][k], row_bytes),
                                                   (uint32_t)v * 16u);
                 }
+                if (sums && seg0[g] >= 0) {
+                    // lane j < K: entry j of each pair's weight-gradient row
+                    // (lanes past K and masked pairs read 0 and touch nothing)
+#pragma unroll
+                    for (int k = 0; k < kBatch; ++k) {
+                        const float* row = rs.gin + (p[g][k] < 0 ? 0 : (int64_t)p[g][k] * rs.gins);
+                        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                            const_cast<float*>(row), 0,
+                            __builtin_bit_cast(int32_t, p[g][k] < 0 ? 0u : 4u * (uint32_t)K),
+                            kBufferWord3);
+                        gsum[g][k] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, 0, 0));
+                    }
+                }
             }
 #pragma unroll
             for (int g = 0; g < kHeldGroup; ++g) {
@@ -285,14 +304,28 @@ __global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
                     if (p[g][k] < 0) continue;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        acc[2 * q] = __builtin_fmaf(wk[g][k], lo_bf16(val[g][k].w[q]), acc[2 * q]);
-                        acc[2 * q + 1] =
-                            __builtin_fmaf(wk[g][k], hi_bf16(val[g][k].w[q]), acc[2 * q + 1]);
+                        if (UNIT) {
+                            acc[2 * q] = acc[2 * q] + lo_bf16(val[g][k].w[q]);
+                            acc[2 * q + 1] = acc[2 * q + 1] + hi_bf16(val[g][k].w[q]);
+                        } else {
+                            acc[2 * q] =
+                                __builtin_fmaf(wk[g][k], lo_bf16(val[g][k].w[q]), acc[2 * q]);
+                            acc[2 * q + 1] =
+                                __builtin_fmaf(wk[g][k], hi_bf16(val[g][k].w[q]), acc[2 * q + 1]);
+                        }
                     }
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     held[i0 + g].w[q] = pack_bf16_rne(acc[2 * q], acc[2 * q + 1]);
+                if (sums && seg0[g] >= 0) {
+                    // k ascending from +0, masked pairs skipped: combine_kernel's order
+                    float a = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < kBatch; ++k)
+                        if (p[g][k] >= 0) a = a + gsum[g][k];
+                    if (lane < K) rs.gout[(t0 + seg0[g]) * rs.gouts + lane] = a;
+                }
             }
         }
     }
@@ -310,12 +343,14 @@ __global__ __launch_bounds__(kHeldThreads) void combine_held_kernel(
 // Whether combine_held_kernel keeps everything in registers (no scratch
 // memory) on this build; checked once. If it ever spilled, the plain form is
 // used throughout.
+template <bool UNIT>
 bool held_kernel_ok() {
     static std::once_flag once;
     static bool ok = false;
     std::call_once(once, [] {
         hipFuncAttributes attr{};
-        ok = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&combine_held_kernel)) ==
+        ok = hipFuncGetAttributes(&attr,
+                                  reinterpret_cast<const void*>(&combine_held_kernel<UNIT>)) ==
                  hipSuccess &&
              attr.localSizeBytes == 0 && attr.maxThreadsPerBlock >= kHeldThreads;
         (void)hipGetLastError();
@@ -697,12 +732,12 @@ extern "C" int moe_combine(const void* y, int64_t y_row_stride, const float* w,
     clear_launch_error();
     const bool pipe = (int64_t)N * segs <= kPipeMaxWaves;
     // Large batches of 16-byte rows with K <= 8 take the held form.
-    const int32_t T = !pipe && vec16 && K <= kBatch && held_kernel_ok()
+    const int32_t T = !pipe && vec16 && K <= kBatch && held_kernel_ok<false>()
                           ? held_tokens(N, segs, stream_cus(stream))
                           : 0;
     if (T > 0) {
-        combine_held_kernel<<<(uint32_t)ceil_div<int64_t>(N, T), kHeldThreads, 0, stream>>>(
-            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, T, oo, out_row_stride);
+        combine_held_kernel<false><<<(uint32_t)ceil_div<int64_t>(N, T), kHeldThreads, 0, stream>>>(
+            yy, y_row_stride, w, w_row_stride, pos, N, K, V, segs, T, oo, out_row_stride, none);
         return check_launch("moe_combine");
     }
     in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
@@ -756,6 +791,17 @@ extern "C" int moe_dispatch_backward(const void* grad_recv, int64_t grad_recv_ro
     const RowSums rs = {grad_recv_w, grad_recv_w_row_stride, grad_w, grad_w_row_stride};
     clear_launch_error();
     const bool pipe = (int64_t)N * segs <= kPipeMaxWaves;
+    // Large batches of 16-byte rows with K <= 8 take the held form, with the
+    // weight-gradient sums in the waves of each token's first segment.
+    const int32_t T = H > 0 && !pipe && vec16 && K <= kBatch && held_kernel_ok<true>()
+                          ? held_tokens(N, segs, stream_cus(stream))
+                          : 0;
+    if (T > 0) {
+        combine_held_kernel<true><<<(uint32_t)ceil_div<int64_t>(N, T), kHeldThreads, 0, stream>>>(
+            gr, grad_recv_row_stride, nullptr, 0, pos, N, K, V, segs, T, gx, grad_x_row_stride,
+            rs);
+        return check_launch("moe_dispatch_backward");
+    }
     in_pieces(blocks, kMaxLaunchItems / kThreads, [&](int64_t first, int64_t count) {
         if (vec16)
             launch_combine_piece<4, true>(pipe, first, count, stream, gr, grad_recv_row_stride,

@@ -625,6 +625,18 @@ def test_combine_held_form(mg, Hc, N, K, mask, strided):
     assert check_combine(out[:, :Hc], y, w, pos) == 0
     if strided:
         assert bool((out[:, Hc:] == -7.0).all())
+    # the dispatch backward (unit weights, with the weight-gradient sums) on
+    # the same rows takes the same form
+    grw = rng.standard_normal((lay.cap, K)).astype(np.float32)
+    gx = torch.full((N, Hc + pad), -7.0, dtype=torch.bfloat16, device="cuda")
+    gw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    mg.moe_dispatch_backward(y_d[:, :Hc], lay.pos, gx[:, :Hc], dev(grw), gw)
+    torch.cuda.synchronize()
+    ref_x, ref_w = oracle.dispatch_backward(y, pos, grw)
+    assert np.array_equal(host_bf16(gx[:, :Hc]), ref_x)
+    assert np.array_equal(gw.cpu().numpy().view(np.uint32), ref_w.view(np.uint32))
+    if strided:
+        assert bool((gx[:, Hc:] == -7.0).all())
 
 
 def test_concurrent_streams(mg):
