@@ -93,8 +93,9 @@ KERNEL_SOURCES = {k: (os.path.join(_CSRC, f),) + _HDRS for k, f in (
     ("scatter_scales_kernel", "quant.hip"),
 )}
 def combine_kernel_name(N, K, Hc):
-    """The kernel moe_combine runs for N tokens, top-K and Hc channels of
-    16-byte-aligned rows (every workload here): the held form past 32768
+    """The kernel moe_combine (and moe_dispatch_backward, with H for Hc) runs
+    for N tokens, top-K and Hc channels of 16-byte-aligned rows (every
+    workload here): the held form past 32768
     waves (one per token and 64-vector segment) for K <= 8 and 8 to 224
     segments per row, else combine_kernel. The same rule as the library's
     (combine.hip), which also needs the device's compute-unit count (always
@@ -962,7 +963,7 @@ def main():
         op_bytes = bwd_algorithmic_bytes(N, K, 7168, Hc, R)
         # the dispatch backward is the combine kernel in its unit-weight form
         kernels = {"combine_backward": "combine_backward_kernel",
-                   "dispatch_backward": "combine_kernel"}
+                   "dispatch_backward": combine_kernel_name(N, K, 7168)}
     else:
         sets = [BufferSet(torch, mg, wl, y, args.fused) for _ in range(max(1, args.sets))]
         names = ("layout", "dispatch", "combine")
