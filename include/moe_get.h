@@ -23,7 +23,10 @@
  *   - The library never allocates, frees or keeps state between calls; all
  *     buffers belong to the caller. Inputs are read-only and must not
  *     overlap outputs. (One exception: moe_get_layout_noalloc keeps its
- *     workspace in a static device array of the library, described there.)
+ *     workspace in a static device array of the library, described there.
+ *     The combine calls also remember, per device, its compute-unit count
+ *     and whether a kernel fits in registers: facts of the device and of the
+ *     build, not of any call.)
  *   - Return value: MOE_OK (0) or a negative MOE_ERR_* code; argument
  *     problems are found before anything is enqueued. moe_last_error()
  *     describes the last failure of the calling thread.
