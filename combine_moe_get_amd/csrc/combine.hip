@@ -199,8 +199,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 
 
 // ---------------------------------------------------------------------------
-// The held form of the combine, for large batches of 16-byte rows with
-// K <= 8 and at least 8 segments per row.
+// The held form of the combine (and, with UNIT, of the dispatch backward),
+// for large batches of 16-byte rows with K <= 8 and 8 to 224 segments per
+// row.
 //
 // combine_kernel stores each output vector as soon as it is summed, so its
 // writes stream out interleaved with the expert-row reads all through the
@@ -217,7 +218,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 // (token, 64-vector segment) pairs, numbered token-major over the
 // workgroup's tokens, unit u on wave u % 8. Two units' 16 row loads are in
 // flight together. The token's pairs are staged in LDS, padded to 8 (row
-// -1, weight 0 past K), so no load waits behind a scalar fetch.
+// -1, weight 0 past K), so no load waits behind a scalar fetch. With UNIT
+// (every weight 1: adds, as combine_kernel's unit form) the wave of each
+// token's first segment also sums the token's K weight-gradient rows, lane
+// j taking entry j.
 // ---------------------------------------------------------------------------
 constexpr int kHeldThreads = 512;
 constexpr int kHeldWaves = kHeldThreads / kWave;
