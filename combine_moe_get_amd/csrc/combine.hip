@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, workgroup i runs on XCD i % 8
 constexpr int kBatch = 8;   // expert rows loaded before the FMAs that use them
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -567,11 +568,16 @@ __global__ __launch_bounds__(kEpiThreads) void combine_epilogue_kernel(const Epi
 //   grad_y[pos[t,k], h] = bf16_rne(w[t,k] * grad_out[t,h])       (fp32 product)
 //   grad_w[t,k]         = sum_h grad_out[t,h] * y[pos[t,k], h]   (fp32)
 // (DeepEP repository dump, README, "Example use in model training": the
-// backward of the combine is a dispatch). One workgroup per token: its
-// gradient row stays in registers while the K expert rows stream through;
-// each lane keeps one fp32 FMA chain per pair over its channels, the 64
-// lanes of a wave are summed by a fixed butterfly and the waves in index
-// order, so the result does not depend on scheduling.
+// backward of the combine is a dispatch). One workgroup per (token, k) pair:
+// each lane loads its channels of the token's gradient row and of the
+// pair's expert row, stores the scaled row and keeps one fp32 FMA chain over
+// its channels; the 64 lanes of a wave are summed by a fixed butterfly and
+// the waves in index order, so the result does not depend on scheduling.
+// Workgroups are renumbered so that XCD x (workgroup i runs on XCD i mod 8)
+// takes a contiguous eighth of the pairs: a token's K pairs then run on one
+// XCD and read its gradient row from that L2. Measured at prefill against
+// one workgroup per token looping over the token's pairs (same outputs bit
+// for bit): 189.5 against 198.5 us.
 // ---------------------------------------------------------------------------
 
 struct BackwardArgs {
@@ -583,98 +589,107 @@ struct BackwardArgs {
     int64_t ys;
     const int32_t* pos;
     int32_t N, K, V;     // V = Hc / 8
+    uint32_t first;      // the launch piece's first pair (beside N, K, V: one load fetches all four)
     uint16_t* gy;
     int64_t gys;
     float* gw;
     int64_t gws;
 };
 
-template <int VPT>
-__global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const BackwardArgs a,
-                                                                        int32_t first_token) {
-    __shared__ float part[kEpiWaves][kBatch];
+// Lane tid of a workgroup of blockDim threads takes vectors tid + j*blockDim
+// (j < VPT) of the row. blockDim is 1024 when the row has more than 1024
+// vectors, else the row's vectors rounded up to whole waves. WANT_W: the
+// weight gradients are wanted (y is read and the dot products formed).
+template <int VPT, bool WANT_W>
+__global__ __launch_bounds__(kEpiThreads) void combine_backward_kernel(const BackwardArgs a) {
+    __shared__ float part[kEpiWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int32_t t = first_token + (int32_t)blockIdx.x;
-    const int32_t* prow = a.pos + (int64_t)t * a.K;
-    const bool want_w = a.gw != nullptr;
-
-    // the token's gradient row, kept as packed bf16 (half the registers of
-    // fp32; unpacking is a shift or a mask)
-    Words<4> g[VPT];
+    // Logical workgroup: XCD (blockIdx % 8) takes a contiguous eighth of this
+    // piece. The grid is a multiple of 8, so this is a bijection. 32-bit
+    // index arithmetic (N*K < 2^31): a 64-bit division would be a long
+    // software routine in every workgroup.
+    const uint32_t per_xcd = gridDim.x / kXcds;
+    const uint32_t pair = a.first + (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const bool live = pair < (uint32_t)a.N * (uint32_t)a.K;   // else the grid's padding
+    const int32_t p = live ? a.pos[pair] : -1;
+    const uint32_t tu = pair / (uint32_t)a.K;
+    const int32_t k = (int32_t)(pair - tu * (uint32_t)a.K);
+    const int64_t t = tu;
+    float d = 0.0f;
+    // No early return: one condition around each lane's work keeps the
+    // kernel-argument fetches in few rounds (the workgroup's life is a short
+    // chain of dependent loads, and every extra round lengthens it). A
+    // masked pair stores nothing and gets a zero weight gradient below.
+    if constexpr (VPT == 1) {
+        const int32_t v = threadIdx.x;
+        if (p >= 0 && v < a.V) {
+            const float wk = a.w[t * a.wst + k];
+            const int64_t col = (int64_t)v * 8;
+            // the gradient row with ordinary loads: the token's other K-1
+            // pairs read it again from L2
+            const u32x4 gq = *reinterpret_cast<const u32x4*>(a.g + t * a.gs + col);
+            const uint32_t g[4] = {gq.x, gq.y, gq.z, gq.w};
+            Words<4> yv;
+            if (WANT_W) yv = load_words<4>(a.y + (int64_t)p * a.ys + col);
+            float o[8];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int32_t v = threadIdx.x + j * kEpiThreads;
-        if (v < a.V) {
-            g[j] = load_words<4>(a.g + (int64_t)t * a.gs + (int64_t)v * 8);
-        } else {
+            for (int q = 0; q < 4; ++q) {
+                o[2 * q] = wk * lo_bf16(g[q]);
+                o[2 * q + 1] = wk * hi_bf16(g[q]);
+            }
+            store_bf16x8(a.gy + (int64_t)p * a.gys + col, o);
+            if (WANT_W) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) g[j].w[q] = 0u;
+                for (int q = 0; q < 4; ++q) {
+                    d = __builtin_fmaf(lo_bf16(g[q]), lo_bf16(yv.w[q]), d);
+                    d = __builtin_fmaf(hi_bf16(g[q]), hi_bf16(yv.w[q]), d);
+                }
+            }
         }
-    }
-    __shared__ TokenPairs tp;
-    stage_token_pairs(tp, prow, a.w + (int64_t)t * a.wst, a.K);
-
-    for (int k0 = 0; k0 < a.K; k0 += kBatch) {
-        int32_t p[kBatch];
-        float wk[kBatch], d[kBatch];
+    } else if (p >= 0 && a.V > 0) {
+        const float wk = a.w[t * a.wst + k];
+        // Every lane issues all its loads first (vectors past the row clamped
+        // to its last one, then neither stored nor summed): a load under a
+        // per-lane branch would wait for the ones before it.
+        Words<4> g[VPT], yv[VPT];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int k = k0 + i;
-            p[i] = k < a.K ? tp.row[k] : -1;
-            wk[i] = k < a.K ? tp.w[k] : 0.0f;
-            d[i] = 0.0f;
+        for (int j = 0; j < VPT; ++j) {
+            const int64_t col = (int64_t)min((int32_t)threadIdx.x + j * (int32_t)blockDim.x,
+                                             a.V - 1) * 8;
+            const u32x4 gq = *reinterpret_cast<const u32x4*>(a.g + t * a.gs + col);
+            g[j] = Words<4>{{gq.x, gq.y, gq.z, gq.w}};
+            if (WANT_W) yv[j] = load_words<4>(a.y + (int64_t)p * a.ys + col);
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int32_t v = threadIdx.x + j * kEpiThreads;
+            const int32_t v = threadIdx.x + j * (int32_t)blockDim.x;
             if (v >= a.V) continue;
-            const int64_t col = (int64_t)v * 8;
-            Words<4> yv[kBatch];
-            if (want_w) {
+            float o[8];
 #pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    yv[i] = load_row_words<4>(row_rsrc(a.y, a.ys, p[i], (uint32_t)a.V * 16),
-                                              (uint32_t)col * 2);
+            for (int q = 0; q < 4; ++q) {
+                o[2 * q] = wk * lo_bf16(g[j].w[q]);
+                o[2 * q + 1] = wk * hi_bf16(g[j].w[q]);
             }
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                if (p[i] < 0) continue;
-                float o[8];
+            store_bf16x8(a.gy + (int64_t)p * a.gys + (int64_t)v * 8, o);
+            if (WANT_W) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    o[2 * q] = wk[i] * lo_bf16(g[j].w[q]);
-                    o[2 * q + 1] = wk[i] * hi_bf16(g[j].w[q]);
-                }
-                store_bf16x8(a.gy + (int64_t)p[i] * a.gys + col, o);
-                if (want_w) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        d[i] = __builtin_fmaf(lo_bf16(g[j].w[q]), lo_bf16(yv[i].w[q]), d[i]);
-                        d[i] = __builtin_fmaf(hi_bf16(g[j].w[q]), hi_bf16(yv[i].w[q]), d[i]);
-                    }
+                    d = __builtin_fmaf(lo_bf16(g[j].w[q]), lo_bf16(yv[j].w[q]), d);
+                    d = __builtin_fmaf(hi_bf16(g[j].w[q]), hi_bf16(yv[j].w[q]), d);
                 }
             }
         }
-        if (!want_w) continue;
+    }
+    if (!WANT_W) return;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-#pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1) d[i] += __shfl_xor(d[i], off, kWave);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) part[wave][i] = d[i];
-        }
-        __syncthreads();
-        if (threadIdx.x < kBatch && k0 + (int)threadIdx.x < a.K) {
-            const int i = threadIdx.x;
-            float sum = 0.0f;
-#pragma unroll
-            for (int wv = 0; wv < kEpiWaves; ++wv) sum += part[wv][i];
-            a.gw[(int64_t)t * a.gws + k0 + i] = prow[k0 + i] >= 0 ? sum : 0.0f;
-        }
-        __syncthreads();   // part is rewritten by the next batch
+    for (int off = kWave / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, kWave);
+    if (lane == 0) part[wave] = d;
+    __syncthreads();
+    if (live && threadIdx.x == 0) {
+        float sum = 0.0f;
+        for (int wv = 0; wv < (int)(blockDim.x / kWave); ++wv) sum += part[wv];
+        a.gw[t * a.gws + k] = p >= 0 ? sum : 0.0f;
     }
 }
 
@@ -957,15 +972,28 @@ extern "C" int moe_combine_backward(const void* grad_out, int64_t grad_out_row_s
     a.gw = grad_w;
     a.gws = grad_w_row_stride;
     const int vpt = ceil_div<int32_t>(a.V, kEpiThreads);
+    const int threads = vpt > 1 ? kEpiThreads
+                                : (int)std::max<int64_t>(kWave, ceil_div<int64_t>(a.V, kWave) * kWave);
+    const int64_t pairs = (int64_t)N * K;
+    const int64_t blocks = ceil_div<int64_t>(pairs, kXcds) * kXcds;
+    const int64_t piece = kMaxLaunchItems / kEpiThreads / kXcds * kXcds;
     clear_launch_error();
-    in_pieces(N, kMaxLaunchItems / kEpiThreads, [&](int64_t first, int64_t count) {
-        const int32_t t0 = (int32_t)first;
-        if (vpt <= 1)
-            combine_backward_kernel<1><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+    in_pieces(blocks, piece, [&](int64_t first, int64_t count) {
+        BackwardArgs b = a;
+        b.first = (uint32_t)first;
+        const bool ww = grad_w != nullptr;
+        if (vpt <= 1 && ww)
+            combine_backward_kernel<1, true><<<(uint32_t)count, threads, 0, stream>>>(b);
+        else if (vpt <= 1)
+            combine_backward_kernel<1, false><<<(uint32_t)count, threads, 0, stream>>>(b);
+        else if (vpt <= 2 && ww)
+            combine_backward_kernel<2, true><<<(uint32_t)count, threads, 0, stream>>>(b);
         else if (vpt <= 2)
-            combine_backward_kernel<2><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+            combine_backward_kernel<2, false><<<(uint32_t)count, threads, 0, stream>>>(b);
+        else if (ww)
+            combine_backward_kernel<4, true><<<(uint32_t)count, threads, 0, stream>>>(b);
         else
-            combine_backward_kernel<4><<<(uint32_t)count, kEpiThreads, 0, stream>>>(a, t0);
+            combine_backward_kernel<4, false><<<(uint32_t)count, threads, 0, stream>>>(b);
     });
     return check_launch("moe_combine_backward");
 }
