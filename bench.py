@@ -88,6 +88,7 @@ KERNEL_SOURCES = {k: (os.path.join(_CSRC, f),) + _HDRS for k, f in (
     ("layout_onepass", "layout.hip"),
     ("dispatch_fp8_kernel", "quant.hip"),
     ("combine_backward_kernel", "combine.hip"),
+    ("combine_backward_group_kernel", "combine.hip"),
     ("dispatch_fp8_padded_kernel", "quant.hip"),
     ("layout_dispatch_kernel", "dispatch.hip"),
     ("scatter_scales_kernel", "quant.hip"),
@@ -962,7 +963,11 @@ def main():
         names = ("combine_backward", "dispatch_backward")
         op_bytes = bwd_algorithmic_bytes(N, K, 7168, Hc, R)
         # the dispatch backward is the combine kernel in its unit-weight form
-        kernels = {"combine_backward": "combine_backward_kernel",
+        # rows of at most 1024 vectors with K a multiple of 4 take the grouped
+        # form (four pairs of a token per workgroup)
+        grouped = Hc // 8 <= 1024 and K % 4 == 0
+        kernels = {"combine_backward": "combine_backward_group_kernel" if grouped
+                   else "combine_backward_kernel",
                    "dispatch_backward": combine_kernel_name(N, K, 7168)}
     else:
         sets = [BufferSet(torch, mg, wl, y, args.fused) for _ in range(max(1, args.sets))]

@@ -145,7 +145,7 @@ def test_dispatch_backward_weights_only_and_strided(mg):
 @pytest.mark.parametrize("seed,N,K,E,Hc,mask", [
     (11, 300, 8, 64, 7168, 0.1), (12, 64, 3, 16, 8, 0.3), (13, 70, 12, 40, 8200, 0.2),
     (14, 20, 32, 32, 16384, 0.0), (15, 9, 1, 4, 32768, 0.5), (16, 40, 8, 8, 256, 1.0),
-    (17, 33, 5, 9, 24, 0.1)])
+    (17, 33, 5, 9, 24, 0.1), (18, 50, 4, 12, 8192, 0.25), (19, 7, 16, 64, 64, 0.5)])
 def test_combine_backward_parity(mg, seed, N, K, E, Hc, mask):
     say(f"combine backward seed={seed} N={N} K={K} Hc={Hc}")
     rng, pos = _pos(seed, N, K, E, mask)
